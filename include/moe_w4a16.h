@@ -1,0 +1,189 @@
+/*
+ * moe_w4a16.h -- C ABI of the NVFP4 weight-only (W4A16) routed-expert MoE
+ * layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (pages: "GLM-5.3-Flash-NVFP4-h -- W4A16 dense-side quantization",
+ * intro and "Config expectations"; "GLM-5.3-Flash on Blackwell", "The
+ * quantization" and "The model loaded, served an API, and produced garbage";
+ * "GLM-5.3-Flash NVFP4 W4A16 for 2x RTX PRO 6000 Blackwell", intro):
+ *
+ *   - every routed expert has gate, up and down projections, each stored as
+ *     its own NVFP4 weight-only tensor: 4-bit E2M1 codes in groups of 16
+ *     along K, one E4M3 scale per group, one FP32 scale per tensor;
+ *   - activations are bf16 and the layer takes NO activation scale: a
+ *     weight-only checkpoint has none, and a layer that reads one computes
+ *     with an uninitialised value;
+ *   - the W4A16 route dequantises weights to bf16 for the matrix units;
+ *   - a missing or unset global scale is refused loudly, never computed.
+ *
+ *   out[t] = sum_j w[t,j] * down_e( silu(gate_e(x[t])) * up_e(x[t]) ),
+ *   e = ids[t,j], with (ids, w) the top-k of the router logits and a softmax
+ *   over the selected k.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named d_* (and every pointer inside moe_nvfp4_tensor) are
+ *     DEVICE pointers; everything else is host memory.  The caller allocates
+ *     and owns all of them, the workspace included.  Device pointers must be
+ *     16-byte aligned.
+ *   - Work is enqueued on `stream` and returns before it completes, except
+ *     where a function says it synchronises.  Nothing on the hot path
+ *     (moe_route_topk, moe_w4a16_forward) allocates, frees, synchronises or
+ *     issues a memset, so both may be captured into a HIP graph.
+ *   - Argument, shape and alignment errors are detected on the host before
+ *     anything is enqueued; the call then has no effect.  Launch failures
+ *     return MOE_ERR_HIP.  A device fault surfaces at the caller's next
+ *     synchronisation, as usual for HIP.
+ *   - The library keeps no state between calls and is thread-safe.
+ *
+ * Limits: 1 <= E <= 1024, 1 <= k <= min(E, 32); quantize_pack needs
+ * K % 32 == 0; the forward needs H % 256 == 0 and I % 128 == 0.
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+#define MOE_OK                  0
+#define MOE_ERR_INVALID_ARG   (-1)  /* null pointer, aliasing, bad enum            */
+#define MOE_ERR_SHAPE         (-2)  /* dimension out of range or not a multiple    */
+#define MOE_ERR_ALIGN         (-3)  /* device pointer not 16-byte aligned          */
+#define MOE_ERR_UNSUPPORTED   (-4)  /* E or k beyond the compiled limits           */
+#define MOE_ERR_NONFINITE     (-5)  /* validate: non-finite global scale           */
+#define MOE_ERR_BAD_SCALE     (-6)  /* validate: global scale <= 0, or a NaN E4M3  */
+#define MOE_ERR_WORKSPACE     (-7)  /* workspace null or smaller than required     */
+#define MOE_ERR_HIP           (-8)  /* a HIP runtime call failed                   */
+
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK    32
+
+/*
+ * One NVFP4 weight-only tensor stack: E experts of an [N, K] projection
+ * (output features N, input features K), canonical layout:
+ *   codes        [E][N][K/2]  byte i of a row = code(2i) | code(2i+1) << 4
+ *                             (even k in the low nibble), E2M1 codes
+ *   scales       [E][N][K/16] E4M3 ("FN") bit patterns, one per 16 k
+ *   global_scale [E]          fp32, finite and > 0
+ * Weight value: (E2M1(code) * E4M3(scale)) * global_scale, in fp32.
+ * The struct itself lives in host memory; its pointers are device pointers.
+ */
+typedef struct {
+    int32_t E, N, K;
+    uint8_t *codes;
+    uint8_t *scales;
+    float *global_scale;
+} moe_nvfp4_tensor;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *moe_status_string(moe_status status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t moe_w4a16_version(void);
+
+/*
+ * Quantize fp32 master weights to NVFP4 (load time, not the hot path).
+ * Follows the weight-only, calibration-free conversion the pages describe
+ * ("GLM-5.3-Flash NVFP4 W4A16 for 2x RTX PRO 6000 Blackwell", intro;
+ * "GLM-5.3-Flash-NVFP4-h", "Config expectations": group size 16 and a FP32
+ * second-level scale per tensor).  Per expert e, all in fp32 with correctly
+ * rounded operations in this order:
+ *   g = amax|W_e| / 2688, or 1 if that is 0;
+ *   per 16-group: s = E4M3_rne_saturating((amax_group / 6) / g);
+ *   code = E2M1_rne_saturating(W / (E4M3(s) * g)), sign kept, ties to even
+ *   (a group whose E4M3(s) * g is 0 gets magnitude-0 codes with the sign bit
+ *   of each weight).
+ * d_w: fp32 [E][N][K] row-major.  out->E/N/K must equal E/N/K; out's buffers
+ * are written (out->global_scale is also used as scratch during the call).
+ * Results are bit-identical to the reference definition above for finite
+ * input; non-finite masters give unspecified (but memory-safe) output.
+ */
+moe_status moe_w4a16_quantize_pack(const float *d_w, int32_t E, int32_t N, int32_t K,
+                                   const moe_nvfp4_tensor *out, hipStream_t stream);
+
+/*
+ * Test hook: dequantize a whole tensor stack to fp32 [E][N][K] with the same
+ * device decode routines the forward uses ((E2M1 * E4M3) * g in fp32).
+ */
+moe_status moe_w4a16_dequantize(const moe_nvfp4_tensor *t, float *d_w_out, hipStream_t stream);
+
+/*
+ * Check a tensor stack before use.  SYNCHRONISES `stream`.  Returns
+ * MOE_ERR_NONFINITE if a global scale is NaN/Inf, MOE_ERR_BAD_SCALE if one is
+ * <= 0 (the unset-scale fault: "GLM-5.3-Flash on Blackwell", "The model
+ * loaded, served an API, and produced garbage") or if a group scale byte is
+ * an E4M3 NaN (0x7F / 0xFF).  Allocates and frees a 4-byte device flag.
+ */
+moe_status moe_w4a16_validate(const moe_nvfp4_tensor *t, hipStream_t stream);
+
+/* Workspace bytes moe_route_topk needs for T tokens (0 is a valid answer). */
+size_t moe_route_workspace_size(int32_t T, int32_t E, int32_t k);
+
+/*
+ * Router top-k + softmax, and the expert-sorted permutation.
+ *   d_logits       fp32 [T][E] router logits (finite)
+ *   d_topk_ids     int32 [T][k] out: per token, experts by descending logit,
+ *                  ties to the lower index
+ *   d_topk_w       fp32 [T][k] out: softmax over the k selected logits
+ *   d_counts       int32 [E]   out: (token, slot) pairs per expert
+ *   d_offsets      int32 [E+1] out: exclusive prefix sum, d_offsets[E] = T*k
+ *   d_sorted_slots int32 [T*k] out: flat slot indices t*k+j grouped by expert,
+ *                  ascending flat index inside each expert (stable)
+ *   d_slot_pos     int32 [T*k] out: inverse of d_sorted_slots
+ *   d_ws           workspace of moe_route_workspace_size(T, E, k) bytes
+ * Deterministic: identical inputs give identical bits.  T == 0 is a no-op.
+ */
+moe_status moe_route_topk(const float *d_logits, int32_t T, int32_t E, int32_t k,
+                          int32_t *d_topk_ids, float *d_topk_w,
+                          int32_t *d_counts, int32_t *d_offsets,
+                          int32_t *d_sorted_slots, int32_t *d_slot_pos,
+                          void *d_ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes moe_w4a16_forward needs. */
+size_t moe_w4a16_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
+
+/*
+ * The routed-expert layer: out = sum_j w[t,j] * SwiGLU-FFN_{ids[t,j]}(x[t]).
+ *   d_x     bf16 [T][H] activations (uint16 bit patterns); no activation scale
+ *   gate,up NVFP4 stacks with N = I, K = H;  down: N = H, K = I;  all with E
+ *   routing arrays exactly as moe_route_topk produces them
+ *   d_out   bf16 [T][H] out (must not overlap d_x)
+ *   d_ws    workspace of moe_w4a16_workspace_size(T, H, I, E, k) bytes
+ * Arithmetic: weights decode exactly to bf16 (E2M1 * E4M3 has at most 6
+ * significant bits), products accumulate in fp32, the global scale is
+ * applied in fp32 after the K reduction, SwiGLU in fp32, the SwiGLU output is
+ * rounded once to bf16, the down projection accumulates in fp32 and the
+ * routing-weighted combine runs in fp32 before one rounding to bf16.
+ * Deterministic: no floating-point atomics.  T == 0 is a no-op.
+ */
+moe_status moe_w4a16_forward(const uint16_t *d_x, int32_t T, int32_t H, int32_t I,
+                             int32_t E, int32_t k,
+                             const moe_nvfp4_tensor *gate, const moe_nvfp4_tensor *up,
+                             const moe_nvfp4_tensor *down,
+                             const int32_t *d_topk_ids, const float *d_topk_w,
+                             const int32_t *d_counts, const int32_t *d_offsets,
+                             const int32_t *d_sorted_slots, const int32_t *d_slot_pos,
+                             uint16_t *d_out, void *d_ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/*
+ * Per-kernel timing for benchmarks.  moe_profile_begin(n) makes the calls that
+ * follow (on any stream) bracket each kernel they launch with a pair of HIP
+ * events recorded on that kernel's stream, for up to n kernels.
+ * moe_profile_end() synchronises on the last event and writes, for each
+ * distinct kernel name (up to `max`), its launch count and total milliseconds.
+ * Returns the number of names written.  Not thread-safe; for benchmarks only.
+ */
+moe_status moe_profile_begin(int32_t max_launches);
+int32_t moe_profile_end(char (*names)[64], int32_t *counts, double *total_ms, int32_t max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H */

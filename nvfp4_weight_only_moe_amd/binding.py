@@ -1,0 +1,220 @@
+"""Thin ctypes binding of libmoe_w4a16.so (C ABI in include/moe_w4a16.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+PyTorch supplies device memory and the current HIP stream.  The entry points
+keep the C names; each checks the returned status and raises ``MoeError``.
+There is no CPU fallback: if the library is missing, loading raises.
+"""
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_w4a16.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "moe_w4a16.h")
+
+MOE_OK = 0
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIGN",
+          -4: "MOE_ERR_UNSUPPORTED", -5: "MOE_ERR_NONFINITE", -6: "MOE_ERR_BAD_SCALE",
+          -7: "MOE_ERR_WORKSPACE", -8: "MOE_ERR_HIP"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class NVFP4TensorC(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("global_scale", ctypes.c_void_p)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_S = ctypes.c_size_t
+_TP = ctypes.POINTER(NVFP4TensorC)
+
+_SIGS = {
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_w4a16_version": (_I, []),
+    "moe_w4a16_quantize_pack": (_I, [_P, _I, _I, _I, _TP, _P]),
+    "moe_w4a16_dequantize": (_I, [_TP, _P, _P]),
+    "moe_w4a16_validate": (_I, [_TP, _P]),
+    "moe_route_workspace_size": (_S, [_I, _I, _I]),
+    "moe_route_topk": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
+    "moe_w4a16_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "moe_w4a16_forward": (_I, [_P, _I, _I, _I, _I, _I, _TP, _TP, _TP, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
+    "moe_profile_begin": (_I, [_I]),
+    "moe_profile_end": (_I, [_P, _P, _P, _I]),
+}
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_symbols():
+    """Names of the functions include/moe_w4a16.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def status_string(status):
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+@dataclass
+class NVFP4Tensor:
+    """E experts of an [N, K] NVFP4 projection in canonical layout (device)."""
+    codes: torch.Tensor         # uint8 [E, N, K/2]
+    scales: torch.Tensor        # uint8 [E, N, K/16]
+    global_scale: torch.Tensor  # float32 [E]
+
+    @property
+    def shape(self):
+        E, N, half = self.codes.shape
+        return E, N, half * 2
+
+    def cstruct(self):
+        E, N, K = self.shape
+        return NVFP4TensorC(E, N, K, self.codes.data_ptr(), self.scales.data_ptr(),
+                            self.global_scale.data_ptr())
+
+    @staticmethod
+    def empty(E, N, K, device="cuda"):
+        return NVFP4Tensor(torch.empty((E, N, K // 2), dtype=torch.uint8, device=device),
+                           torch.empty((E, N, K // 16), dtype=torch.uint8, device=device),
+                           torch.empty((E,), dtype=torch.float32, device=device))
+
+
+def moe_w4a16_version():
+    return int(lib().moe_w4a16_version())
+
+
+def moe_w4a16_quantize_pack(w, out=None, stream=None):
+    """fp32 masters [E, N, K] (device) -> NVFP4Tensor."""
+    E, N, K = w.shape
+    out = NVFP4Tensor.empty(E, N, K, w.device) if out is None else out
+    st = out.cstruct()
+    _check(lib().moe_w4a16_quantize_pack(_ptr(w), E, N, K, ctypes.byref(st), _stream(stream)),
+           "moe_w4a16_quantize_pack")
+    return out
+
+
+def moe_w4a16_dequantize(t, out=None, stream=None):
+    E, N, K = t.shape
+    out = torch.empty((E, N, K), dtype=torch.float32, device=t.codes.device) if out is None else out
+    st = t.cstruct()
+    _check(lib().moe_w4a16_dequantize(ctypes.byref(st), _ptr(out), _stream(stream)), "moe_w4a16_dequantize")
+    return out
+
+
+def moe_w4a16_validate(t, stream=None):
+    st = t.cstruct()
+    _check(lib().moe_w4a16_validate(ctypes.byref(st), _stream(stream)), "moe_w4a16_validate")
+
+
+def moe_route_workspace_size(T, E, k):
+    return int(lib().moe_route_workspace_size(T, E, k))
+
+
+def moe_w4a16_workspace_size(T, H, I, E, k):
+    return int(lib().moe_w4a16_workspace_size(T, H, I, E, k))
+
+
+@dataclass
+class Routing:
+    topk_ids: torch.Tensor      # int32 [T, k]
+    topk_w: torch.Tensor        # float32 [T, k]
+    counts: torch.Tensor        # int32 [E]
+    offsets: torch.Tensor       # int32 [E + 1]
+    sorted_slots: torch.Tensor  # int32 [T * k]
+    slot_pos: torch.Tensor      # int32 [T * k]
+    ws: torch.Tensor            # uint8 workspace
+
+    @staticmethod
+    def empty(T, E, k, device="cuda"):
+        i32 = dict(dtype=torch.int32, device=device)
+        return Routing(torch.empty((T, k), **i32), torch.empty((T, k), dtype=torch.float32, device=device),
+                       torch.empty((E,), **i32), torch.empty((E + 1,), **i32),
+                       torch.empty((T * k,), **i32), torch.empty((T * k,), **i32),
+                       torch.empty((max(moe_route_workspace_size(T, E, k), 16),), dtype=torch.uint8,
+                                   device=device))
+
+
+def moe_route_topk(logits, k, out=None, stream=None):
+    """fp32 logits [T, E] (device) -> Routing."""
+    T, E = logits.shape
+    r = Routing.empty(T, E, k, logits.device) if out is None else out
+    _check(lib().moe_route_topk(_ptr(logits), T, E, k, _ptr(r.topk_ids), _ptr(r.topk_w), _ptr(r.counts),
+                                _ptr(r.offsets), _ptr(r.sorted_slots), _ptr(r.slot_pos), _ptr(r.ws),
+                                r.ws.numel(), _stream(stream)), "moe_route_topk")
+    return r
+
+
+def forward_workspace(T, H, I, E, k, device="cuda"):
+    return torch.empty((max(moe_w4a16_workspace_size(T, H, I, E, k), 16),), dtype=torch.uint8, device=device)
+
+
+def moe_w4a16_forward(x_bits, gate, up, down, routing, out=None, ws=None, stream=None):
+    """bf16 activations (int16/uint16 bit patterns or torch.bfloat16) [T, H] ->
+    bf16 bits [T, H] (int16 tensor; view as torch.bfloat16 for values)."""
+    T, H = x_bits.shape
+    E, I, _ = gate.shape
+    k = routing.topk_ids.shape[1]
+    out = torch.empty((T, H), dtype=torch.int16, device=x_bits.device) if out is None else out
+    ws = forward_workspace(T, H, I, E, k, x_bits.device) if ws is None else ws
+    g, u, d = gate.cstruct(), up.cstruct(), down.cstruct()
+    _check(lib().moe_w4a16_forward(_ptr(x_bits), T, H, I, E, k, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                                   _ptr(routing.topk_ids), _ptr(routing.topk_w), _ptr(routing.counts),
+                                   _ptr(routing.offsets), _ptr(routing.sorted_slots), _ptr(routing.slot_pos),
+                                   _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "moe_w4a16_forward")
+    return out
+
+
+def moe_profile_begin(max_launches=4096):
+    _check(lib().moe_profile_begin(max_launches), "moe_profile_begin")
+
+
+def moe_profile_end(max_names=64):
+    """Synchronises; returns {kernel name: (launches, total ms)}."""
+    names = (ctypes.c_char * 64 * max_names)()
+    counts = (ctypes.c_int32 * max_names)()
+    ms = (ctypes.c_double * max_names)()
+    n = lib().moe_profile_end(ctypes.cast(names, ctypes.c_void_p), ctypes.cast(counts, ctypes.c_void_p),
+                              ctypes.cast(ms, ctypes.c_void_p), max_names)
+    return {names[i].value.decode(): (int(counts[i]), float(ms[i])) for i in range(n)}

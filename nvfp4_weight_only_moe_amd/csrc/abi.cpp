@@ -1,0 +1,272 @@
+// C ABI of libmoe_w4a16: argument checking, workspace layout and dispatch.
+// Every check runs on the host before anything is enqueued, so a refused
+// call has no effect on the device.  See include/moe_w4a16.h for the
+// contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_tensor(const moe_nvfp4_tensor* t, int E, int N, int K) {
+    if (!t || !t->codes || !t->scales || !t->global_scale) return MOE_ERR_INVALID_ARG;
+    if (t->E != E || t->N != N || t->K != K) return MOE_ERR_SHAPE;
+    if (!aligned16(t->codes) || !aligned16(t->scales) || !aligned16(t->global_scale)) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+moe_status check_tensor_self(const moe_nvfp4_tensor* t) {
+    if (!t) return MOE_ERR_INVALID_ARG;
+    if (t->E < 1 || t->N < 1 || t->K < 32 || t->K % 32) return MOE_ERR_SHAPE;
+    if (t->E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+    return check_tensor(t, t->E, t->N, t->K);
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+// ---- profiling state (benchmarks only)
+struct ProfRec {
+    std::string name;
+    hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+int g_prof_max = 0;
+std::vector<ProfRec> g_prof;
+ProfRec* g_prof_open = nullptr;
+
+}  // namespace
+
+void prof_before(const char* name, hipStream_t s) {
+    if (!g_prof_on) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if ((int)g_prof.size() >= g_prof_max) return;
+    ProfRec r{name, nullptr, nullptr};
+    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return;
+    hipEventRecord(r.start, s);
+    g_prof.push_back(r);
+    g_prof_open = &g_prof.back();
+}
+
+void prof_after(hipStream_t s) {
+    if (!g_prof_on) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_open) return;
+    hipEventRecord(g_prof_open->stop, s);
+    g_prof_open = nullptr;
+}
+
+size_t forward_workspace_bytes(int T, int H, int I, int E, int k) {
+    (void)E;
+    const size_t slots = (size_t)T * k;
+    return round_up(slots * I * sizeof(uint16_t), kAlign) + round_up(slots * H * sizeof(float), kAlign);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(moe_status st) {
+    switch (st) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: null pointer, aliasing or bad argument";
+        case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: dimension out of range or not a required multiple";
+        case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: device pointer not 16-byte aligned";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: E or k beyond the compiled limits";
+        case MOE_ERR_NONFINITE: return "MOE_ERR_NONFINITE: a global scale is NaN or infinite";
+        case MOE_ERR_BAD_SCALE: return "MOE_ERR_BAD_SCALE: a global scale is <= 0 or a group scale is an E4M3 NaN";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP runtime call failed";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+int32_t moe_w4a16_version(void) { return 100; }
+
+moe_status moe_w4a16_quantize_pack(const float* d_w, int32_t E, int32_t N, int32_t K, const moe_nvfp4_tensor* out,
+                                   hipStream_t stream) {
+    if (!d_w || !out) return MOE_ERR_INVALID_ARG;
+    if (E < 1 || N < 1 || K < 32 || K % 32) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+    moe_status st = check_tensor(out, E, N, K);
+    if (st != MOE_OK) return st;
+    if (!aligned16(d_w)) return MOE_ERR_ALIGN;
+    const size_t wbytes = (size_t)E * N * K * sizeof(float);
+    if (ranges_overlap(d_w, wbytes, out->codes, (size_t)E * N * K / 2) ||
+        ranges_overlap(d_w, wbytes, out->scales, (size_t)E * N * K / 16) ||
+        ranges_overlap(d_w, wbytes, out->global_scale, (size_t)E * sizeof(float)))
+        return MOE_ERR_INVALID_ARG;
+    return launch_quantize_pack(d_w, E, N, K, out, stream);
+}
+
+moe_status moe_w4a16_dequantize(const moe_nvfp4_tensor* t, float* d_w_out, hipStream_t stream) {
+    moe_status st = check_tensor_self(t);
+    if (st != MOE_OK) return st;
+    if (!d_w_out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(d_w_out)) return MOE_ERR_ALIGN;
+    return launch_dequantize(t, d_w_out, stream);
+}
+
+moe_status moe_w4a16_validate(const moe_nvfp4_tensor* t, hipStream_t stream) {
+    moe_status st = check_tensor_self(t);
+    if (st != MOE_OK) return st;
+    uint32_t* d_flag = nullptr;
+    if (hipMalloc(&d_flag, sizeof(uint32_t)) != hipSuccess) return MOE_ERR_HIP;
+    uint32_t flag = 0;
+    st = MOE_OK;
+    if (hipMemcpyAsync(d_flag, &flag, sizeof(flag), hipMemcpyHostToDevice, stream) != hipSuccess) st = MOE_ERR_HIP;
+    if (st == MOE_OK) st = launch_validate(t, d_flag, stream);
+    if (st == MOE_OK && hipMemcpyAsync(&flag, d_flag, sizeof(flag), hipMemcpyDeviceToHost, stream) != hipSuccess)
+        st = MOE_ERR_HIP;
+    if (st == MOE_OK && hipStreamSynchronize(stream) != hipSuccess) st = MOE_ERR_HIP;
+    hipFree(d_flag);
+    if (st != MOE_OK) return st;
+    if (flag & 1u) return MOE_ERR_NONFINITE;
+    if (flag & 6u) return MOE_ERR_BAD_SCALE;
+    return MOE_OK;
+}
+
+size_t moe_route_workspace_size(int32_t T, int32_t E, int32_t k) {
+    if (T <= 0 || E < 1 || k < 1) return 0;
+    return route_workspace_bytes(T, E, k);
+}
+
+moe_status moe_route_topk(const float* d_logits, int32_t T, int32_t E, int32_t k, int32_t* d_topk_ids,
+                          float* d_topk_w, int32_t* d_counts, int32_t* d_offsets, int32_t* d_sorted_slots,
+                          int32_t* d_slot_pos, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+    if (T < 0 || E < 1 || k < 1) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || k > E) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)T * k > (int64_t)INT32_MAX / 2) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    const void* ptrs[] = {d_logits, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots, d_slot_pos};
+    for (const void* p : ptrs) {
+        if (!p) return MOE_ERR_INVALID_ARG;
+        if (!aligned16(p)) return MOE_ERR_ALIGN;
+    }
+    const size_t need = route_workspace_bytes(T, E, k);
+    if (need > 0) {
+        if (!d_ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+        if (!aligned16(d_ws)) return MOE_ERR_ALIGN;
+    }
+    return launch_route(d_logits, T, E, k, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots, d_slot_pos,
+                        d_ws, stream);
+}
+
+size_t moe_w4a16_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k) {
+    if (T <= 0 || H <= 0 || I <= 0 || k <= 0) return 0;
+    return forward_workspace_bytes(T, H, I, E, k);
+}
+
+moe_status moe_w4a16_forward(const uint16_t* d_x, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                             const moe_nvfp4_tensor* gate, const moe_nvfp4_tensor* up, const moe_nvfp4_tensor* down,
+                             const int32_t* d_topk_ids, const float* d_topk_w, const int32_t* d_counts,
+                             const int32_t* d_offsets, const int32_t* d_sorted_slots, const int32_t* d_slot_pos,
+                             uint16_t* d_out, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+    if (T < 0 || E < 1 || k < 1 || H < 1 || I < 1) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || k > E) return MOE_ERR_UNSUPPORTED;
+    if (H % 256 || I % 128) return MOE_ERR_SHAPE;
+    if ((int64_t)T * k > (int64_t)INT32_MAX / 2) return MOE_ERR_SHAPE;
+    if (!gate || !up || !down) return MOE_ERR_INVALID_ARG;
+    moe_status st;
+    if ((st = check_tensor(gate, E, I, H)) != MOE_OK) return st;
+    if ((st = check_tensor(up, E, I, H)) != MOE_OK) return st;
+    if ((st = check_tensor(down, E, H, I)) != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    const void* ptrs[] = {d_x, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots, d_slot_pos, d_out, d_ws};
+    for (const void* p : ptrs) {
+        if (!p) return p == d_ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
+        if (!aligned16(p)) return MOE_ERR_ALIGN;
+    }
+    const size_t xbytes = (size_t)T * H * sizeof(uint16_t);
+    if (ranges_overlap(d_x, xbytes, d_out, xbytes)) return MOE_ERR_INVALID_ARG;
+    const size_t need = forward_workspace_bytes(T, H, I, E, k);
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    if (ranges_overlap(d_ws, need, d_out, xbytes) || ranges_overlap(d_ws, need, d_x, xbytes))
+        return MOE_ERR_INVALID_ARG;
+
+    FwdArgs a{};
+    a.x = d_x;
+    a.T = T; a.H = H; a.I = I; a.E = E; a.k = k;
+    a.gate = gate; a.up = up; a.down = down;
+    a.ids = d_topk_ids;
+    a.topk_w = d_topk_w;
+    a.counts = d_counts;
+    a.offsets = d_offsets;
+    a.sorted_slots = d_sorted_slots;
+    a.slot_pos = d_slot_pos;
+    a.out = d_out;
+    uint8_t* ws = static_cast<uint8_t*>(d_ws);
+    const size_t slots = (size_t)T * k;
+    a.h = reinterpret_cast<uint16_t*>(ws);
+    a.y = reinterpret_cast<float*>(ws + round_up(slots * I * sizeof(uint16_t), 256));
+    if (decode_path_supported(T, H, I)) return launch_forward_decode(a, stream);
+    return launch_forward_prefill(a, stream);
+}
+
+moe_status moe_profile_begin(int32_t max_launches) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (auto& r : g_prof) {
+        hipEventDestroy(r.start);
+        hipEventDestroy(r.stop);
+    }
+    g_prof.clear();
+    g_prof.reserve(max_launches > 0 ? max_launches : 0);
+    g_prof_max = max_launches > 0 ? max_launches : 0;
+    g_prof_open = nullptr;
+    g_prof_on = g_prof_max > 0;
+    return MOE_OK;
+}
+
+int32_t moe_profile_end(char (*names)[64], int32_t* counts, double* total_ms, int32_t max) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on = false;
+    std::vector<std::string> keys;
+    std::vector<int32_t> cnt;
+    std::vector<double> ms;
+    for (auto& r : g_prof) {
+        float t = 0.0f;
+        if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess)
+            t = -1.0f;
+        size_t i = 0;
+        while (i < keys.size() && keys[i] != r.name) ++i;
+        if (i == keys.size()) {
+            keys.push_back(r.name);
+            cnt.push_back(0);
+            ms.push_back(0.0);
+        }
+        cnt[i] += 1;
+        ms[i] += t;
+        hipEventDestroy(r.start);
+        hipEventDestroy(r.stop);
+    }
+    g_prof.clear();
+    const int n = (int)std::min<size_t>(keys.size(), (size_t)std::max(max, 0));
+    for (int i = 0; i < n; ++i) {
+        if (names) {
+            std::strncpy(names[i], keys[i].c_str(), 63);
+            names[i][63] = '\0';
+        }
+        if (counts) counts[i] = cnt[i];
+        if (total_ms) total_ms[i] = ms[i];
+    }
+    return n;
+}
+
+}  // extern "C"

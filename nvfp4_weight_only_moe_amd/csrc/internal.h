@@ -1,0 +1,60 @@
+// Host-side interface between the C ABI (abi.cpp) and the kernel launchers
+// (*.hip).  Not part of the public API.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_w4a16.h"
+
+namespace moe {
+
+// ---- per-kernel event timing (moe_profile_begin / moe_profile_end)
+void prof_before(const char* name, hipStream_t s);
+void prof_after(hipStream_t s);
+
+// Launch helper: brackets the launch with profiling events when enabled and
+// reports launch errors.
+#define MOE_LAUNCH(name, kern, grid, block, shmem, stream, ...)                  \
+    do {                                                                         \
+        ::moe::prof_before(name, stream);                                        \
+        hipLaunchKernelGGL(kern, grid, block, shmem, stream, __VA_ARGS__);       \
+        ::moe::prof_after(stream);                                               \
+        if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;                 \
+    } while (0)
+
+// ---- quantize.hip
+moe_status launch_quantize_pack(const float* w, int E, int N, int K, const moe_nvfp4_tensor* out,
+                                hipStream_t s);
+moe_status launch_dequantize(const moe_nvfp4_tensor* t, float* w_out, hipStream_t s);
+moe_status launch_validate(const moe_nvfp4_tensor* t, uint32_t* d_flag, hipStream_t s);
+
+// ---- route.hip
+size_t route_workspace_bytes(int T, int E, int k);
+moe_status launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
+                        int32_t* slot_pos, void* ws, hipStream_t s);
+
+// ---- forward (moe_decode.hip / moe_prefill.hip)
+struct FwdArgs {
+    const uint16_t* x;
+    int T, H, I, E, k;
+    const moe_nvfp4_tensor *gate, *up, *down;
+    const int32_t* ids;
+    const float* topk_w;
+    const int32_t* counts;
+    const int32_t* offsets;
+    const int32_t* sorted_slots;
+    const int32_t* slot_pos;
+    uint16_t* out;
+    uint16_t* h;  // workspace: [T*k][I] bf16, expert-sorted rows
+    float* y;     // workspace: [T*k][H] fp32, expert-sorted rows (prefill only)
+};
+
+size_t forward_workspace_bytes(int T, int H, int I, int E, int k);
+bool decode_path_supported(int T, int H, int I);
+moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s);
+moe_status launch_forward_prefill(const FwdArgs& a, hipStream_t s);
+
+}  // namespace moe

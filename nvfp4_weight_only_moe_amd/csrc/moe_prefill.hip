@@ -1,0 +1,356 @@
+// Prefill-shape forward (many tokens): grouped GEMMs on the bf16 MFMA units.
+//
+// The W4A16 route dequantises the 4-bit weights to bf16 inside the GEMM and
+// feeds bf16 matrix instructions; no activation scale is involved ("GLM-5.3-
+// Flash on Blackwell", "The model loaded, served an API, and produced
+// garbage").  E2M1 * E4M3 is exact in bf16, so the MFMA sees the exact
+// weight up to the FP32 global scale, which is applied once per output in
+// the epilogue.
+//
+// k_grouped_gemm<GATEUP, BM> computes, for every expert e and its rows of the
+// expert-sorted permutation (offsets[e] .. offsets[e+1]):
+//   GATEUP: h[p, :] = bf16( silu(gg_e * x_t . G_e^T) * (gu_e * x_t . U_e^T) ),
+//           t = sorted_slots[p] / k          (rows gathered from x)
+//   DOWN:   y[p, :] = gd_e * h_p . D_e^T      (fp32)
+// Workgroup tile: BM rows x 128 h-columns (GATEUP, gate and up together) or
+// BM rows x 256 columns (DOWN); 4 waves, each owning 4 column subtiles of 16
+// and all BM rows, so each weight element is decoded by exactly one wave.
+// The BM x 128 activation tile of a K stage is staged in LDS (double
+// buffered); weights stream from HBM straight into registers with 16-byte
+// loads and are decoded there.  MFMA: v_mfma_f32_16x16x32_bf16.
+//
+// The K order inside a 128-wide stage is permuted identically for both
+// operands (lane group q holds k = 32q + 8s .. 32q + 8s + 7 at step s), which
+// lets one 16-byte load feed a lane's weight codes for all four steps.
+//
+// The grid is persistent; tiles are numbered expert by expert, within an
+// expert in groups of 8 row tiles x all column tiles, and handed out so that
+// each XCD (workgroup id mod 8) works on a contiguous run of tiles: row tiles
+// that share a weight column tile meet in the same L2.
+//
+// k_combine: out[t] = bf16( sum_j w[t,j] * y[slot_pos[t*k+j]] ), fp32, j order.
+#include "device_common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kGThreads = 256;
+constexpr int kBK = 128;                    // K per stage
+constexpr int kLdsRow = kBK * 2 + 16;       // bytes per staged activation row (padded)
+constexpr int kMGroup = 8;                  // row tiles per scheduling group
+
+struct GemmParams {
+    const uint16_t* a;          // GATEUP: x [T][K]; DOWN: h [T*k][K]
+    const int32_t* sorted_slots;
+    int topk;
+    int K, N, E;
+    const uint8_t *c0, *s0;     // gate (GATEUP) or down (DOWN)
+    const float* g0;
+    const uint8_t *c1, *s1;     // up (GATEUP only)
+    const float* g1;
+    const int32_t* counts;
+    const int32_t* offsets;
+    void* out;                  // GATEUP: h bf16 [T*k][N]; DOWN: y fp32 [T*k][N]
+    int ntn;                    // column tiles per expert
+};
+
+__device__ __forceinline__ bf16x8 decode8(uint32_t word, float s) {
+    const floatx2 p0 = e2m1x2_to_f32<0>(word);
+    const floatx2 p1 = e2m1x2_to_f32<1>(word);
+    const floatx2 p2 = e2m1x2_to_f32<2>(word);
+    const floatx2 p3 = e2m1x2_to_f32<3>(word);
+    u32x4 r;
+    r[0] = pack_bf16x2_exact(p0[0] * s, p0[1] * s);
+    r[1] = pack_bf16x2_exact(p1[0] * s, p1[1] * s);
+    r[2] = pack_bf16x2_exact(p2[0] * s, p2[1] * s);
+    r[3] = pack_bf16x2_exact(p3[0] * s, p3[1] * s);
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+template <bool GATEUP, int BM>
+__global__ void __launch_bounds__(kGThreads, BM >= 128 ? 1 : 2) k_grouped_gemm(GemmParams P) {
+    constexpr int MS = BM / 16;                 // row subtiles
+    constexpr int NS = 4;                       // column subtiles per wave
+    constexpr int APASS = BM / 16;              // 16 rows per pass of the A loader
+    constexpr int BN = GATEUP ? 128 : 256;      // output columns per tile
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ int s_prefix[MOE_MAX_EXPERTS + 1];
+    __shared__ int s_cnt[MOE_MAX_EXPERTS];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lcol = lane & 15, kq = lane >> 4;
+
+    // tiles per expert -> exclusive prefix
+    for (int e = tid; e < P.E; e += kGThreads) s_cnt[e] = ((P.counts[e] + BM - 1) / BM) * P.ntn;
+    __syncthreads();
+    block_exclusive_scan(s_cnt, s_prefix, P.E);
+    const int total = s_prefix[P.E];
+
+    const int G = gridDim.x;
+    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+    const bool remap = (G & 7) == 0;
+    const int nst = P.K / kBK;
+
+    for (int it = 0;; ++it) {
+        const int tile = it * G + (remap ? xcd * (G >> 3) + q : (int)blockIdx.x);
+        if (tile >= total) break;
+        // tile -> expert (largest e with prefix[e] <= tile)
+        int lo = 0, hi = P.E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_prefix[mid] <= tile) lo = mid; else hi = mid - 1;
+        }
+        const int e = lo;
+        const int L = tile - s_prefix[e];
+        const int ne = P.counts[e];
+        const int mte = (ne + BM - 1) / BM;
+        const int full = mte / kMGroup;
+        int mt, nt;
+        if (L < full * kMGroup * P.ntn) {
+            const int g = L / (kMGroup * P.ntn), r = L % (kMGroup * P.ntn);
+            nt = r / kMGroup;
+            mt = g * kMGroup + r % kMGroup;
+        } else {
+            const int r = L - full * kMGroup * P.ntn, last = mte - full * kMGroup;
+            nt = r / last;
+            mt = full * kMGroup + r % last;
+        }
+        const int p0 = P.offsets[e] + mt * BM;
+        const int rows = min(BM, ne - mt * BM);
+
+        // activation rows this thread stages (16 threads per row, 16 B each)
+        int64_t a_off[APASS];
+#pragma unroll
+        for (int ps = 0; ps < APASS; ++ps) {
+            const int r = (tid >> 4) + 16 * ps;
+            int64_t off = -1;
+            if (r < rows) {
+                const int64_t src_row = GATEUP ? (int64_t)(P.sorted_slots[p0 + r] / P.topk) : (int64_t)(p0 + r);
+                off = src_row * P.K + (tid & 15) * 8;
+            }
+            a_off[ps] = off;
+        }
+        // weight rows of this wave's column subtiles
+        const uint8_t* cp[NS];
+        const uint8_t* sp[NS];
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+            int col;
+            const uint8_t *cb, *sb;
+            if (GATEUP) {
+                col = nt * BN + wave * 32 + (ns & 1) * 16 + lcol;
+                cb = ns < 2 ? P.c0 : P.c1;
+                sb = ns < 2 ? P.s0 : P.s1;
+            } else {
+                col = nt * BN + wave * 64 + ns * 16 + lcol;
+                cb = P.c0;
+                sb = P.s0;
+            }
+            const int64_t row = (int64_t)e * P.N + col;
+            cp[ns] = cb + row * (P.K / 2) + kq * 16;
+            sp[ns] = sb + row * (P.K / 16) + kq * 2;
+        }
+
+        floatx4 acc[MS][NS];
+#pragma unroll
+        for (int i = 0; i < MS; ++i)
+#pragma unroll
+            for (int j = 0; j < NS; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+        uint4 a_reg[APASS];
+        uint4 b_code[NS];
+        uint32_t b_scale[NS];
+        auto load_stage = [&](int st) {
+            const int k0 = st * kBK;
+#pragma unroll
+            for (int ps = 0; ps < APASS; ++ps)
+                a_reg[ps] = a_off[ps] >= 0 ? *reinterpret_cast<const uint4*>(P.a + a_off[ps] + k0)
+                                           : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) {
+                b_code[ns] = *reinterpret_cast<const uint4*>(cp[ns] + k0 / 2);
+                b_scale[ns] = *reinterpret_cast<const uint16_t*>(sp[ns] + k0 / 16);
+            }
+        };
+        load_stage(0);
+        for (int st = 0; st < nst; ++st) {
+            uint8_t* buf = smem + (st & 1) * (BM * kLdsRow);
+#pragma unroll
+            for (int ps = 0; ps < APASS; ++ps)
+                *reinterpret_cast<uint4*>(buf + ((tid >> 4) + 16 * ps) * kLdsRow + (tid & 15) * 16) = a_reg[ps];
+            const uint4 cur_code[NS] = {b_code[0], b_code[1], b_code[2], b_code[3]};
+            const uint32_t cur_scale[NS] = {b_scale[0], b_scale[1], b_scale[2], b_scale[3]};
+            __syncthreads();
+            if (st + 1 < nst) load_stage(st + 1);
+            float sc[NS][2];
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) {
+                sc[ns][0] = e4m3_to_f32(cur_scale[ns] & 0xFFu);
+                sc[ns][1] = e4m3_to_f32(cur_scale[ns] >> 8);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                bf16x8 bfrag[NS];
+#pragma unroll
+                for (int ns = 0; ns < NS; ++ns) {
+                    const uint32_t w = s == 0 ? cur_code[ns].x : s == 1 ? cur_code[ns].y : s == 2 ? cur_code[ns].z : cur_code[ns].w;
+                    bfrag[ns] = decode8(w, sc[ns][s >> 1]);
+                }
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms) {
+                    const bf16x8 afrag = *reinterpret_cast<const bf16x8*>(buf + (ms * 16 + lcol) * kLdsRow + kq * 64 + s * 16);
+#pragma unroll
+                    for (int ns = 0; ns < NS; ++ns)
+                        acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[ns], acc[ms][ns], 0, 0, 0);
+                }
+            }
+        }
+
+        // epilogue: lane holds rows 4*kq + i (i < 4) of each 16-row subtile, column lcol
+        if (GATEUP) {
+            const float gg = P.g0[e], gu = P.g1[e];
+            uint16_t* h = reinterpret_cast<uint16_t*>(P.out);
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = ms * 16 + kq * 4 + i;
+                    if (r < rows) {
+#pragma unroll
+                        for (int ns = 0; ns < 2; ++ns) {
+                            const float a = gg * acc[ms][ns][i];
+                            const float b = gu * acc[ms][ns + 2][i];
+                            const int col = nt * BN + wave * 32 + ns * 16 + lcol;
+                            h[(int64_t)(p0 + r) * P.N + col] = f32_to_bf16_rne(silu(a) * b);
+                        }
+                    }
+                }
+        } else {
+            const float gd = P.g0[e];
+            float* y = reinterpret_cast<float*>(P.out);
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = ms * 16 + kq * 4 + i;
+                    if (r < rows) {
+#pragma unroll
+                        for (int ns = 0; ns < NS; ++ns) {
+                            const int col = nt * BN + wave * 64 + ns * 16 + lcol;
+                            y[(int64_t)(p0 + r) * P.N + col] = gd * acc[ms][ns][i];
+                        }
+                    }
+                }
+        }
+        __syncthreads();   // LDS buffers are rewritten by the next tile
+    }
+}
+
+// out[t, c..c+7] = bf16( sum_j w[t,j] * y[slot_pos[t*k+j], c..c+7] ), j ascending.
+__global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y, const float* __restrict__ topk_w,
+                                                 const int32_t* __restrict__ slot_pos, int T, int H, int k,
+                                                 uint16_t* __restrict__ out) {
+    const int t = blockIdx.y;
+    const int c = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (c >= H) return;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < k; ++j) {
+        const int slot = t * k + j;
+        const float w = topk_w[slot];
+        const float4* src = reinterpret_cast<const float4*>(y + (int64_t)slot_pos[slot] * H + c);
+        const float4 a = src[0], b = src[1];
+        acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
+        acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
+    }
+    uint4 o;
+    o.x = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+    o.y = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+    o.z = (uint32_t)f32_to_bf16_rne(acc[4]) | ((uint32_t)f32_to_bf16_rne(acc[5]) << 16);
+    o.w = (uint32_t)f32_to_bf16_rne(acc[6]) | ((uint32_t)f32_to_bf16_rne(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(out + (int64_t)t * H + c) = o;
+}
+
+int num_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+int persistent_grid(int64_t tiles_ub) {
+    int64_t g = std::min<int64_t>(tiles_ub, (int64_t)num_cus() * 2);
+    if (g >= 8) g = (g + 7) / 8 * 8;
+    return (int)std::max<int64_t>(g, 1);
+}
+
+template <bool GATEUP, int BM>
+moe_status launch_gemm(const GemmParams& P, int64_t slots, int E, hipStream_t s) {
+    const int64_t tiles_ub = (slots / BM + std::min<int64_t>(E, slots)) * P.ntn;
+    const size_t shmem = 2 * BM * kLdsRow;
+    static bool attr_set = false;  // >64 KB of dynamic LDS must be allowed explicitly
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_grouped_gemm<GATEUP, BM>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem) != hipSuccess)
+            return MOE_ERR_HIP;
+        attr_set = true;
+    }
+    const char* name = GATEUP ? "gemm_gateup" : "gemm_down";
+    MOE_LAUNCH(name, (k_grouped_gemm<GATEUP, BM>), dim3(persistent_grid(tiles_ub)), dim3(kGThreads), shmem, s, P);
+    return MOE_OK;
+}
+
+template <bool GATEUP>
+moe_status launch_gemm_bm(const GemmParams& P, int64_t slots, int E, hipStream_t s) {
+    const int64_t avg = slots / std::max<int64_t>(1, std::min<int64_t>(E, slots));
+    if (avg <= 32) return launch_gemm<GATEUP, 32>(P, slots, E, s);
+    if (avg <= 64) return launch_gemm<GATEUP, 64>(P, slots, E, s);
+    return launch_gemm<GATEUP, 128>(P, slots, E, s);
+}
+
+}  // namespace
+
+moe_status launch_forward_prefill(const FwdArgs& a, hipStream_t s) {
+    const int64_t slots = (int64_t)a.T * a.k;
+    GemmParams g{};
+    g.a = a.x;
+    g.sorted_slots = a.sorted_slots;
+    g.topk = a.k;
+    g.K = a.H;
+    g.N = a.I;
+    g.E = a.E;
+    g.c0 = a.gate->codes; g.s0 = a.gate->scales; g.g0 = a.gate->global_scale;
+    g.c1 = a.up->codes;   g.s1 = a.up->scales;   g.g1 = a.up->global_scale;
+    g.counts = a.counts;
+    g.offsets = a.offsets;
+    g.out = a.h;
+    g.ntn = a.I / 128;
+    moe_status st = launch_gemm_bm<true>(g, slots, a.E, s);
+    if (st != MOE_OK) return st;
+
+    GemmParams d{};
+    d.a = a.h;
+    d.sorted_slots = a.sorted_slots;
+    d.topk = a.k;
+    d.K = a.I;
+    d.N = a.H;
+    d.E = a.E;
+    d.c0 = a.down->codes; d.s0 = a.down->scales; d.g0 = a.down->global_scale;
+    d.counts = a.counts;
+    d.offsets = a.offsets;
+    d.out = a.y;
+    d.ntn = a.H / 256;
+    st = launch_gemm_bm<false>(d, slots, a.E, s);
+    if (st != MOE_OK) return st;
+
+    MOE_LAUNCH("combine", k_combine, dim3((a.H + 2047) / 2048, a.T), dim3(256), 0, s, (const float*)a.y, a.topk_w,
+               a.slot_pos, a.T, a.H, a.k, a.out);
+    return MOE_OK;
+}
+
+}  // namespace moe

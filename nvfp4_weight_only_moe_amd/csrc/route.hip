@@ -1,0 +1,263 @@
+// Router top-k + softmax and the expert-sorted permutation (hot path).
+//
+// The pages say every MoE layer has a BF16 router that is never quantized
+// ("GLM-5.3-Flash on Blackwell", "The quantization"); they do not print the
+// scoring rule.  Taken here: per token, the k largest fp32 logits (ties to
+// the lower expert index) in descending order, and a softmax over those k.
+//
+// The permutation is a stable counting sort of the flat slots t*k+j by
+// expert: a per-expert histogram, an exclusive scan, and a scatter whose
+// in-expert order is the flat order.  Atomics only ever count (LDS
+// histograms); positions come from ballots and prefix sums, so the result is
+// deterministic.
+//
+//   small T (one workgroup):  k_route_small                 (1 launch)
+//   large T:  k_route_topk_hist -> k_route_colscan -> k_route_scatter
+#include <float.h>
+#include <limits.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRT = 256;                 // threads per route workgroup
+constexpr int kRW = kRT / kWave;         // waves per route workgroup
+constexpr int kTokensPerBlock = 64;      // large-T path
+constexpr int kSmallMaxSlots = kTokensPerBlock * MOE_MAX_TOPK;  // small path: T <= 64
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+// One wave selects the top-k of one token's E logits and writes ids/weights.
+// EPL = logits per lane (E <= 64 * EPL).  Lane j ends up holding the j-th
+// selection; the weights are a softmax over the k selected logits.
+template <int EPL>
+__device__ void wave_topk(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids_out,
+                          float* __restrict__ w_out, int32_t* ids_lds) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float v[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int idx = lane + kWave * i;
+        v[i] = idx < E ? row[idx] : -INFINITY;
+    }
+    uint32_t taken = 0;
+    float my_v = 0.0f;
+    int my_i = 0;
+    for (int r = 0; r < k; ++r) {
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int idx = lane + kWave * i;
+            if (idx < E && !((taken >> i) & 1u) && better(v[i], idx, bv, bi)) {
+                bv = v[i];
+                bi = idx;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, kWave);
+            const int oi = __shfl_xor(bi, off, kWave);
+            if (better(ov, oi, bv, bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+        if (lane == r) {
+            my_v = bv;
+            my_i = bi;
+        }
+    }
+    const float m = __shfl(my_v, 0, kWave);
+    const float ex = lane < k ? expf(my_v - m) : 0.0f;
+    const float sum = wave_sum(ex);
+    if (lane < k) {
+        ids_out[lane] = my_i;
+        w_out[lane] = ex / sum;
+        if (ids_lds) ids_lds[lane] = my_i;
+    }
+}
+
+template <int EPL>
+__device__ void topk_tokens(const float* logits, int t0, int t1, int E, int k, int32_t* ids, float* w,
+                            int32_t* ids_lds /* indexed by (t - t0) * k, or null */) {
+    const int wave = threadIdx.x / kWave;
+    for (int t = t0 + wave; t < t1; t += kRW)
+        wave_topk<EPL>(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k,
+                       ids_lds ? ids_lds + (t - t0) * k : nullptr);
+}
+
+// Top-k for tokens [t0, t1), dispatched on the number of logits per lane.
+__device__ void topk_tokens_any(const float* logits, int t0, int t1, int E, int k, int32_t* ids, float* w,
+                                int32_t* ids_lds) {
+    if (E <= 64) topk_tokens<1>(logits, t0, t1, E, k, ids, w, ids_lds);
+    else if (E <= 128) topk_tokens<2>(logits, t0, t1, E, k, ids, w, ids_lds);
+    else if (E <= 256) topk_tokens<4>(logits, t0, t1, E, k, ids, w, ids_lds);
+    else if (E <= 512) topk_tokens<8>(logits, t0, t1, E, k, ids, w, ids_lds);
+    else topk_tokens<16>(logits, t0, t1, E, k, ids, w, ids_lds);
+}
+
+// Stable scatter of the flat slots [f0, f1) given the first free position of
+// each expert for this block (base[e], LDS).  Each wave takes a contiguous
+// run of slots; per-wave histograms give each wave its own starting
+// positions, and inside a wave a slot's rank among equal experts comes from
+// ballots on the expert id bits ("match any").
+__device__ void block_scatter(const int32_t* ids, int f0, int f1, const int* base, int E,
+                              int* hist /* [kRW][E] LDS */, int32_t* sorted_slots, int32_t* slot_pos) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int n = f1 - f0;
+    const int per_wave = ((n + kRW - 1) / kRW + kWave - 1) / kWave * kWave;
+    const int w0 = f0 + wave * per_wave;
+    const int w1 = min(f1, w0 + per_wave);
+    for (int i = threadIdx.x; i < kRW * E; i += kRT) hist[i] = 0;
+    __syncthreads();
+    for (int i = w0 + lane; i < w1; i += kWave) atomicAdd(&hist[wave * E + ids[i]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kRT) {
+        int run = base[e];
+        for (int w = 0; w < kRW; ++w) {
+            const int c = hist[w * E + e];
+            hist[w * E + e] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    int nbits = 1;
+    while ((1 << nbits) < E) ++nbits;
+    int* my_hist = hist + wave * E;
+    for (int c0 = w0; c0 < w1; c0 += kWave) {
+        const int i = c0 + lane;
+        const bool valid = i < w1;
+        const int e = valid ? ids[i] : 0;
+        uint64_t match = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t bal = __ballot(valid && bit);
+            match &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(match & lanemask_lt());
+        int pos = 0;
+        if (valid) pos = my_hist[e] + rank;
+        __builtin_amdgcn_wave_barrier();
+        if (valid && rank == 0) my_hist[e] += __popcll(match);
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            sorted_slots[pos] = i;
+            slot_pos[i] = pos;
+        }
+    }
+}
+
+// Whole route in one workgroup (T <= kTokensPerBlock).
+__global__ void __launch_bounds__(kRT) k_route_small(const float* __restrict__ logits, int T, int E, int k,
+                                                     int32_t* __restrict__ ids, float* __restrict__ w,
+                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_pos) {
+    __shared__ int32_t s_ids[kSmallMaxSlots];
+    __shared__ int s_cnt[MOE_MAX_EXPERTS];
+    __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+    __shared__ int s_hist[kRW * MOE_MAX_EXPERTS];
+    topk_tokens_any(logits, 0, T, E, k, ids, w, s_ids);
+    for (int e = threadIdx.x; e < E; e += kRT) s_cnt[e] = 0;
+    __syncthreads();
+    const int n = T * k;
+    for (int i = threadIdx.x; i < n; i += kRT) atomicAdd(&s_cnt[s_ids[i]], 1);
+    __syncthreads();
+    block_exclusive_scan(s_cnt, s_off, E);
+    for (int e = threadIdx.x; e < E; e += kRT) counts[e] = s_cnt[e];
+    for (int e = threadIdx.x; e <= E; e += kRT) offsets[e] = s_off[e];
+    block_scatter(s_ids, 0, n, s_off, E, s_hist, sorted_slots, slot_pos);
+}
+
+// Large T, step 1: top-k per token and a per-workgroup expert histogram.
+__global__ void __launch_bounds__(kRT) k_route_topk_hist(const float* __restrict__ logits, int T, int E, int k,
+                                                         int32_t* __restrict__ ids, float* __restrict__ w,
+                                                         int32_t* __restrict__ block_hist /* [B][E] */) {
+    __shared__ int32_t s_ids[kTokensPerBlock * MOE_MAX_TOPK];
+    __shared__ int s_cnt[MOE_MAX_EXPERTS];
+    const int t0 = blockIdx.x * kTokensPerBlock;
+    const int t1 = min(T, t0 + kTokensPerBlock);
+    topk_tokens_any(logits, t0, t1, E, k, ids, w, s_ids);
+    for (int e = threadIdx.x; e < E; e += kRT) s_cnt[e] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < (t1 - t0) * k; i += kRT) atomicAdd(&s_cnt[s_ids[i]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kRT) block_hist[(int64_t)blockIdx.x * E + e] = s_cnt[e];
+}
+
+// Large T, step 2: one wave per expert column: exclusive prefix over the
+// workgroups (in place) and the expert's total count.
+__global__ void __launch_bounds__(kRT) k_route_colscan(int32_t* __restrict__ block_hist, int B, int E,
+                                                       int32_t* __restrict__ counts) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int e = blockIdx.x * kRW + threadIdx.x / kWave;
+    if (e >= E) return;
+    int run = 0;
+    for (int b0 = 0; b0 < B; b0 += kWave) {
+        const int b = b0 + lane;
+        const int v = b < B ? block_hist[(int64_t)b * E + e] : 0;
+        int incl = v;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int t = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += t;
+        }
+        if (b < B) block_hist[(int64_t)b * E + e] = run + incl - v;
+        run += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) counts[e] = run;
+}
+
+// Large T, step 3: offsets (every workgroup recomputes them; workgroup 0
+// stores them) and the stable scatter of this workgroup's slots.
+__global__ void __launch_bounds__(kRT) k_route_scatter(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                       const int32_t* __restrict__ counts,
+                                                       const int32_t* __restrict__ block_prefix,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_pos) {
+    __shared__ int s_cnt[MOE_MAX_EXPERTS];
+    __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+    __shared__ int s_hist[kRW * MOE_MAX_EXPERTS];
+    for (int e = threadIdx.x; e < E; e += kRT) s_cnt[e] = counts[e];
+    __syncthreads();
+    block_exclusive_scan(s_cnt, s_off, E);
+    if (blockIdx.x == 0)
+        for (int e = threadIdx.x; e <= E; e += kRT) offsets[e] = s_off[e];
+    for (int e = threadIdx.x; e < E; e += kRT) s_off[e] += block_prefix[(int64_t)blockIdx.x * E + e];
+    __syncthreads();
+    const int t0 = blockIdx.x * kTokensPerBlock;
+    const int t1 = min(T, t0 + kTokensPerBlock);
+    block_scatter(ids, t0 * k, t1 * k, s_off, E, s_hist, sorted_slots, slot_pos);
+}
+
+}  // namespace
+
+size_t route_workspace_bytes(int T, int E, int k) {
+    (void)k;
+    if (T <= kTokensPerBlock) return 0;
+    const int64_t B = (T + kTokensPerBlock - 1) / kTokensPerBlock;
+    return (size_t)(B * E * sizeof(int32_t));
+}
+
+moe_status launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_slots, int32_t* slot_pos, void* ws, hipStream_t s) {
+    if (T <= kTokensPerBlock) {
+        MOE_LAUNCH("route_small", k_route_small, dim3(1), dim3(kRT), 0, s, logits, T, E, k, ids, w, counts,
+                   offsets, sorted_slots, slot_pos);
+        return MOE_OK;
+    }
+    const int B = (T + kTokensPerBlock - 1) / kTokensPerBlock;
+    int32_t* hist = reinterpret_cast<int32_t*>(ws);
+    MOE_LAUNCH("route_topk_hist", k_route_topk_hist, dim3(B), dim3(kRT), 0, s, logits, T, E, k, ids, w, hist);
+    MOE_LAUNCH("route_colscan", k_route_colscan, dim3((E + kRW - 1) / kRW), dim3(kRT), 0, s, hist, B, E, counts);
+    MOE_LAUNCH("route_scatter", k_route_scatter, dim3(B), dim3(kRT), 0, s, (const int32_t*)ids, T, E, k,
+               (const int32_t*)counts, (const int32_t*)hist, offsets, sorted_slots, slot_pos);
+    return MOE_OK;
+}
+
+}  // namespace moe

@@ -64,7 +64,17 @@ def quantize(w):
         raise ValueError("non-finite master weight")
     n, k = w.shape
     g = global_scale(np.max(np.abs(w)) if w.size else np.float32(0))
+    packed = np.empty((n, k // 2), dtype=np.uint8)
+    scales = np.empty((n, k // GROUP), dtype=np.uint8)
+    rows = max(1, (1 << 16) // k)          # a few rows at a time keeps temporaries small
+    for r0 in range(0, n, rows):
+        packed[r0:r0 + rows], scales[r0:r0 + rows] = _quantize_rows(w[r0:r0 + rows], g)
+    return packed, scales, np.float32(g)
 
+
+def _quantize_rows(w, g):
+    """Steps 3-5 for a block of rows with the tensor's global scale ``g``."""
+    n, k = w.shape
     groups = w.reshape(n, k // GROUP, GROUP)
     amax_g = np.max(np.abs(groups), axis=2)
     s_f = (amax_g / np.float32(6.0)) / g                       # two fp32 divides
@@ -79,7 +89,7 @@ def quantize(w):
                                       np.float32(0.0)), q).astype(np.float32)
     codes = e2m1_encode(q).reshape(n, k)
     packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
-    return packed, s_b.astype(np.uint8), np.float32(g)
+    return packed, s_b.astype(np.uint8)
 
 
 def unpack_codes(packed):
@@ -94,12 +104,18 @@ def unpack_codes(packed):
 
 def dequantize(packed, scales, g):
     """fp32 [N, K] weights from one packed tensor: (E2M1 * E4M3) * g."""
-    codes = unpack_codes(packed)
-    n, k = codes.shape
-    c = e2m1_decode(codes).astype(np.float32).reshape(n, k // GROUP, GROUP)
-    s = e4m3_decode(scales).astype(np.float32)[:, :, None]
-    w = (c * s).astype(np.float32) * np.float32(g)
-    return w.astype(np.float32).reshape(n, k)
+    packed = np.asarray(packed, dtype=np.uint8)
+    n, k = packed.shape[0], packed.shape[1] * 2
+    out = np.empty((n, k), dtype=np.float32)
+    rows = max(1, (1 << 16) // k)          # a few rows at a time keeps temporaries small
+    for r0 in range(0, n, rows):
+        codes = unpack_codes(packed[r0:r0 + rows])
+        m = codes.shape[0]
+        c = e2m1_decode(codes).astype(np.float32).reshape(m, k // GROUP, GROUP)
+        s = e4m3_decode(scales[r0:r0 + rows]).astype(np.float32)[:, :, None]
+        w = (c * s).astype(np.float32) * np.float32(g)
+        out[r0:r0 + rows] = w.reshape(m, k)
+    return out
 
 
 def quantize_layer(masters):

@@ -1,0 +1,105 @@
+"""The C ABI on the CPU: the library loads, exports what the header declares,
+and refuses bad arguments on the host before touching the device.
+
+Every call here fails (or is a T = 0 no-op) before any HIP call, so nothing
+needs a GPU.  Device pointers are fake, 16-byte aligned integers.
+"""
+import ctypes
+
+import pytest
+
+from nvfp4_weight_only_moe_amd import binding as b
+
+A = 0x10000  # a fake, aligned device address
+
+
+def T_(E, N, K, base=A):
+    return b.NVFP4TensorC(E, N, K, base, base + 0x100000, base + 0x200000)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return b.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = b.header_symbols()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code, name in b.STATUS.items():
+        assert b.status_string(code).startswith(name)
+    assert "UNKNOWN" in b.status_string(-99)
+
+
+def fwd(L, x=A, T=4, H=256, I=128, E=8, k=2, gate=None, up=None, down=None, ptr=A, out=A + 0x800000,
+        ws=A + 0x900000, ws_bytes=1 << 30):
+    gate = gate or T_(E, I, H)
+    up = up or T_(E, I, H, A + 0x1000000)
+    down = down or T_(E, H, I, A + 0x2000000)
+    p = [ptr] * 6
+    return L.moe_w4a16_forward(x, T, H, I, E, k, ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down),
+                               *p, out, ws, ws_bytes, None)
+
+
+def test_forward_argument_errors(L):
+    assert fwd(L, T=0) == b.MOE_OK                                 # no-op
+    assert fwd(L, T=-1) == -2                                      # SHAPE
+    assert fwd(L, H=200) == -2                                     # H % 256
+    assert fwd(L, I=100) == -2                                     # I % 128
+    assert fwd(L, k=9) == -4                                       # k > E
+    assert fwd(L, E=2000, k=2) == -4                               # E > 1024
+    assert fwd(L, k=33, E=64) == -4                                # k > 32
+    assert fwd(L, x=0) == -1                                       # null x
+    assert fwd(L, ptr=0) == -1                                     # null routing arrays
+    assert fwd(L, x=A + 4) == -3                                   # misaligned
+    assert fwd(L, out=A) == -1                                     # out aliases x
+    assert fwd(L, ws=0) == -7                                      # no workspace
+    assert fwd(L, ws_bytes=16) == -7                               # workspace too small
+    assert fwd(L, gate=T_(8, 128, 512)) == -2                      # wrong gate K
+    assert fwd(L, down=T_(8, 128, 256)) == -2                      # down not [H, I]
+    assert fwd(L, up=b.NVFP4TensorC(8, 128, 256, A, A, 0)) == -1   # missing global scale
+    assert fwd(L, up=b.NVFP4TensorC(8, 128, 256, A + 8, A, A)) == -3
+    assert L.moe_w4a16_forward(A, 4, 256, 128, 8, 2, None, None, None, A, A, A, A, A, A, A, A, 1 << 30, None) == -1
+
+
+def test_route_argument_errors(L):
+    def r(T=4, E=8, k=2, ptr=A, ws=A, ws_bytes=1 << 20):
+        return L.moe_route_topk(ptr, T, E, k, ptr, ptr, ptr, ptr, ptr, ptr, ws, ws_bytes, None)
+    assert r(T=0) == b.MOE_OK
+    assert r(T=-1) == -2
+    assert r(k=0) == -2
+    assert r(k=9) == -4
+    assert r(E=1025, k=2) == -4
+    assert r(ptr=0) == -1
+    assert r(ptr=A + 2) == -3
+    big = 100000
+    assert L.moe_route_workspace_size(big, 256, 8) > 0
+    assert r(T=big, E=256, k=8, ws_bytes=0) == -7
+    assert r(T=big, E=256, k=8, ws=0) == -7
+    assert L.moe_route_workspace_size(1, 256, 8) == 0
+
+
+def test_quantize_dequantize_validate_argument_errors(L):
+    t = T_(2, 64, 256)
+    assert L.moe_w4a16_quantize_pack(None, 2, 64, 256, ctypes.byref(t), None) == -1
+    assert L.moe_w4a16_quantize_pack(A + 0x4000000, 2, 64, 48, ctypes.byref(t), None) == -2   # K % 32
+    assert L.moe_w4a16_quantize_pack(A + 0x4000000, 2, 64, 128, ctypes.byref(t), None) == -2  # K mismatch
+    assert L.moe_w4a16_quantize_pack(A + 0x4000004, 2, 64, 256, ctypes.byref(t), None) == -3
+    assert L.moe_w4a16_quantize_pack(A, 2, 64, 256, ctypes.byref(t), None) == -1              # w overlaps out
+    assert L.moe_w4a16_quantize_pack(A + 0x4000000, 2, 64, 256, None, None) == -1
+    assert L.moe_w4a16_quantize_pack(A + 0x4000000, 2000, 64, 256, ctypes.byref(T_(2000, 64, 256)), None) == -4
+    assert L.moe_w4a16_dequantize(ctypes.byref(t), None, None) == -1
+    assert L.moe_w4a16_dequantize(ctypes.byref(T_(2, 64, 40)), A, None) == -2
+    assert L.moe_w4a16_validate(None, None) == -1
+    assert L.moe_w4a16_validate(ctypes.byref(T_(0, 64, 256)), None) == -2
+
+
+def test_workspace_sizes(L):
+    assert L.moe_w4a16_workspace_size(0, 5120, 1536, 256, 8) == 0
+    need = L.moe_w4a16_workspace_size(16, 256, 128, 8, 2)
+    assert need >= 16 * 2 * (128 * 2 + 256 * 4)
+    assert need % 256 == 0

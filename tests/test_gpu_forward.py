@@ -1,0 +1,106 @@
+"""GPU parity: the layer forward against the oracle on small seeded problems
+(decode path: T <= 8 with H % 1024 == 0 and I % 512 == 0; grouped-GEMM path
+otherwise), ragged and skewed routing, edge cases, determinism."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, Problem, bf16_bits_to_f64, compare_out, log, to_dev
+from nvfp4_weight_only_moe_amd import binding as B
+from nvfp4_weight_only_moe_amd import workloads as wls
+
+pytestmark = pytest.mark.gpu
+
+
+def run_and_compare(p, where):
+    out, r, _ = p.run_gpu()
+    assert np.array_equal(r.topk_ids.cpu().numpy(), p.ids)
+    got = bf16_bits_to_f64(out)
+    ref = p.reference()
+    compare_out(got, ref, where)
+    # the diagnostic oracle rounds h to bf16 like the device: much closer
+    tight = p.reference(round_h_bf16=True)
+    rel = np.linalg.norm(got - tight) / np.linalg.norm(tight)
+    log(f"{where}: rel_fro vs bf16-h oracle {rel:.3e}")
+    return got
+
+
+def test_tiny_workload():
+    wl = wls.WORKLOADS[0]
+    ms = [wls.masters(wl, p) for p in (wls.GATE, wls.UP, wls.DOWN)]
+    xb, x = wls.activations(wl)
+    lg = wls.logits(wl)
+    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in ms)
+    r = B.moe_route_topk(to_dev(lg), wl.k)
+    out = B.moe_w4a16_forward(to_dev(xb, torch.int16), gate, up, down, r)
+    torch.cuda.synchronize()
+    layer = {n: oracle.quantize_layer(m) for n, m in zip(("gate", "up", "down"), ms)}
+    ids, w = oracle.route_topk(lg, wl.k)
+    ref = oracle.moe_forward(x, layer, ids, w)
+    compare_out(bf16_bits_to_f64(out), ref, wl.name)
+
+
+@pytest.mark.parametrize("T,H,I,E,k,seed", [
+    (1, 1024, 512, 8, 2, 1),       # decode path
+    (3, 1024, 512, 16, 4, 2),
+    (8, 2048, 1024, 32, 8, 3),
+    (8, 1024, 1536, 8, 8, 4),      # k == E: every expert touched by every token
+    (9, 1024, 512, 16, 2, 5),      # just past the decode path
+    (33, 256, 128, 8, 2, 6),       # grouped GEMM, 32-row tiles
+    (100, 512, 384, 16, 4, 7),     # 64-row tiles, ragged
+    (257, 256, 256, 4, 2, 8),      # 128-row tiles, several row tiles per expert
+    (40, 768, 256, 1, 1, 9),       # E = 1, k = 1
+])
+def test_random_shapes(T, H, I, E, k, seed):
+    run_and_compare(Problem(T, H, I, E, k, seed), f"T{T}-H{H}-I{I}-E{E}-k{k}")
+
+
+@pytest.mark.parametrize("T,H,I", [(6, 1024, 512), (300, 256, 128)])
+def test_all_tokens_on_one_expert(T, H, I):
+    E, k = 16, 2
+    r = np.random.default_rng(T)
+    lg = r.standard_normal((T, E)).astype(np.float32)
+    lg[:, 11] += 40.0
+    run_and_compare(Problem(T, H, I, E, k, 20 + T, logits=lg), f"skew-T{T}")
+
+
+def test_zero_tokens_is_noop():
+    p = Problem(4, 256, 128, 8, 2, 30)
+    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
+    r = B.moe_route_topk(to_dev(p.logits[:0]), 2)
+    out = torch.full((0, 256), 7, dtype=torch.int16, device=DEV)
+    B.moe_w4a16_forward(torch.zeros((0, 256), dtype=torch.int16, device=DEV), gate, up, down, r, out=out)
+    torch.cuda.synchronize()
+
+
+def test_zero_input_gives_zero_output():
+    p = Problem(5, 256, 128, 8, 2, 31)
+    p.xb[:] = 0
+    out, _, _ = p.run_gpu()
+    assert not bf16_bits_to_f64(out).any()
+
+
+@pytest.mark.parametrize("T,H,I", [(8, 1024, 512), (120, 512, 256)])
+def test_deterministic(T, H, I):
+    p = Problem(T, H, I, 16, 4, 40)
+    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
+    r = B.moe_route_topk(to_dev(p.logits), 4)
+    xb = to_dev(p.xb, torch.int16)
+    a = B.moe_w4a16_forward(xb, gate, up, down, r)
+    b = B.moe_w4a16_forward(xb, gate, up, down, r)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_magnitude_not_correlation_only():
+    """A layer whose global scales are scaled by 25 keeps cosine ~1 but must
+    fail the output bar -- the check that catches a wrong scale
+    ('GLM-5.3-Flash on Blackwell': a 25x magnitude error at cosine 0.996)."""
+    p = Problem(6, 1024, 512, 8, 2, 50)
+    out, r, (gate, up, down) = p.run_gpu()
+    down.global_scale.mul_(25.0)
+    bad = B.moe_w4a16_forward(to_dev(p.xb, torch.int16), gate, up, down, r)
+    torch.cuda.synchronize()
+    with pytest.raises(AssertionError):
+        compare_out(bf16_bits_to_f64(bad), p.reference(), "scaled-by-25")
