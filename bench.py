@@ -1,0 +1,285 @@
+"""Benchmark of the NVFP4 W4A16 routed-expert MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config C] [--gpus 1]
+
+A step is one pass of the hot path over one batch of synthetic input:
+router top-k + permutation (moe_route_topk) and the layer forward
+(moe_w4a16_forward: gate/up grouped GEMM + SwiGLU, down grouped GEMM,
+routing-weighted combine).  Quantization is load time and is not in a step.
+
+Default workload: decode, 1 token, hidden 5120, intermediate 1536, 256
+experts, top-8 (the "decode-t1" workload).  Inputs are resident in HBM before
+timing.  For decode workloads the step cycles through L distinct device
+copies of the packed layer so that the 256 MB Infinity Cache cannot serve the
+weights (a model has one such layer per MoE block); the steps are replayed
+from a HIP graph that holds L consecutive steps.
+
+Prints one JSON line: the driver's fields plus "roofline" (dominant kernel,
+HIP-event timed on its own stream) and "cpu_baseline" (the CPU oracle timed
+on a bounded sample of the same workload).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+METRIC = "MoE-layer tokens/s + weight GB/s (decode) and TFLOP/s (prefill), % roofline"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", type=int, default=1, help="workload index (1 = decode, 1 token)")
+    ap.add_argument("--copies", type=int, default=None, help="layer copies cycled through (decode)")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def packed_bytes(N, K):
+    return N * K // 2 + N * K // 16 + 4
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer fits one MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from nvfp4_weight_only_moe_amd import binding as B
+    from nvfp4_weight_only_moe_amd import workloads as wls
+
+    wl = wls.WORKLOADS[args.config]
+    decode = wl.T <= 8
+    steps = args.steps or (400 if decode else (40 if wl.T <= 2048 else 10))
+    warmup = args.warmup if args.warmup is not None else (40 if decode else 3)
+    copies = args.copies or (16 if decode else 1)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    # ---------------------------------------------------------------- layer
+    t0 = time.time()
+    from concurrent.futures import ThreadPoolExecutor
+    threads = min(16, len(os.sched_getaffinity(0)))
+    layer = {}
+    quant_ms = 0.0
+    for proj, name in ((wls.GATE, "gate"), (wls.UP, "up"), (wls.DOWN, "down")):
+        n, k = wls.proj_shape(wl, proj)
+        t = B.NVFP4Tensor.empty(wl.E, n, k, dev)
+        batch = 32
+        with ThreadPoolExecutor(threads) as ex:
+            for e0 in range(0, wl.E, batch):
+                ms = np.stack(list(ex.map(lambda e: wls.master(wl, proj, e), range(e0, e0 + batch))))
+                w = torch.from_numpy(ms).to(dev)
+                sl = B.NVFP4Tensor(t.codes[e0:e0 + batch], t.scales[e0:e0 + batch], t.global_scale[e0:e0 + batch])
+                torch.cuda.synchronize()
+                q0 = time.perf_counter()
+                B.moe_w4a16_quantize_pack(w, out=sl)
+                torch.cuda.synchronize()
+                quant_ms += (time.perf_counter() - q0) * 1e3
+                del w
+        layer[name] = t
+        log(f"packed {name} ({time.time() - t0:.1f} s)")
+    for name in ("gate", "up", "down"):
+        B.moe_w4a16_validate(layer[name])
+    layers = [layer]
+    for c in range(1, copies):
+        layers.append({n: B.NVFP4Tensor(t.codes.clone(), t.scales.clone(), t.global_scale.clone())
+                       for n, t in layer.items()})
+    torch.cuda.synchronize()
+    log(f"{copies} layer copies resident ({time.time() - t0:.1f} s)")
+
+    # ---------------------------------------------------------------- inputs
+    xb, _ = wls.activations(wl)
+    lg = wls.logits(wl)
+    x_d = torch.from_numpy(xb.view(np.int16)).to(dev)
+    lg_d = torch.from_numpy(lg).to(dev)
+    route = B.Routing.empty(wl.T, wl.E, wl.k, dev)
+    out = torch.empty((wl.T, wl.H), dtype=torch.int16, device=dev)
+    ws = B.forward_workspace(wl.T, wl.H, wl.I, wl.E, wl.k, dev)
+
+    def step(i):
+        B.moe_route_topk(lg_d, wl.k, out=route)
+        L = layers[i % copies]
+        B.moe_w4a16_forward(x_d, L["gate"], L["up"], L["down"], route, out=out, ws=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+    counts = route.counts.cpu().numpy()
+    U = int((counts > 0).sum())
+
+    # ---------------------------------------------------------------- eager timing
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(n)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    eager_ms = timed(lambda n: [step(i) for i in range(n)], steps)
+    assert torch.equal(out, ref_out)
+    log(f"eager: {eager_ms * 1e3:.2f} us/step")
+
+    # ---------------------------------------------------------------- graph timing
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(2):
+                step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(copies):
+                step(i)
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref_out):
+            log("graph replay output differs from eager: graph timing discarded")
+        else:
+            reps = max(1, steps // copies)
+            for _ in range(3):
+                g.replay()
+            graph_ms = timed(lambda n: [g.replay() for _ in range(n)], reps) / copies
+            assert torch.equal(out, ref_out)
+            log(f"graph: {graph_ms * 1e3:.2f} us/step")
+    ms_per_step = graph_ms if graph_ms is not None else eager_ms
+
+    # ---------------------------------------------------------------- per-kernel timing
+    B.moe_profile_begin(64 * max(steps, 1))
+    for i in range(steps):
+        step(i)
+    prof = B.moe_profile_end()
+    per_kernel_us = {k: round(v[1] / v[0] * 1e3, 3) for k, v in prof.items()}
+    dominant = max(prof, key=lambda k: prof[k][1] / steps)
+    dom_us = prof[dominant][1] / prof[dominant][0] * 1e3
+    log(f"per-kernel us: {per_kernel_us}")
+
+    # ---------------------------------------------------------------- roofline
+    H, I, T, k = wl.H, wl.I, wl.T, wl.k
+    w_gu = 2 * packed_bytes(I, H)
+    w_d = packed_bytes(H, I)
+    alg_bytes_step = U * (w_gu + w_d) + T * H * 2 * 2 + T * wl.E * 4
+    flops_step = 6.0 * T * k * H * I
+    kernel_work = {
+        "dec_gateup": ("hbm", U * w_gu + T * H * 2),
+        "dec_down": ("hbm", U * w_d + T * H * 2),
+        "gemm_gateup": ("mfma", 4.0 * T * k * H * I),
+        "gemm_down": ("mfma", 2.0 * T * k * H * I),
+    }
+    if dominant in kernel_work:
+        bound, work = kernel_work[dominant]
+    else:
+        bound, work = "hbm", alg_bytes_step
+    if bound == "hbm":
+        achieved = work / (dom_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dominant,
+                    "kernel_avg_us": round(dom_us, 3), "algorithmic_bytes_per_launch": int(work)}
+    else:
+        achieved = work / (dom_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": dominant, "kernel_avg_us": round(dom_us, 3),
+                    "algorithmic_flops_per_launch": work}
+
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    step_gbps = alg_bytes_step / (ms_per_step * 1e-3) / 1e9
+    step_tflops = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of 268435456 bytes (read 256 MiB, write 256 MiB each)")
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, lg, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": wl.E, "k": k,
+                   "layer_copies": copies, "hip_graph": graph_ms is not None, "touched_experts": U},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "step_algorithmic_GBps": round(step_gbps, 1), "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "weight_GBps": round(U * (w_gu + w_d) / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_TFLOPs": round(step_tflops, 3), "step_mfma_frac": round(step_tflops / BF16_PEAK_TFLOPS, 5),
+        "eager_ms_per_step": round(eager_ms, 6), "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 6),
+        "per_kernel_us": per_kernel_us, "quantize_pack_ms_total": round(quant_ms, 2),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(wl, logits, budget_s):
+    """The oracle (fp64 numpy) on the host: route + FFN + combine for a
+    bounded sample of the workload's tokens, expert quantization excluded."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    from nvfp4_weight_only_moe_amd import workloads as wls
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    _, x = wls.activations(wl)
+    n_tok = 1 if wl.T <= 8 else 2
+    tokens = list(range(n_tok))
+    ids, _ = oracle.route_topk(logits[:n_tok], wl.k)
+    experts = sorted(set(int(e) for e in ids.ravel()))
+    threads = min(16, len(os.sched_getaffinity(0)))
+    todo = [(p, n, e) for p, n in ((wls.GATE, "gate"), (wls.UP, "up"), (wls.DOWN, "down")) for e in experts]
+    with ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(lambda a: oracle.quantize(wls.master(wl, a[0], a[2])), todo))
+    layer = {n: ({}, {}, {}) for n in ("gate", "up", "down")}
+    for (p, n, e), (c, s, g) in zip(todo, res):
+        layer[n][0][e], layer[n][1][e], layer[n][2][e] = c, s, g
+    runs, t_total = 0, 0.0
+    while t_total < budget_s and runs < 50:
+        t0 = time.perf_counter()
+        ids_s, w_s = oracle.route_topk(logits[:n_tok], wl.k)
+        oracle.moe_forward(x[:n_tok], layer, ids_s, w_s, tokens=tokens)
+        t_total += time.perf_counter() - t0
+        runs += 1
+    per_run = t_total / runs
+    return {"value": round(n_tok / per_run, 4), "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{n_tok} token(s) of {wl.name}: route + SwiGLU FFN of {len(experts)} experts (dequantize "
+                      f"+ fp64) + combine, {runs} runs, {t_total:.1f} s; expert quantization excluded",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()
