@@ -58,7 +58,7 @@ void prof_before(const char* name, hipStream_t s) {
     if ((int)g_prof.size() >= g_prof_max) return;
     ProfRec r{name, nullptr, nullptr};
     if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return;
-    hipEventRecord(r.start, s);
+    (void)hipEventRecord(r.start, s);
     g_prof.push_back(r);
     g_prof_open = &g_prof.back();
 }
@@ -67,8 +67,21 @@ void prof_after(hipStream_t s) {
     if (!g_prof_on) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (!g_prof_open) return;
-    hipEventRecord(g_prof_open->stop, s);
+    (void)hipEventRecord(g_prof_open->stop, s);
     g_prof_open = nullptr;
+}
+
+moe_status allow_dynamic_lds(const void* kernel, size_t bytes) {
+    static std::mutex mu;
+    static std::vector<std::pair<const void*, size_t>> done;
+    std::lock_guard<std::mutex> lk(mu);
+    for (auto& d : done)
+        if (d.first == kernel && d.second >= bytes) return MOE_OK;
+    if (bytes > 64 * 1024 &&
+        hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess)
+        return MOE_ERR_HIP;
+    done.emplace_back(kernel, bytes);
+    return MOE_OK;
 }
 
 size_t forward_workspace_bytes(int T, int H, int I, int E, int k) {
@@ -136,7 +149,7 @@ moe_status moe_w4a16_validate(const moe_nvfp4_tensor* t, hipStream_t stream) {
     if (st == MOE_OK && hipMemcpyAsync(&flag, d_flag, sizeof(flag), hipMemcpyDeviceToHost, stream) != hipSuccess)
         st = MOE_ERR_HIP;
     if (st == MOE_OK && hipStreamSynchronize(stream) != hipSuccess) st = MOE_ERR_HIP;
-    hipFree(d_flag);
+    (void)hipFree(d_flag);
     if (st != MOE_OK) return st;
     if (flag & 1u) return MOE_ERR_NONFINITE;
     if (flag & 6u) return MOE_ERR_BAD_SCALE;
@@ -216,15 +229,15 @@ moe_status moe_w4a16_forward(const uint16_t* d_x, int32_t T, int32_t H, int32_t 
     const size_t slots = (size_t)T * k;
     a.h = reinterpret_cast<uint16_t*>(ws);
     a.y = reinterpret_cast<float*>(ws + round_up(slots * I * sizeof(uint16_t), 256));
-    if (decode_path_supported(T, H, I)) return launch_forward_decode(a, stream);
+    if (decode_path_supported(T, k, H, I)) return launch_forward_decode(a, stream);
     return launch_forward_prefill(a, stream);
 }
 
 moe_status moe_profile_begin(int32_t max_launches) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     for (auto& r : g_prof) {
-        hipEventDestroy(r.start);
-        hipEventDestroy(r.stop);
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
     }
     g_prof.clear();
     g_prof.reserve(max_launches > 0 ? max_launches : 0);
@@ -253,8 +266,8 @@ int32_t moe_profile_end(char (*names)[64], int32_t* counts, double* total_ms, in
         }
         cnt[i] += 1;
         ms[i] += t;
-        hipEventDestroy(r.start);
-        hipEventDestroy(r.stop);
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
     }
     g_prof.clear();
     const int n = (int)std::min<size_t>(keys.size(), (size_t)std::max(max, 0));

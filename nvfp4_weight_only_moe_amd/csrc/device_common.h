@@ -39,14 +39,14 @@ __device__ __forceinline__ bf16x2 e2m1x2_to_bf16(uint32_t word) {
     return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, SEL);
 }
 
-// E4M3 ("FN") byte -> fp32, exactly, from the bit fields.  NaN patterns are
-// rejected by moe_w4a16_validate and are not special-cased here.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20))
-                        : (float)m * 0x1p-9f;
-    return (b & 0x80u) ? -mag : mag;
+// E4M3 ("FN") byte SEL of `word` -> fp32, exactly, with gfx950's FP8
+// conversion (OCP E4M3: bias 7, subnormals m * 2^-9, 0x7F/0xFF NaN; NaN
+// patterns are rejected by moe_w4a16_validate).
+template <int SEL>
+__device__ __forceinline__ float e4m3_byte_to_f32(uint32_t word) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)word, SEL);
 }
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) { return e4m3_byte_to_f32<0>(b); }
 
 // fp32 pair -> bf16 pair by truncation.  Only used on values that are exact
 // in bf16 (E2M1 * E4M3 products), where truncation is exact.
@@ -72,7 +72,95 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
+// ---------------------------------------------------------------- LDS DMA
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One wave copies 64 x 16 B (1 KiB) from global memory straight into LDS
+// (gfx950 global_load_lds_dwordx4): lane i's 16 bytes land at lds + 16 i.
+// No registers are involved; completion is tracked like any vector load.
+__device__ __forceinline__ void wave_copy_1k_to_lds(const uint4* __restrict__ src, uint4* lds) {
+    const int lane = threadIdx.x & 63;
+    __builtin_amdgcn_global_load_lds(src + lane, (lds_void*)lds, 16, 0, 0);
+}
+
+// Wait for every outstanding memory operation of this wave.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (they complete in issue order); LDS and scalar counters are not waited on.
+template <int N>
+__device__ __forceinline__ void wait_vmem_at_most() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // ---------------------------------------------------------------- wave ops
+// DPP moves (GFX9 data-parallel primitives): a lane reads a neighbour's
+// register without going through LDS.  Lanes whose source is outside the
+// row, or whose row is masked off, receive `old`.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float old, float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                 __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                                                 0xF, false));
+}
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// Inclusive prefix sums inside each row of 16 lanes (lane 15 of a row holds
+// the row total).
+__device__ __forceinline__ float row_prefix_sum(float v) {
+    v += dpp_f32<kDppRowShr1>(0.0f, v);
+    v += dpp_f32<kDppRowShr2>(0.0f, v);
+    v += dpp_f32<kDppRowShr4>(0.0f, v);
+    v += dpp_f32<kDppRowShr8>(0.0f, v);
+    return v;
+}
+
+// Sum over all 64 lanes, returned in every lane (DPP, no LDS traffic).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v = row_prefix_sum(v);
+    v += dpp_f32<kDppRowBcast15, 0xA>(0.0f, v);   // rows 1, 3 += lane 15 / 47
+    v += dpp_f32<kDppRowBcast31, 0xC>(0.0f, v);   // rows 2, 3 += lane 31
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Sums over lanes 0..31 and 32..63; returns the sum of the caller's half.
+__device__ __forceinline__ float half_wave_sum_dpp(float v) {
+    v = row_prefix_sum(v);
+    v += dpp_f32<kDppRowBcast15, 0xA>(0.0f, v);   // lane 31 = rows 0+1, lane 63 = rows 2+3
+    const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+    const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    return (threadIdx.x & 32) ? hi : lo;
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i32(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes (lane i gets lanes 0..i), DPP only.
+__device__ __forceinline__ int wave_inclusive_scan_dpp(int v) {
+    v += dpp_i32<kDppRowShr1>(0, v);
+    v += dpp_i32<kDppRowShr2>(0, v);
+    v += dpp_i32<kDppRowShr4>(0, v);
+    v += dpp_i32<kDppRowShr8>(0, v);
+    v += dpp_i32<kDppRowBcast15, 0xA>(0, v);
+    v += dpp_i32<kDppRowBcast31, 0xC>(0, v);
+    return v;
+}
+
+// Maximum over all 64 lanes (NaN-free inputs), returned in every lane.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = fmaxf(v, dpp_f32<kDppRowShr1>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<kDppRowShr2>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<kDppRowShr4>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<kDppRowShr8>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<kDppRowBcast15, 0xA>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<kDppRowBcast31, 0xC>(-INFINITY, v));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
@@ -91,25 +179,40 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
     return lane ? (~0ull >> (64 - lane)) : 0ull;
 }
 
-// Index of the b-th expert with a nonzero count (ascending), or -1.  Called
-// by a whole wave; counts has E entries.
-__device__ __forceinline__ int nth_active_expert(const int32_t* __restrict__ counts, int E, int b) {
+// The b-th expert with a nonzero count (ascending), its count and its first
+// row in expert-sorted order (the exclusive prefix of the counts), or e = -1.
+// Called by a whole wave.  All count loads are issued before any is used
+// (EPL = ceil(E / 64) per lane), so the lookup costs one memory latency.
+struct ActiveExpert {
+    int e, count, first_row;
+};
+template <int EPL>
+__device__ __forceinline__ ActiveExpert nth_active_expert(const int32_t* __restrict__ counts, int E, int b) {
     const int lane = threadIdx.x & (kWave - 1);
-    int seen = 0;
-    for (int base = 0; base < E; base += kWave) {
-        const int e = base + lane;
-        const bool act = e < E && counts[e] > 0;
-        const uint64_t m = __ballot(act);
+    int c[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = i * kWave + lane;
+        c[i] = e < E ? counts[e] : 0;
+    }
+    int seen = 0, rows = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const uint64_t m = __ballot(c[i] > 0);
         const int n = __popcll(m);
+        const int incl = wave_inclusive_scan_dpp(c[i]);   // counts over the lanes of this chunk
         if (b < seen + n) {
-            const int want = b - seen;  // the want-th set bit of m
-            const int rank = __popcll(m & lanemask_lt());
-            const uint64_t hit = __ballot(act && rank == want);
-            return base + __ffsll((unsigned long long)hit) - 1;
+            const int want = b - seen;
+            const uint64_t hit = __ballot(c[i] > 0 && __popcll(m & lanemask_lt()) == want);
+            const int src = __ffsll((unsigned long long)hit) - 1;
+            const int cnt = __builtin_amdgcn_readlane(c[i], src);
+            const int excl = __builtin_amdgcn_readlane(incl, src) - cnt;
+            return ActiveExpert{i * kWave + src, cnt, rows + excl};
         }
         seen += n;
+        rows += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
-    return -1;
+    return ActiveExpert{-1, 0, 0};
 }
 
 // Exclusive scan of cnt[0..E) into off[0..E] (off[E] = total) by a

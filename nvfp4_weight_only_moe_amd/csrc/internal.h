@@ -24,6 +24,10 @@ void prof_after(hipStream_t s);
         if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;                 \
     } while (0)
 
+// Allow `bytes` of dynamic LDS for `kernel` (HIP needs an explicit opt-in
+// above 64 KB).  Cached per kernel; host-side only, never captured.
+moe_status allow_dynamic_lds(const void* kernel, size_t bytes);
+
 // ---- quantize.hip
 moe_status launch_quantize_pack(const float* w, int E, int N, int K, const moe_nvfp4_tensor* out,
                                 hipStream_t s);
@@ -53,7 +57,7 @@ struct FwdArgs {
 };
 
 size_t forward_workspace_bytes(int T, int H, int I, int E, int k);
-bool decode_path_supported(int T, int H, int I);
+bool decode_path_supported(int T, int k, int H, int I);
 moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s);
 moe_status launch_forward_prefill(const FwdArgs& a, hipStream_t s);
 

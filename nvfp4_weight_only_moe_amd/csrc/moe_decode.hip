@@ -10,182 +10,285 @@
 //
 // Two kernels:
 //   k_dec_gateup: one workgroup per (touched expert, block of rows of I).
-//     Lanes split K: lane l owns the 16-groups l, l+64, ... of every row, so
-//     each wave load is a contiguous 512 B run of codes and its x chunk is
-//     loaded once and reused for every row the wave owns.  Codes decode to
-//     bf16 pairs (gfx950 FP4 conversion) and meet x in v_dot2_f32_bf16; the
-//     group scale multiplies each 16-term partial sum, the global scale the
-//     row total.  SwiGLU runs on the reduced gate/up pair; h is rounded once
-//     to bf16 and stored in expert-sorted row order.
-//   k_dec_down: one wave per 2 output rows of H, looping over every touched
-//     expert in ascending order and every token of that expert, so the
+//     The expert's tokens are staged once in LDS.  Lanes split K: lane l
+//     owns the 16-groups l, l+64, ... of a row, so each wave load is a
+//     contiguous 512 B run of codes.  A wave walks its rows with the next
+//     row's gate and up codes already in flight (register double buffer).
+//     Codes decode to bf16 pairs (gfx950 FP4 conversion) and meet x in
+//     v_dot2_f32_bf16; the group scale multiplies each 16-term partial sum,
+//     the global scale the row total.  Row sums are DPP reductions; SwiGLU
+//     runs on the gate/up pair and h is rounded once to bf16 and stored in
+//     expert-sorted row order.
+//   k_dec_down: one workgroup per block of output rows of H; every wave owns
+//     two rows (one per half-wave) and loops over every touched expert in
+//     ascending order and every token of that expert, so the
 //     routing-weighted combine happens in registers (fp32, fixed order, no
-//     atomics) and out is written once in bf16.
+//     atomics) and out is written once in bf16.  The h rows of a chunk of
+//     experts (contiguous in sorted order) are staged in LDS once per
+//     workgroup, and the weight codes of the whole chunk are loaded before
+//     any of them is used.
 #include "device_common.h"
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kDecWaves = 4;            // waves per gate/up workgroup
-constexpr int kDecRows = 2;             // rows of I per gate/up wave
-constexpr int kDownExpertChunk = 8;     // experts whose weights are in flight together
+constexpr int kGuThreads = 256;         // gate/up workgroup
+constexpr int kGuWaves = kGuThreads / kWave;
+constexpr int kDownMaxWaves = 12;
+constexpr int kDownChunkExperts = 8;    // experts whose down codes are in flight together
+constexpr int kDownChunkSlots = 16;     // h rows staged in LDS per chunk
+constexpr int kDownAhead = 3;           // experts' down codes in flight ahead of the one computed
+constexpr int kDecodeMaxSlots = 64;     // T * k on the decode path
+constexpr int kXTokens = 2;             // activation rows staged in LDS at a time (gate/up)
 
-// Dot of 8 bf16 pairs (one 16-group of x) with the 16 codes of a group,
-// unscaled: codes decode to exact bf16 pairs, v_dot2 accumulates in fp32.
-__device__ __forceinline__ float group_dot(uint2 codes, const uint32_t* xw) {
+// Dot of 8 bf16 pairs (one 16-group of activations) with the 16 codes of a
+// group, unscaled: codes decode to exact bf16 pairs, v_dot2 accumulates in
+// fp32.
+__device__ __forceinline__ float group_dot(uint2 codes, uint4 xa, uint4 xb) {
     float acc = 0.0f;
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<0>(codes.x)), xw[0], acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<1>(codes.x)), xw[1], acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<2>(codes.x)), xw[2], acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<3>(codes.x)), xw[3], acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<0>(codes.y)), xw[4], acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<1>(codes.y)), xw[5], acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<2>(codes.y)), xw[6], acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<3>(codes.y)), xw[7], acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<0>(codes.x)), xa.x, acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<1>(codes.x)), xa.y, acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<2>(codes.x)), xa.z, acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<3>(codes.x)), xa.w, acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<0>(codes.y)), xb.x, acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<1>(codes.y)), xb.y, acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<2>(codes.y)), xb.z, acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<3>(codes.y)), xb.w, acc);
     return acc;
 }
 
-// GPL = 16-groups per lane along H (H = 1024 * GPL).
-template <int GPL>
-__global__ void __launch_bounds__(kDecWaves * kWave)
-k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k,
-             const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs, const float* __restrict__ gg,
-             const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const float* __restrict__ ug,
-             const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-             const int32_t* __restrict__ sorted_slots, uint16_t* __restrict__ h) {
-    const int e = nth_active_expert(counts, E, blockIdx.y);
-    if (e < 0) return;
+// A wave computes two consecutive output features n, n + 1 per stage.  Their
+// gate rows are one contiguous run of H codes (H / 16 chunks of 32), as are
+// their up rows; lane l takes chunk q = l + 64 j (j < CPL, H = 1024 * CPL)
+// of both runs, so gate and up share the activation chunk and every load is a
+// uniform base plus a 16-byte lane offset.  Chunk q belongs to feature
+// n + (q >= H / 32).  RW stages (2 * RW features) per wave, EPL = expert
+// counts per lane (E <= 64 * EPL).
+// The expert lookup needs one batch of small loads; the activation rows then
+// go straight to LDS, and the codes of all stages are requested before any
+// is used: stages are computed in order as they land (vector loads complete
+// in issue order).
+template <int CPL, int RW, int EPL>
+__global__ void __launch_bounds__(kGuThreads, 4)
+k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slots,
+             const uint8_t* gc, const uint8_t* gs, const float* __restrict__ gg,
+             const uint8_t* uc, const uint8_t* us, const float* __restrict__ ug,
+             const int32_t* __restrict__ counts, const int32_t* __restrict__ sorted_slots,
+             uint16_t* __restrict__ h) {
+    extern __shared__ uint4 xs[];   // [kXTokens][H / 8]
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int n0 = (blockIdx.x * kDecWaves + wave) * kDecRows;
-    const int ngroups = H / 16;
+    const int my_slot = lane < slots ? sorted_slots[lane] : 0;   // slots <= 64 on this path
+    const ActiveExpert ae = nth_active_expert<EPL>(counts, E, blockIdx.y);
+    if (ae.e < 0) return;
+    const int e = ae.e, ne = ae.count, p0 = ae.first_row;
+    const int H8 = H / 8;
+    constexpr int ncr = 32 * CPL;            // 32-wide chunks per weight row (H = 1024 * CPL)
 
-    // Issue every weight load of this wave first.
-    uint2 cw[2][kDecRows][GPL];
-    uint32_t sw[2][kDecRows][GPL];
-#pragma unroll
-    for (int r = 0; r < kDecRows; ++r) {
-        const int64_t row = (int64_t)e * I + n0 + r;
-#pragma unroll
-        for (int j = 0; j < GPL; ++j) {
-            const int g = lane + kWave * j;
-            cw[0][r][j] = reinterpret_cast<const uint2*>(gc + row * (H / 2))[g];
-            cw[1][r][j] = reinterpret_cast<const uint2*>(uc + row * (H / 2))[g];
-            sw[0][r][j] = gs[row * ngroups + g];
-            sw[1][r][j] = us[row * ngroups + g];
+    // activation rows of up to kXTokens tokens at a time live in LDS
+    const int nchunk = H8 / 64;              // H % 512 == 0 on this path
+    auto stage_x = [&](int q0) {
+        for (int q = q0; q < min(ne, q0 + kXTokens); ++q) {
+            const int t = __builtin_amdgcn_readlane(my_slot, p0 + q) / k;
+            const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * H);
+            for (int c = wave; c < nchunk; c += kGuWaves)
+                wave_copy_1k_to_lds(src + c * 64, xs + (q - q0) * H8 + c * 64);
         }
-    }
+    };
+    stage_x(0);
+
+    const int nb = (blockIdx.x * kGuWaves + wave) * (2 * RW);   // first feature of this wave
     const float g_gate = gg[e], g_up = ug[e];
-    const int p0 = offsets[e];
-    const int ne = counts[e];
-    float sc[2][kDecRows][GPL];
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int r = 0; r < kDecRows; ++r)
-#pragma unroll
-            for (int j = 0; j < GPL; ++j) sc[p][r][j] = e4m3_to_f32(sw[p][r][j]);
+    uint4 cg[2][CPL], cu[2][CPL];
+    uint32_t sg[2][CPL], su[2][CPL];
+#define MOE_GU_LOAD(r, b)                                                                       \
+    do {                                                                                        \
+        const int64_t row_ = (int64_t)e * I + min(nb + 2 * (r), I - 2);                         \
+        const uint4* gcr_ = reinterpret_cast<const uint4*>(gc + row_ * (H / 2));                \
+        const uint4* ucr_ = reinterpret_cast<const uint4*>(uc + row_ * (H / 2));                \
+        const uint16_t* gsr_ = reinterpret_cast<const uint16_t*>(gs + row_ * (H / 16));         \
+        const uint16_t* usr_ = reinterpret_cast<const uint16_t*>(us + row_ * (H / 16));         \
+        _Pragma("unroll") for (int j = 0; j < CPL; ++j) {                                       \
+            const int q = lane + kWave * j;                                                     \
+            cg[b][j] = gcr_[q];                                                                 \
+            cu[b][j] = ucr_[q];                                                                 \
+            sg[b][j] = gsr_[q];                                                                 \
+            su[b][j] = usr_[q];                                                                 \
+        }                                                                                       \
+        asm volatile("" ::: "memory");  /* issue here, not at the first use */                  \
+    } while (0)
+    MOE_GU_LOAD(0, 0);
+    wait_vmem_at_most<0>();                  // x rows (issued first) and stage 0's codes
+    __builtin_amdgcn_s_barrier();            // plain barrier: a fence would wait for every load
 
-    for (int q = 0; q < ne; ++q) {
-        const int slot = sorted_slots[p0 + q];
-        const int t = slot / k;
-        const uint16_t* xr = x + (int64_t)t * H;
-        uint32_t xw[GPL][8];
-#pragma unroll
-        for (int j = 0; j < GPL; ++j) {
-            const uint4* src = reinterpret_cast<const uint4*>(xr + (lane + kWave * j) * 16);
-            const uint4 a = src[0], b = src[1];
-            xw[j][0] = a.x; xw[j][1] = a.y; xw[j][2] = a.z; xw[j][3] = a.w;
-            xw[j][4] = b.x; xw[j][5] = b.y; xw[j][6] = b.z; xw[j][7] = b.w;
+#pragma unroll 1
+    for (int q0 = 0; q0 < ne; q0 += kXTokens) {
+        if (q0 > 0) {                        // next tokens: restage x, reload stage 0
+            __syncthreads();
+            stage_x(q0);
+            MOE_GU_LOAD(0, 0);
+            wait_all_memory();
+            __syncthreads();
         }
-        float acc[2][kDecRows];
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
+        for (int r = 0; r < RW; ++r) {
+            const int b = r & 1;
+            if (r + 1 < RW) MOE_GU_LOAD(r + 1, b ^ 1);
+            const int n = nb + 2 * r;
+#pragma unroll 1
+            for (int qt = q0; qt < min(ne, q0 + kXTokens); ++qt) {
+                const uint4* xq = xs + (qt - q0) * H8;
+                float a0 = 0.0f, a1 = 0.0f, b0 = 0.0f, b1 = 0.0f;
 #pragma unroll
-            for (int r = 0; r < kDecRows; ++r) {
-                float a = 0.0f;
-#pragma unroll
-                for (int j = 0; j < GPL; ++j) a += sc[p][r][j] * group_dot(cw[p][r][j], xw[j]);
-                acc[p][r] = wave_sum(a);
+                for (int j = 0; j < CPL; ++j) {
+                    const int q = lane + kWave * j;
+                    const bool second = q >= ncr;
+                    const uint4* xc = xq + 4 * (second ? q - ncr : q);
+                    const uint4 x0 = xc[0], x1 = xc[1], x2 = xc[2], x3 = xc[3];
+                    // opaque copies: keep the code decode inside the token loop instead
+                    // of hoisting 2 x CPL x 16 decoded pairs into registers
+                    uint4 g4 = cg[b][j], u4 = cu[b][j];
+                    const uint32_t gsc = sg[b][j], usc = su[b][j];
+                    asm volatile("" : "+v"(g4.x), "+v"(g4.y), "+v"(g4.z), "+v"(g4.w));
+                    asm volatile("" : "+v"(u4.x), "+v"(u4.y), "+v"(u4.z), "+v"(u4.w));
+                    const float dg_ = e4m3_byte_to_f32<0>(gsc) * group_dot(make_uint2(g4.x, g4.y), x0, x1) +
+                                      e4m3_byte_to_f32<1>(gsc) * group_dot(make_uint2(g4.z, g4.w), x2, x3);
+                    const float du_ = e4m3_byte_to_f32<0>(usc) * group_dot(make_uint2(u4.x, u4.y), x0, x1) +
+                                      e4m3_byte_to_f32<1>(usc) * group_dot(make_uint2(u4.z, u4.w), x2, x3);
+                    a0 += second ? 0.0f : dg_;
+                    a1 += second ? dg_ : 0.0f;
+                    b0 += second ? 0.0f : du_;
+                    b1 += second ? du_ : 0.0f;
+                }
+                a0 = wave_sum_dpp(a0);
+                a1 = wave_sum_dpp(a1);
+                b0 = wave_sum_dpp(b0);
+                b1 = wave_sum_dpp(b1);
+                if (lane < 2 && n + lane < I) {
+                    const float av = lane ? a1 : a0, bv = lane ? b1 : b0;
+                    h[(int64_t)(p0 + qt) * I + n + lane] = f32_to_bf16_rne(silu(g_gate * av) * (g_up * bv));
+                }
             }
-        if (lane < kDecRows) {
-            float av = acc[0][0], bv = acc[1][0];
-#pragma unroll
-            for (int r = 1; r < kDecRows; ++r)
-                if (lane == r) { av = acc[0][r]; bv = acc[1][r]; }
-            const float hv = silu(g_gate * av) * (g_up * bv);
-            h[(int64_t)(p0 + q) * I + n0 + lane] = f32_to_bf16_rne(hv);
         }
     }
+#undef MOE_GU_LOAD
 }
 
 // GPL2 = 16-groups per half-wave lane along I (I = 512 * GPL2); MAXT tokens.
 template <int GPL2, int MAXT>
-__global__ void __launch_bounds__(kWave)
+__global__ void __launch_bounds__(kDownMaxWaves * kWave)
 k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
-           const uint8_t* __restrict__ dc, const uint8_t* __restrict__ ds, const float* __restrict__ dg,
+           const uint8_t* dc, const uint8_t* ds, const float* __restrict__ dg,
            const float* __restrict__ topk_w, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
            const int32_t* __restrict__ sorted_slots, uint16_t* __restrict__ out) {
+    extern __shared__ uint4 hs[];     // [kDownChunkSlots][I / 8]
+    __shared__ int s_cnt[MOE_MAX_EXPERTS], s_off[MOE_MAX_EXPERTS];
     __shared__ int s_list[MOE_MAX_EXPERTS];
-    const int lane = threadIdx.x;
+    __shared__ float s_g[MOE_MAX_EXPERTS];
+    __shared__ int s_slot[kDecodeMaxSlots], s_tok[kDecodeMaxSlots];
+    __shared__ float s_w[kDecodeMaxSlots], s_wgt[kDecodeMaxSlots];
+    __shared__ int s_U;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int half = lane >> 5, l32 = lane & 31;
-    const int n = blockIdx.x * 2 + half;           // output row of H
-    const int ngroups = I / 16;
+    const int waves = blockDim.x / kWave;
+    const int n = (blockIdx.x * waves + wave) * 2 + half;      // output row of H
+    const bool row_ok = n < H;
+    const int nr = row_ok ? n : H - 1;
+    const int ngroups = I / 16, I8 = I / 8;
+    const int slots = T * k;                                   // <= kDecodeMaxSlots on this path
 
-    // Compact list of touched experts, ascending.
-    int U = 0;
-    for (int base = 0; base < E; base += kWave) {
-        const int e = base + lane;
-        const bool act = e < E && counts[e] > 0;
-        const uint64_t m = __ballot(act);
-        if (act) s_list[U + __popcll(m & lanemask_lt())] = e;
-        U += __popcll(m);
+    // all small inputs in one batch of independent loads
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        s_cnt[e] = counts[e];
+        s_off[e] = offsets[e];
+        s_g[e] = dg[e];
+    }
+    if (threadIdx.x < slots) {
+        s_slot[threadIdx.x] = sorted_slots[threadIdx.x];
+        s_w[threadIdx.x] = topk_w[threadIdx.x];
     }
     __syncthreads();
+    if (threadIdx.x < slots) {
+        const int slot = s_slot[threadIdx.x];
+        s_tok[threadIdx.x] = slot / k;
+        s_wgt[threadIdx.x] = s_w[slot];
+    }
+    if (wave == 0) {    // compact list of touched experts, ascending
+        int U = 0;
+        for (int base = 0; base < E; base += kWave) {
+            const int e = base + lane;
+            const bool act = e < E && s_cnt[e] > 0;
+            const uint64_t m = __ballot(act);
+            if (act) s_list[U + __popcll(m & lanemask_lt())] = e;
+            U += __popcll(m);
+        }
+        if (lane == 0) s_U = U;
+    }
+    __syncthreads();
+    const int U = s_U;
 
     float acc[MAXT];
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) acc[t] = 0.0f;
 
-    for (int u0 = 0; u0 < U; u0 += kDownExpertChunk) {
-        const int nu = min(kDownExpertChunk, U - u0);
-        uint2 cw[kDownExpertChunk][GPL2];
-        uint32_t sw[kDownExpertChunk][GPL2];
-#pragma unroll
-        for (int u = 0; u < kDownExpertChunk; ++u) {
-            if (u < nu) {
-                const int e = s_list[u0 + u];
-                const int64_t row = (int64_t)e * H + n;
-#pragma unroll
-                for (int j = 0; j < GPL2; ++j) {
-                    const int g = l32 + 32 * j;
-                    cw[u][j] = reinterpret_cast<const uint2*>(dc + row * (I / 2))[g];
-                    sw[u][j] = ds[row * ngroups + g];
-                }
-            }
+    int u0 = 0;
+    while (u0 < U) {
+        // chunk [u0, u1): at most kDownChunkExperts experts and kDownChunkSlots h rows
+        const int pA = s_off[s_list[u0]];
+        int u1 = u0 + 1;
+        while (u1 < U && u1 - u0 < kDownChunkExperts &&
+               s_off[s_list[u1]] + s_cnt[s_list[u1]] - pA <= kDownChunkSlots)
+            ++u1;
+        const int pB = s_off[s_list[u1 - 1]] + s_cnt[s_list[u1 - 1]];
+
+        // h rows of the chunk straight to LDS (contiguous in sorted order)
+        __syncthreads();    // the previous chunk's LDS rows are no longer read
+        {
+            const uint4* hsrc = reinterpret_cast<const uint4*>(h + (int64_t)pA * I);
+            const int nchunk = (pB - pA) * I8 / 64;       // I % 512 == 0 on this path
+            for (int c = wave; c < nchunk; c += waves) wave_copy_1k_to_lds(hsrc + c * 64, hs + c * 64);
         }
+        // codes of every chunk slot (slots past the chunk re-read its last
+        // expert, so the number of loads in flight is fixed); kDownAhead
+        // experts are in flight while one is computed
+        uint2 cw[kDownChunkExperts][GPL2];
+        uint32_t sw[kDownChunkExperts][GPL2];
+#define MOE_DOWN_LOAD(u)                                                                        \
+        do {                                                                                    \
+            const int64_t row_ = (int64_t)s_list[min(u0 + (u), u1 - 1)] * H + nr;               \
+            _Pragma("unroll") for (int j = 0; j < GPL2; ++j) {                                  \
+                const int g = l32 + 32 * j;                                                     \
+                cw[u][j] = reinterpret_cast<const uint2*>(dc + row_ * (I / 2))[g];              \
+                sw[u][j] = ds[row_ * ngroups + g];                                              \
+            }                                                                                   \
+            asm volatile("" ::: "memory");  /* issue here, not at the first use */              \
+        } while (0)
 #pragma unroll
-        for (int u = 0; u < kDownExpertChunk; ++u) {
-            if (u < nu) {
+        for (int u = 0; u < kDownAhead; ++u) MOE_DOWN_LOAD(u);
+        // this wave's h rows and its first expert's codes have landed
+        wait_vmem_at_most<2 * GPL2 * (kDownAhead - 1)>();
+        __builtin_amdgcn_s_barrier();   // plain barrier: a fence here would wait for every load
+
+#pragma unroll
+        for (int u = 0; u < kDownChunkExperts; ++u) {
+            if (u + kDownAhead < kDownChunkExperts) MOE_DOWN_LOAD(u + kDownAhead);
+            if (u0 + u < u1) {
                 const int e = s_list[u0 + u];
-                const float ge = dg[e];
-                const int p0 = offsets[e], ne = counts[e];
+                const float ge = s_g[e];
+                const int q0 = s_off[e] - pA, ne = s_cnt[e];
                 float sc[GPL2];
 #pragma unroll
                 for (int j = 0; j < GPL2; ++j) sc[j] = e4m3_to_f32(sw[u][j]);
-                for (int q = 0; q < ne; ++q) {
-                    const int slot = sorted_slots[p0 + q];
-                    const int t = slot / k;
-                    const float wgt = topk_w[slot] * ge;
-                    const uint16_t* hr = h + (int64_t)(p0 + q) * I;
+                for (int q = q0; q < q0 + ne; ++q) {
+                    const int t = s_tok[pA + q];
+                    const float wgt = s_wgt[pA + q] * ge;
+                    const uint4* hr = hs + q * I8;
                     float a = 0.0f;
 #pragma unroll
                     for (int j = 0; j < GPL2; ++j) {
-                        const uint4* src = reinterpret_cast<const uint4*>(hr + (l32 + 32 * j) * 16);
-                        const uint4 va = src[0], vb = src[1];
-                        const uint32_t hw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-                        a += sc[j] * group_dot(cw[u][j], hw);
+                        const int g = l32 + 32 * j;
+                        a += sc[j] * group_dot(cw[u][j], hr[2 * g], hr[2 * g + 1]);
                     }
 #pragma unroll
                     for (int tt = 0; tt < MAXT; ++tt)
@@ -193,29 +296,58 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
                 }
             }
         }
+#undef MOE_DOWN_LOAD
+        u0 = u1;
     }
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) {
-        const float v = half_wave_sum(acc[t]);
-        if (t < T && l32 == 0) out[(int64_t)t * H + n] = f32_to_bf16_rne(v);
+        const float v = half_wave_sum_dpp(acc[t]);
+        if (t < T && l32 == 0 && row_ok) out[(int64_t)t * H + n] = f32_to_bf16_rne(v);
     }
 }
 
-template <int GPL>
-moe_status launch_gateup_gpl(const FwdArgs& a, hipStream_t s) {
-    const dim3 grid(a.I / (kDecWaves * kDecRows), std::min(a.T * a.k, a.E));
-    MOE_LAUNCH("dec_gateup", k_dec_gateup<GPL>, grid, dim3(kDecWaves * kWave), 0, s, a.x, a.H, a.I, a.E, a.k,
+constexpr int kGuRowsPerWave = 1;      // stages of two features per gate/up wave
+
+template <int CPL, int EPL>
+moe_status launch_gateup_epl(const FwdArgs& a, hipStream_t s) {
+    const int rows_per_block = kGuWaves * 2 * kGuRowsPerWave;
+    const dim3 grid((a.I + rows_per_block - 1) / rows_per_block, std::min(a.T * a.k, a.E));
+    const size_t shmem = (size_t)std::min(a.T, kXTokens) * a.H * sizeof(uint16_t);
+    auto kern = k_dec_gateup<CPL, kGuRowsPerWave, EPL>;
+    if (allow_dynamic_lds(reinterpret_cast<const void*>(kern), shmem) != MOE_OK) return MOE_ERR_HIP;
+    MOE_LAUNCH("dec_gateup", kern, grid, dim3(kGuThreads), shmem, s, a.x, a.H, a.I, a.E, a.k, a.T * a.k,
                (const uint8_t*)a.gate->codes, (const uint8_t*)a.gate->scales, (const float*)a.gate->global_scale,
                (const uint8_t*)a.up->codes, (const uint8_t*)a.up->scales, (const float*)a.up->global_scale,
-               a.counts, a.offsets, a.sorted_slots, a.h);
+               a.counts, a.sorted_slots, a.h);
     return MOE_OK;
+}
+
+template <int CPL>
+moe_status launch_gateup_gpl(const FwdArgs& a, hipStream_t s) {
+    return a.E <= 256 ? launch_gateup_epl<CPL, 4>(a, s) : launch_gateup_epl<CPL, 16>(a, s);
+}
+
+int down_waves_per_block(int H) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    // one workgroup per CU when the rows divide evenly: 2 rows per wave
+    int w = (H + 2 * cus - 1) / (2 * cus);
+    return std::max(1, std::min(w, kDownMaxWaves));
 }
 
 template <int GPL2, int MAXT>
 moe_status launch_down_t(const FwdArgs& a, hipStream_t s) {
-    MOE_LAUNCH("dec_down", (k_dec_down<GPL2, MAXT>), dim3(a.H / 2), dim3(kWave), 0, s, (const uint16_t*)a.h, a.T,
-               a.H, a.I, a.E, a.k, (const uint8_t*)a.down->codes, (const uint8_t*)a.down->scales,
-               (const float*)a.down->global_scale, a.topk_w, a.counts, a.offsets, a.sorted_slots, a.out);
+    static int waves = 0;
+    if (!waves) waves = down_waves_per_block(a.H);
+    const int rows_per_block = 2 * waves;
+    const size_t shmem = (size_t)kDownChunkSlots * a.I * sizeof(uint16_t);
+    if (allow_dynamic_lds(reinterpret_cast<const void*>(&k_dec_down<GPL2, MAXT>), shmem) != MOE_OK)
+        return MOE_ERR_HIP;
+    MOE_LAUNCH("dec_down", (k_dec_down<GPL2, MAXT>), dim3((a.H + rows_per_block - 1) / rows_per_block),
+               dim3(waves * kWave), shmem, s, (const uint16_t*)a.h, a.T, a.H, a.I, a.E, a.k,
+               (const uint8_t*)a.down->codes, (const uint8_t*)a.down->scales, (const float*)a.down->global_scale,
+               a.topk_w, a.counts, a.offsets, a.sorted_slots, a.out);
     return MOE_OK;
 }
 
@@ -229,9 +361,9 @@ moe_status launch_down_gpl(const FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool decode_path_supported(int T, int H, int I) {
-    return T >= 1 && T <= 8 && H % 1024 == 0 && H / 1024 <= 8 && I % 512 == 0 && I / 512 <= 4 &&
-           I % (kDecWaves * kDecRows) == 0;
+bool decode_path_supported(int T, int k, int H, int I) {
+    return T >= 1 && T <= 8 && T * k <= kDecodeMaxSlots && H % 1024 == 0 && H / 1024 <= 8 && I % 512 == 0 &&
+           I / 512 <= 4;
 }
 
 moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s) {

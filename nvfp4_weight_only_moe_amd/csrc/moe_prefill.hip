@@ -186,8 +186,8 @@ __global__ void __launch_bounds__(kGThreads, BM >= 128 ? 1 : 2) k_grouped_gemm(G
             float sc[NS][2];
 #pragma unroll
             for (int ns = 0; ns < NS; ++ns) {
-                sc[ns][0] = e4m3_to_f32(cur_scale[ns] & 0xFFu);
-                sc[ns][1] = e4m3_to_f32(cur_scale[ns] >> 8);
+                sc[ns][0] = e4m3_byte_to_f32<0>(cur_scale[ns]);
+                sc[ns][1] = e4m3_byte_to_f32<1>(cur_scale[ns]);
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -293,13 +293,8 @@ template <bool GATEUP, int BM>
 moe_status launch_gemm(const GemmParams& P, int64_t slots, int E, hipStream_t s) {
     const int64_t tiles_ub = (slots / BM + std::min<int64_t>(E, slots)) * P.ntn;
     const size_t shmem = 2 * BM * kLdsRow;
-    static bool attr_set = false;  // >64 KB of dynamic LDS must be allowed explicitly
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_grouped_gemm<GATEUP, BM>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem) != hipSuccess)
-            return MOE_ERR_HIP;
-        attr_set = true;
-    }
+    if (allow_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm<GATEUP, BM>), shmem) != MOE_OK)
+        return MOE_ERR_HIP;
     const char* name = GATEUP ? "gemm_gateup" : "gemm_down";
     MOE_LAUNCH(name, (k_grouped_gemm<GATEUP, BM>), dim3(persistent_grid(tiles_ub)), dim3(kGThreads), shmem, s, P);
     return MOE_OK;

@@ -27,13 +27,13 @@ constexpr int kRW = kRT / kWave;         // waves per route workgroup
 constexpr int kTokensPerBlock = 64;      // large-T path
 constexpr int kSmallMaxSlots = kTokensPerBlock * MOE_MAX_TOPK;  // small path: T <= 64
 
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-    return v > bv || (v == bv && i < bi);
-}
-
 // One wave selects the top-k of one token's E logits and writes ids/weights.
-// EPL = logits per lane (E <= 64 * EPL).  Lane j ends up holding the j-th
-// selection; the weights are a softmax over the k selected logits.
+// EPL = logits per lane (E <= 64 * EPL).  Each round finds the maximum with
+// a DPP reduction, then the lowest expert index holding it with one ballot
+// per logit slot (slot i covers indices 64i .. 64i+63, so the first slot and
+// lane with a match is the lowest index), and retires that logit.  Lane j
+// ends up holding the j-th selection; the weights are a softmax over the k
+// selected logits.  -0.0 is folded into +0.0 so that the two compare equal.
 template <int EPL>
 __device__ void wave_topk(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids_out,
                           float* __restrict__ w_out, int32_t* ids_lds) {
@@ -42,40 +42,34 @@ __device__ void wave_topk(const float* __restrict__ row, int E, int k, int32_t* 
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int idx = lane + kWave * i;
-        v[i] = idx < E ? row[idx] : -INFINITY;
+        v[i] = idx < E ? row[idx] + 0.0f : -INFINITY;
     }
-    uint32_t taken = 0;
     float my_v = 0.0f;
     int my_i = 0;
     for (int r = 0; r < k; ++r) {
-        float bv = -INFINITY;
-        int bi = INT_MAX;
+        float lm = v[0];
+#pragma unroll
+        for (int i = 1; i < EPL; ++i) lm = fmaxf(lm, v[i]);
+        const float m = wave_max_dpp(lm);
+        int sel = -1;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
-            const int idx = lane + kWave * i;
-            if (idx < E && !((taken >> i) & 1u) && better(v[i], idx, bv, bi)) {
-                bv = v[i];
-                bi = idx;
-            }
+            const uint64_t b = __ballot(v[i] == m);
+            if (sel < 0 && b) sel = kWave * i + __ffsll((unsigned long long)b) - 1;
         }
+        if (lane == (sel & (kWave - 1))) {
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, kWave);
-            const int oi = __shfl_xor(bi, off, kWave);
-            if (better(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
+            for (int i = 0; i < EPL; ++i)
+                if (i == sel / kWave) v[i] = -INFINITY;
         }
-        if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
         if (lane == r) {
-            my_v = bv;
-            my_i = bi;
+            my_v = m;
+            my_i = sel;
         }
     }
-    const float m = __shfl(my_v, 0, kWave);
-    const float ex = lane < k ? expf(my_v - m) : 0.0f;
-    const float sum = wave_sum(ex);
+    const float m0 = __shfl(my_v, 0, kWave);
+    const float ex = lane < k ? expf(my_v - m0) : 0.0f;
+    const float sum = wave_sum_dpp(ex);
     if (lane < k) {
         ids_out[lane] = my_i;
         w_out[lane] = ex / sum;

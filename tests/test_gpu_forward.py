@@ -104,3 +104,40 @@ def test_magnitude_not_correlation_only():
     torch.cuda.synchronize()
     with pytest.raises(AssertionError):
         compare_out(bf16_bits_to_f64(bad), p.reference(), "scaled-by-25")
+
+
+@pytest.mark.parametrize("T,H,I", [(8, 1024, 512), (100, 512, 256)])
+def test_hip_graph_replay_matches_eager(T, H, I):
+    """route + forward captured in a HIP graph: every replay, with unrelated
+    eager work between replays, reproduces the eager output bit for bit."""
+    E, k = 16, 4
+    p = Problem(T, H, I, E, k, 60 + T)
+    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
+    lg, xb = to_dev(p.logits), to_dev(p.xb, torch.int16)
+    route = B.Routing.empty(T, E, k, DEV)
+    out = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    ws = B.forward_workspace(T, H, I, E, k, DEV)
+
+    def step():
+        B.moe_route_topk(lg, k, out=route)
+        B.moe_w4a16_forward(xb, gate, up, down, route, out=out, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = B.moe_route_topk(to_dev(p.logits[::-1].copy()), k)
+    for i in range(4):
+        out.fill_(i + 1)
+        ws.fill_(0xAB)
+        B.moe_w4a16_forward(xb, gate, up, down, other)      # unrelated eager work
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i}"
