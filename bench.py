@@ -57,6 +57,39 @@ def packed_bytes(N, K):
     return N * K // 2 + N * K // 16 + 4
 
 
+# Sources that determine each kernel's memory traffic; the counters stored in
+# profiles/traffic.json are only reported while these files are unchanged.
+KERNEL_SOURCES = {
+    "dec_gateup": ["moe_decode.hip", "device_common.h"],
+    "dec_down": ["moe_decode.hip", "device_common.h"],
+    "gemm_gateup": ["moe_prefill.hip", "device_common.h"],
+    "gemm_down": ["moe_prefill.hip", "device_common.h"],
+}
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, "nvfp4_weight_only_moe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter profile, or None when
+    there is none for this kernel/workload or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(f"{kernel}@{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -200,12 +233,14 @@ def main():
     if bound == "hbm":
         achieved = work / (dom_us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dominant,
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(dominant, wl.name),
+                    "kernel": dominant,
                     "kernel_avg_us": round(dom_us, 3), "algorithmic_bytes_per_launch": int(work)}
     else:
         achieved = work / (dom_us * 1e-6) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                    "traffic": measured_traffic(dominant, wl.name),
                     "kernel": dominant, "kernel_avg_us": round(dom_us, 3),
                     "algorithmic_flops_per_launch": work}
 

@@ -173,9 +173,10 @@ moe_status moe_w4a16_forward(const uint16_t *d_x, int32_t T, int32_t H, int32_t 
 
 /*
  * Per-kernel timing for benchmarks.  moe_profile_begin(n) makes the calls that
- * follow (on any stream) bracket each kernel they launch with a pair of HIP
- * events recorded on that kernel's stream, for up to n kernels.
- * moe_profile_end() synchronises on the last event and writes, for each
+ * follow (on any stream) launch each kernel with a pair of HIP timing events
+ * that the launch stamps with the kernel's own start and end
+ * (hipExtLaunchKernel), for up to n kernels; do not profile while a stream is
+ * being captured.  moe_profile_end() synchronises on the events and writes, for each
  * distinct kernel name (up to `max`), its launch count and total milliseconds.
  * Returns the number of names written.  Not thread-safe; for benchmarks only.
  */

@@ -48,27 +48,23 @@ std::mutex g_prof_mu;
 bool g_prof_on = false;
 int g_prof_max = 0;
 std::vector<ProfRec> g_prof;
-ProfRec* g_prof_open = nullptr;
 
 }  // namespace
 
-void prof_before(const char* name, hipStream_t s) {
-    if (!g_prof_on) return;
+bool prof_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
+    if (!g_prof_on) return false;
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    if ((int)g_prof.size() >= g_prof_max) return;
+    if ((int)g_prof.size() >= g_prof_max) return false;
     ProfRec r{name, nullptr, nullptr};
-    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return;
-    (void)hipEventRecord(r.start, s);
+    if (hipEventCreate(&r.start) != hipSuccess) return false;
+    if (hipEventCreate(&r.stop) != hipSuccess) {
+        (void)hipEventDestroy(r.start);
+        return false;
+    }
     g_prof.push_back(r);
-    g_prof_open = &g_prof.back();
-}
-
-void prof_after(hipStream_t s) {
-    if (!g_prof_on) return;
-    std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (!g_prof_open) return;
-    (void)hipEventRecord(g_prof_open->stop, s);
-    g_prof_open = nullptr;
+    *start = r.start;
+    *stop = r.stop;
+    return true;
 }
 
 moe_status allow_dynamic_lds(const void* kernel, size_t bytes) {
@@ -242,7 +238,6 @@ moe_status moe_profile_begin(int32_t max_launches) {
     g_prof.clear();
     g_prof.reserve(max_launches > 0 ? max_launches : 0);
     g_prof_max = max_launches > 0 ? max_launches : 0;
-    g_prof_open = nullptr;
     g_prof_on = g_prof_max > 0;
     return MOE_OK;
 }

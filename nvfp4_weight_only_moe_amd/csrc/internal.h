@@ -2,6 +2,7 @@
 // (*.hip).  Not part of the public API.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -10,18 +11,22 @@
 
 namespace moe {
 
-// ---- per-kernel event timing (moe_profile_begin / moe_profile_end)
-void prof_before(const char* name, hipStream_t s);
-void prof_after(hipStream_t s);
+// ---- per-kernel timing (moe_profile_begin / moe_profile_end)
+// While profiling is on, returns true and a pair of timing events that the
+// launch itself stamps with the kernel's start and end (hipExtLaunchKernel),
+// so the interval is the kernel's execution, not the gap between markers.
+bool prof_events(const char* name, hipEvent_t* start, hipEvent_t* stop);
 
-// Launch helper: brackets the launch with profiling events when enabled and
-// reports launch errors.
-#define MOE_LAUNCH(name, kern, grid, block, shmem, stream, ...)                  \
-    do {                                                                         \
-        ::moe::prof_before(name, stream);                                        \
-        hipLaunchKernelGGL(kern, grid, block, shmem, stream, __VA_ARGS__);       \
-        ::moe::prof_after(stream);                                               \
-        if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;                 \
+// Launch helper: timed launch when profiling is on; reports launch errors.
+#define MOE_LAUNCH(name, kern, grid, block, shmem, stream, ...)                          \
+    do {                                                                                 \
+        hipEvent_t moe_ev0_ = nullptr, moe_ev1_ = nullptr;                               \
+        if (::moe::prof_events(name, &moe_ev0_, &moe_ev1_))                              \
+            hipExtLaunchKernelGGL(kern, grid, block, shmem, stream, moe_ev0_, moe_ev1_, 0, \
+                                  __VA_ARGS__);                                          \
+        else                                                                             \
+            hipLaunchKernelGGL(kern, grid, block, shmem, stream, __VA_ARGS__);           \
+        if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;                         \
     } while (0)
 
 // Allow `bytes` of dynamic LDS for `kernel` (HIP needs an explicit opt-in
