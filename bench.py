@@ -3,9 +3,11 @@
     python bench.py [--steps K] [--warmup W] [--config C] [--gpus 1]
 
 A step is one pass of the hot path over one batch of synthetic input:
-router top-k + permutation (moe_route_topk) and the layer forward
-(moe_w4a16_forward: gate/up grouped GEMM + SwiGLU, down grouped GEMM,
-routing-weighted combine).  Quantization is load time and is not in a step.
+router top-k + permutation and the layer forward (gate/up grouped GEMM +
+SwiGLU, down grouped GEMM, routing-weighted combine), issued as one
+moe_w4a16_route_forward call (on decode shapes a single kernel launch), or
+with --split as moe_route_topk followed by moe_w4a16_forward.  Quantization
+is load time and is not in a step.
 
 Default workload: decode, 1 token, hidden 5120, intermediate 1536, 256
 experts, top-8 (the "decode-t1" workload).  Inputs are resident in HBM before
@@ -48,6 +50,11 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--decode-variant", type=int, default=0,
+                    help="decode-shape kernels (moe_debug_set_decode_variant): 0 per-expert-block "
+                         "kernels (default), 1 one persistent launch, 2 its two halves")
+    ap.add_argument("--split", action="store_true",
+                    help="step = moe_route_topk + moe_w4a16_forward (two calls) instead of route_forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM counter scaling)")
     return ap.parse_args()
@@ -60,6 +67,7 @@ def packed_bytes(N, K):
 # Sources that determine each kernel's memory traffic; the counters stored in
 # profiles/traffic.json are only reported while these files are unchanged.
 KERNEL_SOURCES = {
+    "dec_fused": ["decode_fused_kernel.h", "device_common.h", "route_common.h"],
     "dec_gateup": ["moe_decode.hip", "device_common.h"],
     "dec_down": ["moe_decode.hip", "device_common.h"],
     "gemm_gateup": ["moe_prefill.hip", "device_common.h"],
@@ -102,6 +110,7 @@ def main():
     from nvfp4_weight_only_moe_amd import workloads as wls
 
     wl = wls.WORKLOADS[args.config]
+    B.moe_debug_set_decode_variant(args.decode_variant)
     decode = wl.T <= 8
     steps = args.steps or (400 if decode else (40 if wl.T <= 2048 else 10))
     warmup = args.warmup if args.warmup is not None else (40 if decode else 3)
@@ -151,9 +160,12 @@ def main():
     ws = B.forward_workspace(wl.T, wl.H, wl.I, wl.E, wl.k, dev)
 
     def step(i):
-        B.moe_route_topk(lg_d, wl.k, out=route)
         L = layers[i % copies]
-        B.moe_w4a16_forward(x_d, L["gate"], L["up"], L["down"], route, out=out, ws=ws)
+        if args.split:
+            B.moe_route_topk(lg_d, wl.k, out=route)
+            B.moe_w4a16_forward(x_d, L["gate"], L["up"], L["down"], route, out=out, ws=ws)
+        else:
+            B.moe_w4a16_route_forward(lg_d, x_d, L["gate"], L["up"], L["down"], wl.k, routing=route, out=out, ws=ws)
 
     for i in range(warmup):
         step(i)
@@ -221,6 +233,7 @@ def main():
     alg_bytes_step = U * (w_gu + w_d) + T * H * 2 * 2 + T * wl.E * 4
     flops_step = 6.0 * T * k * H * I
     kernel_work = {
+        "dec_fused": ("hbm", U * (w_gu + w_d) + T * H * 2 * 2 + T * wl.E * 4),
         "dec_gateup": ("hbm", U * w_gu + T * H * 2),
         "dec_down": ("hbm", U * w_d + T * H * 2),
         "gemm_gateup": ("mfma", 4.0 * T * k * H * I),
@@ -266,7 +279,9 @@ def main():
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": wl.E, "k": k,
-                   "layer_copies": copies, "hip_graph": graph_ms is not None, "touched_experts": U},
+                   "layer_copies": copies, "hip_graph": graph_ms is not None, "touched_experts": U,
+                   "step_calls": "route_topk+forward" if args.split else "route_forward",
+                   "decode_variant": args.decode_variant if decode else None},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "step_algorithmic_GBps": round(step_gbps, 1), "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),

@@ -144,7 +144,11 @@ moe_status moe_route_topk(const float *d_logits, int32_t T, int32_t E, int32_t k
                           int32_t *d_sorted_slots, int32_t *d_slot_pos,
                           void *d_ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes moe_w4a16_forward needs. */
+/*
+ * Workspace bytes moe_w4a16_forward and moe_w4a16_route_forward need.  Its
+ * first 256 bytes must be zero before the first call on it
+ * (moe_w4a16_workspace_init); the calls keep them zero afterwards.
+ */
 size_t moe_w4a16_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
 
 /*
@@ -170,6 +174,56 @@ moe_status moe_w4a16_forward(const uint16_t *d_x, int32_t T, int32_t H, int32_t 
                              const int32_t *d_sorted_slots, const int32_t *d_slot_pos,
                              uint16_t *d_out, void *d_ws, size_t ws_bytes,
                              hipStream_t stream);
+
+/*
+ * Route and layer in one call: moe_route_topk on d_logits (fp32 [T][E]),
+ * storing every routing output exactly as moe_route_topk does, followed by
+ * moe_w4a16_forward on that routing.  For decode shapes (1 <= T <= 8,
+ * T*k <= 64, H % 1024 == 0, H <= 8192, I % 512 == 0, I <= 2048) everything
+ * runs in a single kernel launch; otherwise it is the route kernels followed
+ * by the forward kernels.  Same workspace as moe_w4a16_forward.
+ */
+moe_status moe_w4a16_route_forward(const float *d_logits, const uint16_t *d_x,
+                                   int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                   const moe_nvfp4_tensor *gate, const moe_nvfp4_tensor *up,
+                                   const moe_nvfp4_tensor *down,
+                                   int32_t *d_topk_ids, float *d_topk_w,
+                                   int32_t *d_counts, int32_t *d_offsets,
+                                   int32_t *d_sorted_slots, int32_t *d_slot_pos,
+                                   uint16_t *d_out, void *d_ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/*
+ * Prepare a forward workspace for first use: zeroes its first 256 bytes, the
+ * words through which the workgroups of the single-launch decode path hand
+ * the SwiGLU output over to the down projection.  A workspace must start
+ * with these bytes zero (this call, or memory allocated zero-filled); every
+ * forward leaves them zero again, so a workspace is prepared once, not per
+ * call.  Calls that share a workspace must be ordered on one stream.
+ */
+moe_status moe_w4a16_workspace_init(void *d_ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Test hook: how many times a workgroup of the single-launch decode path
+ * polls for the other workgroups' SwiGLU outputs before it computes all of
+ * them itself (default 1048576).  0 forces that local computation in every
+ * workgroup, which exercises the path taken when not every workgroup of the
+ * grid can be resident at once.  Process-wide; not for use while forwards
+ * run on other threads.
+ */
+void moe_debug_set_decode_wait_limit(int32_t polls);
+
+/*
+ * Benchmarking and test hook: which kernels run decode shapes (1-8 tokens).
+ * 0 (default): a gate/up kernel and a down kernel, one workgroup per
+ * (expert, block of rows); 1: the whole layer in one persistent launch
+ * (with the route, for moe_w4a16_route_forward); 2: the gate/up and down
+ * halves of that persistent kernel as two launches.  All give results within the
+ * forward's tolerance of each other; each is deterministic.  Shapes a
+ * variant does not cover use variant 0.  Process-wide.  Returns
+ * MOE_ERR_INVALID_ARG for other values.
+ */
+moe_status moe_debug_set_decode_variant(int32_t variant);
 
 /*
  * Per-kernel timing for benchmarks.  moe_profile_begin(n) makes the calls that

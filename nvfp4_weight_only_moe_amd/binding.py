@@ -51,6 +51,11 @@ _SIGS = {
     "moe_route_topk": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
     "moe_w4a16_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "moe_w4a16_forward": (_I, [_P, _I, _I, _I, _I, _I, _TP, _TP, _TP, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
+    "moe_w4a16_route_forward": (_I, [_P, _P, _I, _I, _I, _I, _I, _TP, _TP, _TP, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _S, _P]),
+    "moe_w4a16_workspace_init": (_I, [_P, _S, _P]),
+    "moe_debug_set_decode_wait_limit": (None, [_I]),
+    "moe_debug_set_decode_variant": (_I, [_I]),
     "moe_profile_begin": (_I, [_I]),
     "moe_profile_end": (_I, [_P, _P, _P, _I]),
 }
@@ -187,7 +192,21 @@ def moe_route_topk(logits, k, out=None, stream=None):
 
 
 def forward_workspace(T, H, I, E, k, device="cuda"):
-    return torch.empty((max(moe_w4a16_workspace_size(T, H, I, E, k), 16),), dtype=torch.uint8, device=device)
+    """A forward workspace, allocated zero-filled (so it is ready for use
+    without moe_w4a16_workspace_init)."""
+    return torch.zeros((max(moe_w4a16_workspace_size(T, H, I, E, k), 256),), dtype=torch.uint8, device=device)
+
+
+def moe_w4a16_workspace_init(ws, stream=None):
+    _check(lib().moe_w4a16_workspace_init(_ptr(ws), ws.numel(), _stream(stream)), "moe_w4a16_workspace_init")
+
+
+def moe_debug_set_decode_wait_limit(polls):
+    lib().moe_debug_set_decode_wait_limit(int(polls))
+
+
+def moe_debug_set_decode_variant(variant):
+    _check(lib().moe_debug_set_decode_variant(int(variant)), "moe_debug_set_decode_variant")
 
 
 def moe_w4a16_forward(x_bits, gate, up, down, routing, out=None, ws=None, stream=None):
@@ -204,6 +223,24 @@ def moe_w4a16_forward(x_bits, gate, up, down, routing, out=None, ws=None, stream
                                    _ptr(routing.offsets), _ptr(routing.sorted_slots), _ptr(routing.slot_pos),
                                    _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "moe_w4a16_forward")
     return out
+
+
+def moe_w4a16_route_forward(logits, x_bits, gate, up, down, k, routing=None, out=None, ws=None, stream=None):
+    """Route (as moe_route_topk, outputs stored in `routing`) and run the
+    layer; decode shapes run as one kernel launch.  Returns (out, routing)."""
+    T, H = x_bits.shape
+    E, I, _ = gate.shape
+    assert logits.shape == (T, E)
+    routing = Routing.empty(T, E, k, x_bits.device) if routing is None else routing
+    out = torch.empty((T, H), dtype=torch.int16, device=x_bits.device) if out is None else out
+    ws = forward_workspace(T, H, I, E, k, x_bits.device) if ws is None else ws
+    g, u, d = gate.cstruct(), up.cstruct(), down.cstruct()
+    _check(lib().moe_w4a16_route_forward(_ptr(logits), _ptr(x_bits), T, H, I, E, k, ctypes.byref(g), ctypes.byref(u),
+                                         ctypes.byref(d), _ptr(routing.topk_ids), _ptr(routing.topk_w),
+                                         _ptr(routing.counts), _ptr(routing.offsets), _ptr(routing.sorted_slots),
+                                         _ptr(routing.slot_pos), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_w4a16_route_forward")
+    return out, routing
 
 
 def moe_profile_begin(max_launches=4096):

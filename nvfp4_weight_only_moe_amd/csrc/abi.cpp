@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -80,10 +81,98 @@ moe_status allow_dynamic_lds(const void* kernel, size_t bytes) {
     return MOE_OK;
 }
 
+// Forward workspace: [sync words | h (bf16 [T*k][I]) | y (fp32 [T*k][H]) |
+// route scratch].  The sync words are at a fixed offset so that one
+// workspace serves calls of any shape.
+constexpr size_t kSyncBytes = 256;
+
 size_t forward_workspace_bytes(int T, int H, int I, int E, int k) {
-    (void)E;
     const size_t slots = (size_t)T * k;
-    return round_up(slots * I * sizeof(uint16_t), kAlign) + round_up(slots * H * sizeof(float), kAlign);
+    return kSyncBytes + round_up(slots * I * sizeof(uint16_t), kAlign) + round_up(slots * H * sizeof(float), kAlign) +
+           round_up(route_workspace_bytes(T, E, k), kAlign);
+}
+
+struct WsLayout {
+    uint32_t* sync;
+    uint16_t* h;
+    float* y;
+    void* route;
+};
+
+WsLayout ws_layout(void* d_ws, int T, int H, int I, int k) {
+    uint8_t* ws = static_cast<uint8_t*>(d_ws);
+    const size_t slots = (size_t)T * k;
+    const size_t hb = round_up(slots * I * sizeof(uint16_t), kAlign);
+    const size_t yb = round_up(slots * H * sizeof(float), kAlign);
+    return WsLayout{reinterpret_cast<uint32_t*>(ws), reinterpret_cast<uint16_t*>(ws + kSyncBytes),
+                    reinterpret_cast<float*>(ws + kSyncBytes + hb), ws + kSyncBytes + hb + yb};
+}
+
+// Decode-shape kernels: 0 = gate/up and down kernels of moe_decode.hip,
+// 1 = one launch for the whole layer (route included when routing here),
+// 2 = the gate/up and down halves of the single-launch kernel as two
+// launches.  Chosen by moe_debug_set_decode_variant (a benchmarking and test
+// hook); 0, the fastest measured on MI355X, is the default.  Shapes a
+// variant does not cover fall back to 0, then to the grouped-GEMM path.
+int g_decode_variant = 0;
+
+moe_status launch_decode_forward(const FwdArgs& a, uint32_t* sync, hipStream_t stream) {
+    if (g_decode_variant == 1 && fused_decode_supported(a.T, a.k, a.H, a.I))
+        return launch_decode_fused(a, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, sync, stream);
+    if (g_decode_variant == 2 && fused_decode_supported(a.T, a.k, a.H, a.I)) return launch_decode_two(a, stream);
+    if (decode_path_supported(a.T, a.k, a.H, a.I)) return launch_forward_decode(a, stream);
+    return launch_forward_prefill(a, stream);
+}
+
+// Checks shared by moe_w4a16_forward and moe_w4a16_route_forward.
+moe_status check_forward(const uint16_t* d_x, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                         const moe_nvfp4_tensor* gate, const moe_nvfp4_tensor* up, const moe_nvfp4_tensor* down,
+                         const void* const* ptrs, int nptrs, const uint16_t* d_out, void* d_ws, size_t ws_bytes) {
+    if (T < 0 || E < 1 || k < 1 || H < 1 || I < 1) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || k > E) return MOE_ERR_UNSUPPORTED;
+    if (H % 256 || I % 128) return MOE_ERR_SHAPE;
+    if ((int64_t)T * k > (int64_t)INT32_MAX / 2) return MOE_ERR_SHAPE;
+    if (!gate || !up || !down) return MOE_ERR_INVALID_ARG;
+    moe_status st;
+    if ((st = check_tensor(gate, E, I, H)) != MOE_OK) return st;
+    if ((st = check_tensor(up, E, I, H)) != MOE_OK) return st;
+    if ((st = check_tensor(down, E, H, I)) != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    for (int i = 0; i < nptrs; ++i) {
+        if (!ptrs[i]) return MOE_ERR_INVALID_ARG;
+        if (!aligned16(ptrs[i])) return MOE_ERR_ALIGN;
+    }
+    if (!d_x || !d_out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(d_x) || !aligned16(d_out)) return MOE_ERR_ALIGN;
+    if (!d_ws) return MOE_ERR_WORKSPACE;
+    if (!aligned16(d_ws)) return MOE_ERR_ALIGN;
+    const size_t xbytes = (size_t)T * H * sizeof(uint16_t);
+    if (ranges_overlap(d_x, xbytes, d_out, xbytes)) return MOE_ERR_INVALID_ARG;
+    const size_t need = forward_workspace_bytes(T, H, I, E, k);
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    if (ranges_overlap(d_ws, need, d_out, xbytes) || ranges_overlap(d_ws, need, d_x, xbytes))
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+FwdArgs make_args(const uint16_t* d_x, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                  const moe_nvfp4_tensor* gate, const moe_nvfp4_tensor* up, const moe_nvfp4_tensor* down,
+                  const int32_t* ids, const float* w, const int32_t* counts, const int32_t* offsets,
+                  const int32_t* sorted, const int32_t* pos, uint16_t* d_out, const WsLayout& L) {
+    FwdArgs a{};
+    a.x = d_x;
+    a.T = T; a.H = H; a.I = I; a.E = E; a.k = k;
+    a.gate = gate; a.up = up; a.down = down;
+    a.ids = ids;
+    a.topk_w = w;
+    a.counts = counts;
+    a.offsets = offsets;
+    a.sorted_slots = sorted;
+    a.slot_pos = pos;
+    a.out = d_out;
+    a.h = L.h;
+    a.y = L.y;
+    return a;
 }
 
 }  // namespace moe
@@ -188,45 +277,49 @@ moe_status moe_w4a16_forward(const uint16_t* d_x, int32_t T, int32_t H, int32_t 
                              const int32_t* d_topk_ids, const float* d_topk_w, const int32_t* d_counts,
                              const int32_t* d_offsets, const int32_t* d_sorted_slots, const int32_t* d_slot_pos,
                              uint16_t* d_out, void* d_ws, size_t ws_bytes, hipStream_t stream) {
-    if (T < 0 || E < 1 || k < 1 || H < 1 || I < 1) return MOE_ERR_SHAPE;
-    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || k > E) return MOE_ERR_UNSUPPORTED;
-    if (H % 256 || I % 128) return MOE_ERR_SHAPE;
-    if ((int64_t)T * k > (int64_t)INT32_MAX / 2) return MOE_ERR_SHAPE;
-    if (!gate || !up || !down) return MOE_ERR_INVALID_ARG;
-    moe_status st;
-    if ((st = check_tensor(gate, E, I, H)) != MOE_OK) return st;
-    if ((st = check_tensor(up, E, I, H)) != MOE_OK) return st;
-    if ((st = check_tensor(down, E, H, I)) != MOE_OK) return st;
-    if (T == 0) return MOE_OK;
-    const void* ptrs[] = {d_x, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots, d_slot_pos, d_out, d_ws};
-    for (const void* p : ptrs) {
-        if (!p) return p == d_ws ? MOE_ERR_WORKSPACE : MOE_ERR_INVALID_ARG;
-        if (!aligned16(p)) return MOE_ERR_ALIGN;
-    }
-    const size_t xbytes = (size_t)T * H * sizeof(uint16_t);
-    if (ranges_overlap(d_x, xbytes, d_out, xbytes)) return MOE_ERR_INVALID_ARG;
-    const size_t need = forward_workspace_bytes(T, H, I, E, k);
-    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
-    if (ranges_overlap(d_ws, need, d_out, xbytes) || ranges_overlap(d_ws, need, d_x, xbytes))
-        return MOE_ERR_INVALID_ARG;
+    const void* ptrs[] = {d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots, d_slot_pos};
+    moe_status st = check_forward(d_x, T, H, I, E, k, gate, up, down, ptrs, 6, d_out, d_ws, ws_bytes);
+    if (st != MOE_OK || T == 0) return st;
+    const WsLayout L = ws_layout(d_ws, T, H, I, k);
+    const FwdArgs a = make_args(d_x, T, H, I, E, k, gate, up, down, d_topk_ids, d_topk_w, d_counts, d_offsets,
+                                d_sorted_slots, d_slot_pos, d_out, L);
+    return launch_decode_forward(a, L.sync, stream);
+}
 
-    FwdArgs a{};
-    a.x = d_x;
-    a.T = T; a.H = H; a.I = I; a.E = E; a.k = k;
-    a.gate = gate; a.up = up; a.down = down;
-    a.ids = d_topk_ids;
-    a.topk_w = d_topk_w;
-    a.counts = d_counts;
-    a.offsets = d_offsets;
-    a.sorted_slots = d_sorted_slots;
-    a.slot_pos = d_slot_pos;
-    a.out = d_out;
-    uint8_t* ws = static_cast<uint8_t*>(d_ws);
-    const size_t slots = (size_t)T * k;
-    a.h = reinterpret_cast<uint16_t*>(ws);
-    a.y = reinterpret_cast<float*>(ws + round_up(slots * I * sizeof(uint16_t), 256));
-    if (decode_path_supported(T, k, H, I)) return launch_forward_decode(a, stream);
-    return launch_forward_prefill(a, stream);
+moe_status moe_w4a16_route_forward(const float* d_logits, const uint16_t* d_x, int32_t T, int32_t H, int32_t I,
+                                   int32_t E, int32_t k, const moe_nvfp4_tensor* gate, const moe_nvfp4_tensor* up,
+                                   const moe_nvfp4_tensor* down, int32_t* d_topk_ids, float* d_topk_w,
+                                   int32_t* d_counts, int32_t* d_offsets, int32_t* d_sorted_slots,
+                                   int32_t* d_slot_pos, uint16_t* d_out, void* d_ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+    const void* ptrs[] = {d_logits, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots, d_slot_pos};
+    moe_status st = check_forward(d_x, T, H, I, E, k, gate, up, down, ptrs, 7, d_out, d_ws, ws_bytes);
+    if (st != MOE_OK || T == 0) return st;
+    const WsLayout L = ws_layout(d_ws, T, H, I, k);
+    const FwdArgs a = make_args(d_x, T, H, I, E, k, gate, up, down, d_topk_ids, d_topk_w, d_counts, d_offsets,
+                                d_sorted_slots, d_slot_pos, d_out, L);
+    if (g_decode_variant == 1 && fused_decode_supported(T, k, H, I))
+        return launch_decode_fused(a, d_logits, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots,
+                                   d_slot_pos, L.sync, stream);
+    st = launch_route(d_logits, T, E, k, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots, d_slot_pos,
+                      L.route, stream);
+    if (st != MOE_OK) return st;
+    return launch_decode_forward(a, L.sync, stream);
+}
+
+moe_status moe_w4a16_workspace_init(void* d_ws, size_t ws_bytes, hipStream_t stream) {
+    if (!d_ws) return MOE_ERR_WORKSPACE;
+    if (!aligned16(d_ws)) return MOE_ERR_ALIGN;
+    if (ws_bytes < kSyncBytes) return MOE_ERR_WORKSPACE;
+    return launch_zero_words(static_cast<uint32_t*>(d_ws), (int)(kSyncBytes / sizeof(uint32_t)), stream);
+}
+
+void moe_debug_set_decode_wait_limit(int32_t polls) { set_decode_wait_limit(polls); }
+
+moe_status moe_debug_set_decode_variant(int32_t variant) {
+    if (variant < 0 || variant > 2) return MOE_ERR_INVALID_ARG;
+    g_decode_variant = variant;
+    return MOE_OK;
 }
 
 moe_status moe_profile_begin(int32_t max_launches) {

@@ -72,6 +72,22 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
+// Dot of 8 bf16 pairs (one 16-group of activations) with the 16 codes of a
+// group, unscaled: codes decode to exact bf16 pairs, v_dot2 accumulates in
+// fp32.
+__device__ __forceinline__ float group_dot(uint2 codes, uint4 xa, uint4 xb) {
+    float acc = 0.0f;
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<0>(codes.x)), xa.x, acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<1>(codes.x)), xa.y, acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<2>(codes.x)), xa.z, acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<3>(codes.x)), xa.w, acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<0>(codes.y)), xb.x, acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<1>(codes.y)), xb.y, acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<2>(codes.y)), xb.z, acc);
+    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<3>(codes.y)), xb.w, acc);
+    return acc;
+}
+
 // ---------------------------------------------------------------- LDS DMA
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -85,6 +101,15 @@ __device__ __forceinline__ void wave_copy_1k_to_lds(const uint4* __restrict__ sr
 
 // Wait for every outstanding memory operation of this wave.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Workgroup barrier that waits only for this wave's LDS operations, not for
+// its vector-memory loads in flight (a __syncthreads fence waits for all).
+__device__ __forceinline__ void wait_lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt 63 (no wait), expcnt 7 (no wait), lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // Wait until at most N vector-memory loads of this wave are outstanding
 // (they complete in issue order); LDS and scalar counters are not waited on.

@@ -63,6 +63,15 @@ struct FwdArgs {
 
 size_t forward_workspace_bytes(int T, int H, int I, int E, int k);
 bool decode_path_supported(int T, int k, int H, int I);
+// moe_decode_fused.hip: single-launch decode path (route optional: logits
+// non-null routes in the kernel and stores the routing outputs)
+bool fused_decode_supported(int T, int k, int H, int I);
+void set_decode_wait_limit(int polls);
+moe_status launch_decode_fused(const FwdArgs& a, const float* logits, int32_t* ids_out, float* w_out,
+                               int32_t* counts_out, int32_t* offsets_out, int32_t* sorted_out, int32_t* pos_out,
+                               uint32_t* sync, hipStream_t s);
+moe_status launch_decode_two(const FwdArgs& a, hipStream_t s);
+moe_status launch_zero_words(uint32_t* p, int n, hipStream_t s);
 moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s);
 moe_status launch_forward_prefill(const FwdArgs& a, hipStream_t s);
 

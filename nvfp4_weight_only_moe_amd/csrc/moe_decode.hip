@@ -42,22 +42,6 @@ constexpr int kDownAhead = 3;           // experts' down codes in flight ahead o
 constexpr int kDecodeMaxSlots = 64;     // T * k on the decode path
 constexpr int kXTokens = 2;             // activation rows staged in LDS at a time (gate/up)
 
-// Dot of 8 bf16 pairs (one 16-group of activations) with the 16 codes of a
-// group, unscaled: codes decode to exact bf16 pairs, v_dot2 accumulates in
-// fp32.
-__device__ __forceinline__ float group_dot(uint2 codes, uint4 xa, uint4 xb) {
-    float acc = 0.0f;
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<0>(codes.x)), xa.x, acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<1>(codes.x)), xa.y, acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<2>(codes.x)), xa.z, acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<3>(codes.x)), xa.w, acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<0>(codes.y)), xb.x, acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<1>(codes.y)), xb.y, acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<2>(codes.y)), xb.z, acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, e2m1x2_to_bf16<3>(codes.y)), xb.w, acc);
-    return acc;
-}
-
 // A wave computes two consecutive output features n, n + 1 per stage.  Their
 // gate rows are one contiguous run of H codes (H / 16 chunks of 32), as are
 // their up rows; lane l takes chunk q = l + 64 j (j < CPL, H = 1024 * CPL)

@@ -1,0 +1,11 @@
+// Instantiations of the decode kernel (decode_fused_kernel.h) for 2-8 tokens,
+// mode kDown.
+#include "decode_fused_kernel.h"
+
+namespace moe {
+namespace fused {
+moe_status launch_t8_down(const FusedParams& p, int grid, hipStream_t s) {
+    return launch_shape<8, kDown>(p, grid, s);
+}
+}  // namespace fused
+}  // namespace moe

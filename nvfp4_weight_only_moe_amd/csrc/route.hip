@@ -18,6 +18,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "route_common.h"
 
 namespace moe {
 namespace {
@@ -27,53 +28,19 @@ constexpr int kRW = kRT / kWave;         // waves per route workgroup
 constexpr int kTokensPerBlock = 64;      // large-T path
 constexpr int kSmallMaxSlots = kTokensPerBlock * MOE_MAX_TOPK;  // small path: T <= 64
 
-// One wave selects the top-k of one token's E logits and writes ids/weights.
-// EPL = logits per lane (E <= 64 * EPL).  Each round finds the maximum with
-// a DPP reduction, then the lowest expert index holding it with one ballot
-// per logit slot (slot i covers indices 64i .. 64i+63, so the first slot and
-// lane with a match is the lowest index), and retires that logit.  Lane j
-// ends up holding the j-th selection; the weights are a softmax over the k
-// selected logits.  -0.0 is folded into +0.0 so that the two compare equal.
+// One wave: top-k of one token's E logits (wave_topk_select) written to
+// ids/weights, and to LDS when ids_lds is given.
 template <int EPL>
 __device__ void wave_topk(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids_out,
                           float* __restrict__ w_out, int32_t* ids_lds) {
     const int lane = threadIdx.x & (kWave - 1);
-    float v[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int idx = lane + kWave * i;
-        v[i] = idx < E ? row[idx] + 0.0f : -INFINITY;
-    }
-    float my_v = 0.0f;
-    int my_i = 0;
-    for (int r = 0; r < k; ++r) {
-        float lm = v[0];
-#pragma unroll
-        for (int i = 1; i < EPL; ++i) lm = fmaxf(lm, v[i]);
-        const float m = wave_max_dpp(lm);
-        int sel = -1;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const uint64_t b = __ballot(v[i] == m);
-            if (sel < 0 && b) sel = kWave * i + __ffsll((unsigned long long)b) - 1;
-        }
-        if (lane == (sel & (kWave - 1))) {
-#pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                if (i == sel / kWave) v[i] = -INFINITY;
-        }
-        if (lane == r) {
-            my_v = m;
-            my_i = sel;
-        }
-    }
-    const float m0 = __shfl(my_v, 0, kWave);
-    const float ex = lane < k ? expf(my_v - m0) : 0.0f;
-    const float sum = wave_sum_dpp(ex);
+    int id;
+    float w;
+    wave_topk_select<EPL>(row, E, k, id, w);
     if (lane < k) {
-        ids_out[lane] = my_i;
-        w_out[lane] = ex / sum;
-        if (ids_lds) ids_lds[lane] = my_i;
+        ids_out[lane] = id;
+        w_out[lane] = w;
+        if (ids_lds) ids_lds[lane] = id;
     }
 }
 
@@ -128,17 +95,12 @@ __device__ void block_scatter(const int32_t* ids, int f0, int f1, const int* bas
         const int i = c0 + lane;
         const bool valid = i < w1;
         const int e = valid ? ids[i] : 0;
-        uint64_t match = __ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t bal = __ballot(valid && bit);
-            match &= bit ? bal : ~bal;
-        }
-        const int rank = __popcll(match & lanemask_lt());
+        int same = 0;
+        const int rank = wave_rank_equal(e, valid, nbits, &same);
         int pos = 0;
         if (valid) pos = my_hist[e] + rank;
         __builtin_amdgcn_wave_barrier();
-        if (valid && rank == 0) my_hist[e] += __popcll(match);
+        if (valid && rank == 0) my_hist[e] += same;
         __builtin_amdgcn_wave_barrier();
         if (valid) {
             sorted_slots[pos] = i;

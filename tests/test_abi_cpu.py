@@ -103,3 +103,44 @@ def test_workspace_sizes(L):
     need = L.moe_w4a16_workspace_size(16, 256, 128, 8, 2)
     assert need >= 16 * 2 * (128 * 2 + 256 * 4)
     assert need % 256 == 0
+
+
+def rfwd(L, logits=A + 0x700000, x=A, T=4, H=256, I=128, E=8, k=2, ptr=A + 0x600000, out=A + 0x800000,
+         ws=A + 0x900000, ws_bytes=1 << 30):
+    gate, up, down = T_(E, I, H), T_(E, I, H, A + 0x1000000), T_(E, H, I, A + 0x2000000)
+    p = [ptr] * 6
+    return L.moe_w4a16_route_forward(logits, x, T, H, I, E, k, ctypes.byref(gate), ctypes.byref(up),
+                                     ctypes.byref(down), *p, out, ws, ws_bytes, None)
+
+
+def test_route_forward_argument_errors(L):
+    assert rfwd(L, T=0) == b.MOE_OK
+    assert rfwd(L, T=-1) == -2
+    assert rfwd(L, logits=0) == -1                                  # null logits
+    assert rfwd(L, logits=A + 4) == -3
+    assert rfwd(L, ptr=0) == -1                                     # null routing outputs
+    assert rfwd(L, k=9) == -4
+    assert rfwd(L, H=200) == -2
+    assert rfwd(L, out=A) == -1                                     # out aliases x
+    assert rfwd(L, ws=0) == -7
+    assert rfwd(L, ws_bytes=16) == -7
+
+
+def test_workspace_init_and_size(L):
+    assert L.moe_w4a16_workspace_init(0, 1 << 20, None) == -7
+    assert L.moe_w4a16_workspace_init(A + 4, 1 << 20, None) == -3
+    assert L.moe_w4a16_workspace_init(A, 128, None) == -7           # smaller than the sync words
+    # the workspace always begins with the 256 sync bytes, then h and y
+    T, H, I, E, k = 3, 1024, 512, 16, 4
+    assert L.moe_w4a16_workspace_size(T, H, I, E, k) >= 256 + T * k * I * 2 + T * k * H * 4
+    # large T also carries the route scratch
+    assert L.moe_w4a16_workspace_size(1000, H, I, E, k) >= (
+        256 + 1000 * k * (I * 2 + H * 4) + L.moe_route_workspace_size(1000, E, k))
+
+
+def test_decode_variant_hook(L):
+    assert L.moe_debug_set_decode_variant(3) == -1
+    assert L.moe_debug_set_decode_variant(-1) == -1
+    for v in (0, 1, 2):
+        assert L.moe_debug_set_decode_variant(v) == 0
+    assert L.moe_debug_set_decode_variant(0) == 0

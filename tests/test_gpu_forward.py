@@ -136,8 +136,123 @@ def test_hip_graph_replay_matches_eager(T, H, I):
     other = B.moe_route_topk(to_dev(p.logits[::-1].copy()), k)
     for i in range(4):
         out.fill_(i + 1)
-        ws.fill_(0xAB)
+        ws[256:].fill_(0xAB)    # everything but the sync words, which calls keep at zero
         B.moe_w4a16_forward(xb, gate, up, down, other)      # unrelated eager work
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {i}"
+
+
+# ------------------------------------------------------------------ route + forward in one call
+@pytest.fixture
+def decode_variant(request):
+    """Select the decode-shape kernels (moe_debug_set_decode_variant) for one
+    test; the default (0) is restored afterwards."""
+    B.moe_debug_set_decode_variant(request.param)
+    yield request.param
+    B.moe_debug_set_decode_variant(0)
+
+
+DECODE_CASES = [
+    (1, 1024, 512, 8, 2, 70),
+    (1, 2048, 1536, 8, 6, 71),
+    (4, 2048, 1024, 32, 8, 72),
+    (8, 1024, 1536, 8, 8, 73),       # k == E
+    (8, 3072, 512, 300, 8, 74),      # E > 256: five logits per lane in the top-k
+]
+
+
+@pytest.mark.parametrize("decode_variant", [0, 1, 2], indirect=True)
+@pytest.mark.parametrize("T,H,I,E,k,seed", DECODE_CASES + [(40, 512, 256, 16, 4, 75)])
+def test_route_forward_matches_route_then_forward(T, H, I, E, k, seed, decode_variant):
+    """moe_w4a16_route_forward stores exactly moe_route_topk's outputs and
+    exactly moe_w4a16_forward's result (with the single-launch variant the
+    route runs inside the layer's kernel), for every decode variant, and
+    matches the oracle."""
+    p = Problem(T, H, I, E, k, seed)
+    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
+    lg, xb = to_dev(p.logits), to_dev(p.xb, torch.int16)
+    log(f"route_forward T{T} H{H} I{I} E{E} k{k} decode variant {decode_variant}")
+    r_ref = B.moe_route_topk(lg, k)
+    out_ref = B.moe_w4a16_forward(xb, gate, up, down, r_ref)
+    out, r = B.moe_w4a16_route_forward(lg, xb, gate, up, down, k)
+    torch.cuda.synchronize()
+    for name in ("topk_ids", "topk_w", "counts", "offsets", "sorted_slots", "slot_pos"):
+        assert torch.equal(getattr(r, name), getattr(r_ref, name)), name
+    assert np.array_equal(r.topk_ids.cpu().numpy(), p.ids)
+    assert torch.equal(out, out_ref)
+    compare_out(bf16_bits_to_f64(out), p.reference(), f"route_forward-T{T}")
+
+
+@pytest.mark.parametrize("decode_variant", [1], indirect=True)
+@pytest.mark.parametrize("T,H,I,E,k,seed", DECODE_CASES[:3])
+def test_decode_local_h_path_is_bit_identical(T, H, I, E, k, seed, decode_variant):
+    """With the hand-off wait limit at 0 every workgroup computes all of h
+    itself (the path taken when the grid is not fully resident); the result
+    is bit-identical to the normal hand-off."""
+    p = Problem(T, H, I, E, k, seed)
+    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
+    lg, xb = to_dev(p.logits), to_dev(p.xb, torch.int16)
+    out_ref, _ = B.moe_w4a16_route_forward(lg, xb, gate, up, down, k)
+    torch.cuda.synchronize()
+    ws = B.forward_workspace(T, H, I, E, k, DEV)
+    try:
+        B.moe_debug_set_decode_wait_limit(0)
+        outs = [B.moe_w4a16_route_forward(lg, xb, gate, up, down, k, ws=ws)[0] for _ in range(2)]
+        torch.cuda.synchronize()
+    finally:
+        B.moe_debug_set_decode_wait_limit(1 << 20)
+    for o in outs:
+        assert torch.equal(o, out_ref)
+    # the workspace is still good for the normal path afterwards
+    again, _ = B.moe_w4a16_route_forward(lg, xb, gate, up, down, k, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(again, out_ref)
+
+
+@pytest.mark.parametrize("decode_variant", [1, 2], indirect=True)
+def test_workspace_reused_across_problems(decode_variant):
+    """One workspace serves consecutive calls with different inputs, routings
+    and shapes: no call reads another call's intermediate values, and
+    moe_w4a16_workspace_init restores a workspace whose sync words were
+    overwritten."""
+    cases = [(1, 1024, 512, 16, 4, 80), (8, 1024, 512, 16, 4, 81), (3, 2048, 512, 16, 4, 82),
+             (1, 1024, 512, 16, 4, 83), (50, 1024, 512, 16, 4, 84), (2, 1024, 512, 16, 4, 85)]
+    ws = B.forward_workspace(50, 2048, 512, 16, 4, DEV)
+    probs = []
+    for T, H, I, E, k, seed in cases:
+        p = Problem(T, H, I, E, k, seed)
+        packed = [B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms]
+        fresh, _ = B.moe_w4a16_route_forward(to_dev(p.logits), to_dev(p.xb, torch.int16), *packed, k)
+        probs.append((p, packed, fresh))
+    torch.cuda.synchronize()
+    for rnd in range(2):
+        for p, packed, fresh in probs:
+            out, _ = B.moe_w4a16_route_forward(to_dev(p.logits), to_dev(p.xb, torch.int16), *packed, p.k, ws=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(out, fresh), f"round {rnd} T{p.T} H{p.H}"
+        ws.fill_(0x5A)
+        B.moe_w4a16_workspace_init(ws)
+
+
+@pytest.mark.parametrize("T,H,I,E,k,seed", DECODE_CASES)
+def test_decode_variants_agree(T, H, I, E, k, seed):
+    """The three decode-shape kernel sets each match the oracle, and agree
+    with one another to the forward's tolerance."""
+    p = Problem(T, H, I, E, k, seed)
+    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
+    lg, xb = to_dev(p.logits), to_dev(p.xb, torch.int16)
+    ref = p.reference()
+    outs = []
+    try:
+        for v in (0, 1, 2):
+            B.moe_debug_set_decode_variant(v)
+            out, _ = B.moe_w4a16_route_forward(lg, xb, gate, up, down, k)
+            torch.cuda.synchronize()
+            got = bf16_bits_to_f64(out)
+            compare_out(got, ref, f"variant {v} T{T}")
+            outs.append(got)
+    finally:
+        B.moe_debug_set_decode_variant(0)
+    for v in (1, 2):
+        compare_out(outs[v], outs[0], f"variant {v} vs 0")

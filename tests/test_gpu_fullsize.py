@@ -73,6 +73,40 @@ def test_fullsize_decode_8_tokens():
     check_tokens(2, list(range(8)))
 
 
+@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_fullsize_route_forward_decode(cfg, variant):
+    """At full size, for every decode variant: moe_w4a16_route_forward equals
+    moe_route_topk followed by moe_w4a16_forward bit for bit (routing and
+    output), and the output matches the oracle on sampled tokens."""
+    B.moe_debug_set_decode_variant(variant)
+    try:
+        _route_forward_case(cfg)
+    finally:
+        B.moe_debug_set_decode_variant(0)
+
+
+def _route_forward_case(cfg):
+    wl = wls.WORKLOADS[cfg]
+    layer = full_layer_gpu()
+    xb, _ = wls.activations(wl)
+    lg, x_d = to_dev(wls.logits(wl)), to_dev(xb, torch.int16)
+    r_ref = B.moe_route_topk(lg, wl.k)
+    out_ref = B.moe_w4a16_forward(x_d, layer["gate"], layer["up"], layer["down"], r_ref)
+    out, r = B.moe_w4a16_route_forward(lg, x_d, layer["gate"], layer["up"], layer["down"], wl.k)
+    torch.cuda.synchronize()
+    for name in ("topk_ids", "topk_w", "counts", "offsets", "sorted_slots", "slot_pos"):
+        assert torch.equal(getattr(r, name), getattr(r_ref, name)), name
+    assert torch.equal(out, out_ref)
+    log(f"{wl.name}: route_forward identical to route + forward")
+    x = wls.activations(wl)[1]
+    ids, w = oracle.route_topk(wls.logits(wl), wl.k)
+    tokens = [0, wl.T - 1]
+    experts = sorted(set(int(e) for t in tokens for e in ids[t]))
+    ref = omoe.moe_forward(x, oracle_experts(experts), ids, w, tokens=tokens)
+    compare_out(bf16_bits_to_f64(out)[tokens], ref[tokens], wl.name)
+
+
 def test_fullsize_prefill_1024_sampled():
     check_tokens(3, [0, 511, 1023])
 
