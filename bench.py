@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--decode-variant", type=int, default=0,
                     help="decode-shape kernels (moe_debug_set_decode_variant): 0 per-expert-block "
                          "kernels (default), 1 one persistent launch, 2 its two halves")
+    ap.add_argument("--prefill-variant", type=int, default=2,
+                    help="grouped-GEMM kernels (moe_debug_set_prefill_variant): 0 register-staged, "
+                         "1 LDS-pipelined, 2 chosen per product by rows per expert (default)")
     ap.add_argument("--split", action="store_true",
                     help="step = moe_route_topk + moe_w4a16_forward (two calls) instead of route_forward")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -111,6 +114,7 @@ def main():
 
     wl = wls.WORKLOADS[args.config]
     B.moe_debug_set_decode_variant(args.decode_variant)
+    B.moe_debug_set_prefill_variant(args.prefill_variant)
     decode = wl.T <= 8
     steps = args.steps or (400 if decode else (40 if wl.T <= 2048 else 10))
     warmup = args.warmup if args.warmup is not None else (40 if decode else 3)
@@ -281,7 +285,8 @@ def main():
         "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": wl.E, "k": k,
                    "layer_copies": copies, "hip_graph": graph_ms is not None, "touched_experts": U,
                    "step_calls": "route_topk+forward" if args.split else "route_forward",
-                   "decode_variant": args.decode_variant if decode else None},
+                   "decode_variant": args.decode_variant if decode else None,
+                   "prefill_variant": None if decode else args.prefill_variant},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "step_algorithmic_GBps": round(step_gbps, 1), "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),

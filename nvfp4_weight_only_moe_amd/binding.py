@@ -56,6 +56,7 @@ _SIGS = {
     "moe_w4a16_workspace_init": (_I, [_P, _S, _P]),
     "moe_debug_set_decode_wait_limit": (None, [_I]),
     "moe_debug_set_decode_variant": (_I, [_I]),
+    "moe_debug_set_prefill_variant": (_I, [_I]),
     "moe_profile_begin": (_I, [_I]),
     "moe_profile_end": (_I, [_P, _P, _P, _I]),
 }
@@ -207,6 +208,10 @@ def moe_debug_set_decode_wait_limit(polls):
 
 def moe_debug_set_decode_variant(variant):
     _check(lib().moe_debug_set_decode_variant(int(variant)), "moe_debug_set_decode_variant")
+
+
+def moe_debug_set_prefill_variant(variant):
+    _check(lib().moe_debug_set_prefill_variant(int(variant)), "moe_debug_set_prefill_variant")
 
 
 def moe_w4a16_forward(x_bits, gate, up, down, routing, out=None, ws=None, stream=None):

@@ -116,12 +116,37 @@ WsLayout ws_layout(void* d_ws, int T, int H, int I, int k) {
 // variant does not cover fall back to 0, then to the grouped-GEMM path.
 int g_decode_variant = 0;
 
+// Grouped-GEMM kernels for larger T: 0 = register-staged (k_grouped_gemm)
+// for both products, 1 = LDS-pipelined (k_gemm_pipe) for both, 2 = chosen
+// per product from the mean rows per touched expert (the default).  The
+// pipelined kernel's 128-row tiles pay off on gate/up once experts hold a few
+// hundred rows (16K tokens, top-8 of 256: 5.9 ms against 7.3 ms on MI355X);
+// with few rows per expert its padding costs more than it saves, and on down
+// (K = I, short) the register-staged kernel measured as fast or faster.
+// Chosen by moe_debug_set_prefill_variant.
+int g_prefill_variant = 2;
+constexpr int64_t kPipeMinRowsPerExpert = 256;
+
+moe_status launch_prefill(const FwdArgs& a, hipStream_t stream) {
+    const bool pipe_ok = prefill_pipe_supported(a.H, a.I);
+    const int64_t slots = (int64_t)a.T * a.k;
+    const int64_t per_expert = slots / std::max<int64_t>(1, std::min<int64_t>(a.E, slots));
+    const bool pipe_gateup =
+        pipe_ok && (g_prefill_variant == 1 || (g_prefill_variant == 2 && per_expert >= kPipeMinRowsPerExpert));
+    const bool pipe_down = pipe_ok && g_prefill_variant == 1;
+    moe_status st = pipe_gateup ? launch_gateup_pipe(a, stream) : launch_gateup_grouped(a, stream);
+    if (st != MOE_OK) return st;
+    st = pipe_down ? launch_down_pipe(a, stream) : launch_down_grouped(a, stream);
+    if (st != MOE_OK) return st;
+    return launch_combine(a, stream);
+}
+
 moe_status launch_decode_forward(const FwdArgs& a, uint32_t* sync, hipStream_t stream) {
     if (g_decode_variant == 1 && fused_decode_supported(a.T, a.k, a.H, a.I))
         return launch_decode_fused(a, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, sync, stream);
     if (g_decode_variant == 2 && fused_decode_supported(a.T, a.k, a.H, a.I)) return launch_decode_two(a, stream);
     if (decode_path_supported(a.T, a.k, a.H, a.I)) return launch_forward_decode(a, stream);
-    return launch_forward_prefill(a, stream);
+    return launch_prefill(a, stream);
 }
 
 // Checks shared by moe_w4a16_forward and moe_w4a16_route_forward.
@@ -315,6 +340,12 @@ moe_status moe_w4a16_workspace_init(void* d_ws, size_t ws_bytes, hipStream_t str
 }
 
 void moe_debug_set_decode_wait_limit(int32_t polls) { set_decode_wait_limit(polls); }
+
+moe_status moe_debug_set_prefill_variant(int32_t variant) {
+    if (variant < 0 || variant > 2) return MOE_ERR_INVALID_ARG;
+    g_prefill_variant = variant;
+    return MOE_OK;
+}
 
 moe_status moe_debug_set_decode_variant(int32_t variant) {
     if (variant < 0 || variant > 2) return MOE_ERR_INVALID_ARG;

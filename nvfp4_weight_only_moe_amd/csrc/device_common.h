@@ -99,6 +99,20 @@ __device__ __forceinline__ void wave_copy_1k_to_lds(const uint4* __restrict__ sr
     __builtin_amdgcn_global_load_lds(src + lane, (lds_void*)lds, 16, 0, 0);
 }
 
+// The same LDS-DMA, 16 or 4 bytes per lane, issued as inline assembly: the
+// compiler does not see the LDS write, so it inserts no wait on it before
+// later LDS reads (it would wait for every load in flight); the caller must
+// wait (vmcnt) and synchronise before the data is read.  The s_nop gives the
+// M0 write its wait state.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, lds_void* ldst) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"((uint32_t)(uintptr_t)ldst)
+                 : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void* gsrc, lds_void* ldst) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "{m0}"((uint32_t)(uintptr_t)ldst)
+                 : "memory");
+}
+
 // Wait for every outstanding memory operation of this wave.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 

@@ -73,6 +73,13 @@ moe_status launch_decode_fused(const FwdArgs& a, const float* logits, int32_t* i
 moe_status launch_decode_two(const FwdArgs& a, hipStream_t s);
 moe_status launch_zero_words(uint32_t* p, int n, hipStream_t s);
 moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s);
-moe_status launch_forward_prefill(const FwdArgs& a, hipStream_t s);
+// moe_prefill.hip: register-staged grouped GEMMs and the combine
+moe_status launch_gateup_grouped(const FwdArgs& a, hipStream_t s);
+moe_status launch_down_grouped(const FwdArgs& a, hipStream_t s);
+moe_status launch_combine(const FwdArgs& a, hipStream_t s);
+// moe_prefill_pipe.hip: LDS-pipelined grouped GEMMs
+bool prefill_pipe_supported(int H, int I);
+moe_status launch_gateup_pipe(const FwdArgs& a, hipStream_t s);
+moe_status launch_down_pipe(const FwdArgs& a, hipStream_t s);
 
 }  // namespace moe

@@ -310,7 +310,7 @@ moe_status launch_gemm_bm(const GemmParams& P, int64_t slots, int E, hipStream_t
 
 }  // namespace
 
-moe_status launch_forward_prefill(const FwdArgs& a, hipStream_t s) {
+moe_status launch_gateup_grouped(const FwdArgs& a, hipStream_t s) {
     const int64_t slots = (int64_t)a.T * a.k;
     GemmParams g{};
     g.a = a.x;
@@ -325,9 +325,11 @@ moe_status launch_forward_prefill(const FwdArgs& a, hipStream_t s) {
     g.offsets = a.offsets;
     g.out = a.h;
     g.ntn = a.I / 128;
-    moe_status st = launch_gemm_bm<true>(g, slots, a.E, s);
-    if (st != MOE_OK) return st;
+    return launch_gemm_bm<true>(g, slots, a.E, s);
+}
 
+moe_status launch_down_grouped(const FwdArgs& a, hipStream_t s) {
+    const int64_t slots = (int64_t)a.T * a.k;
     GemmParams d{};
     d.a = a.h;
     d.sorted_slots = a.sorted_slots;
@@ -340,9 +342,10 @@ moe_status launch_forward_prefill(const FwdArgs& a, hipStream_t s) {
     d.offsets = a.offsets;
     d.out = a.y;
     d.ntn = a.H / 256;
-    st = launch_gemm_bm<false>(d, slots, a.E, s);
-    if (st != MOE_OK) return st;
+    return launch_gemm_bm<false>(d, slots, a.E, s);
+}
 
+moe_status launch_combine(const FwdArgs& a, hipStream_t s) {
     MOE_LAUNCH("combine", k_combine, dim3((a.H + 2047) / 2048, a.T), dim3(256), 0, s, (const float*)a.y, a.topk_w,
                a.slot_pos, a.T, a.H, a.k, a.out);
     return MOE_OK;

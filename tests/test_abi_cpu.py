@@ -144,3 +144,11 @@ def test_decode_variant_hook(L):
     for v in (0, 1, 2):
         assert L.moe_debug_set_decode_variant(v) == 0
     assert L.moe_debug_set_decode_variant(0) == 0
+
+
+def test_prefill_variant_hook(L):
+    assert L.moe_debug_set_prefill_variant(3) == -1
+    assert L.moe_debug_set_prefill_variant(-1) == -1
+    assert L.moe_debug_set_prefill_variant(0) == 0
+    assert L.moe_debug_set_prefill_variant(1) == 0
+    assert L.moe_debug_set_prefill_variant(2) == 0

@@ -256,3 +256,39 @@ def test_decode_variants_agree(T, H, I, E, k, seed):
         B.moe_debug_set_decode_variant(0)
     for v in (1, 2):
         compare_out(outs[v], outs[0], f"variant {v} vs 0")
+
+
+PREFILL_CASES = [
+    # the LDS-pipelined kernels take H % 512 == 0 and I % 256 == 0
+    (33, 512, 256, 8, 2, 90),        # one short row tile per expert, K = 256 (four stages)
+    (100, 1024, 512, 16, 4, 91),     # ragged row tiles
+    (257, 512, 256, 4, 2, 92),       # several row tiles per expert
+    (300, 1024, 512, 8, 8, 93),      # k == E
+    (40, 1024, 256, 1, 1, 94),       # E = 1, k = 1
+    (600, 2048, 1536, 8, 4, 95),     # longer K: the ring runs across tile boundaries
+    (100, 512, 384, 16, 4, 96),      # I % 256 != 0: the register-staged kernels in every variant
+    (700, 512, 256, 8, 4, 97),       # 350 rows per expert: variant 2 mixes the kernel sets
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,seed", PREFILL_CASES)
+def test_prefill_variants_agree(T, H, I, E, k, seed):
+    """Every grouped-GEMM kernel choice matches the oracle and the others."""
+    p = Problem(T, H, I, E, k, seed)
+    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
+    lg, xb = to_dev(p.logits), to_dev(p.xb, torch.int16)
+    ref = p.reference()
+    outs = []
+    try:
+        for v in (0, 1, 2):
+            B.moe_debug_set_prefill_variant(v)
+            log(f"prefill variant {v} T{T} H{H} I{I} E{E} k{k}")
+            out, _ = B.moe_w4a16_route_forward(lg, xb, gate, up, down, k)
+            torch.cuda.synchronize()
+            got = bf16_bits_to_f64(out)
+            compare_out(got, ref, f"prefill variant {v} T{T}")
+            outs.append(got)
+    finally:
+        B.moe_debug_set_prefill_variant(2)
+    for v in (1, 2):
+        compare_out(outs[v], outs[0], f"prefill variant {v} vs 0")
