@@ -50,9 +50,10 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--decode-variant", type=int, default=0,
+    ap.add_argument("--decode-variant", type=int, default=3,
                     help="decode-shape kernels (moe_debug_set_decode_variant): 0 per-expert-block "
-                         "kernels (default), 1 one persistent launch, 2 its two halves")
+                         "kernels, 1 one persistent launch, 2 its two halves, 3 the kernels of 0 "
+                         "with a single token's route inside the gate/up kernel (default)")
     ap.add_argument("--prefill-variant", type=int, default=2,
                     help="grouped-GEMM kernels (moe_debug_set_prefill_variant): 0 register-staged, "
                          "1 LDS-pipelined, 2 chosen per product by rows per expert (default)")
@@ -72,9 +73,10 @@ def packed_bytes(N, K):
 KERNEL_SOURCES = {
     "dec_fused": ["decode_fused_kernel.h", "device_common.h", "route_common.h"],
     "dec_gateup": ["moe_decode.hip", "device_common.h"],
+    "dec_gateup_route": ["moe_decode.hip", "device_common.h", "route_common.h"],
     "dec_down": ["moe_decode.hip", "device_common.h"],
-    "gemm_gateup": ["moe_prefill.hip", "device_common.h"],
-    "gemm_down": ["moe_prefill.hip", "device_common.h"],
+    "gemm_gateup": ["moe_prefill.hip", "moe_prefill_pipe.hip", "device_common.h"],
+    "gemm_down": ["moe_prefill.hip", "moe_prefill_pipe.hip", "device_common.h"],
 }
 
 
@@ -239,6 +241,7 @@ def main():
     kernel_work = {
         "dec_fused": ("hbm", U * (w_gu + w_d) + T * H * 2 * 2 + T * wl.E * 4),
         "dec_gateup": ("hbm", U * w_gu + T * H * 2),
+        "dec_gateup_route": ("hbm", U * w_gu + T * H * 2 + T * wl.E * 4),
         "dec_down": ("hbm", U * w_d + T * H * 2),
         "gemm_gateup": ("mfma", 4.0 * T * k * H * I),
         "gemm_down": ("mfma", 2.0 * T * k * H * I),

@@ -215,10 +215,13 @@ void moe_debug_set_decode_wait_limit(int32_t polls);
 
 /*
  * Benchmarking and test hook: which kernels run decode shapes (1-8 tokens).
- * 0 (default): a gate/up kernel and a down kernel, one workgroup per
- * (expert, block of rows); 1: the whole layer in one persistent launch
- * (with the route, for moe_w4a16_route_forward); 2: the gate/up and down
- * halves of that persistent kernel as two launches.  All give results within the
+ * 0: a gate/up kernel and a down kernel, one workgroup per (expert, block
+ * of rows); 1: the whole layer in one persistent launch (with the route,
+ * for moe_w4a16_route_forward); 2: the gate/up and down halves of that
+ * persistent kernel as two launches; 3 (default): the kernels of 0, and for
+ * moe_w4a16_route_forward with one token the routing is computed inside the
+ * gate/up kernel from the logits (no separate route launch; other calls run
+ * 0).  All give results within the
  * forward's tolerance of each other; each is deterministic.  Shapes a
  * variant does not cover use variant 0.  Process-wide.  Returns
  * MOE_ERR_INVALID_ARG for other values.

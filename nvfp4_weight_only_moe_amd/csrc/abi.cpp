@@ -111,10 +111,13 @@ WsLayout ws_layout(void* d_ws, int T, int H, int I, int k) {
 // Decode-shape kernels: 0 = gate/up and down kernels of moe_decode.hip,
 // 1 = one launch for the whole layer (route included when routing here),
 // 2 = the gate/up and down halves of the single-launch kernel as two
-// launches.  Chosen by moe_debug_set_decode_variant (a benchmarking and test
-// hook); 0, the fastest measured on MI355X, is the default.  Shapes a
+// launches, 3 = the kernels of 0, with the routing of a single token computed
+// by the gate/up kernel (moe_w4a16_route_forward with T == 1; everything else
+// runs 0).  Chosen by moe_debug_set_decode_variant (a benchmarking and test
+// hook); 3 is the default: on MI355X at one token (H 5120, I 1536, 256
+// experts, top-8) it saves the route launch, 32.0 us per layer against 34.6.  Shapes a
 // variant does not cover fall back to 0, then to the grouped-GEMM path.
-int g_decode_variant = 0;
+int g_decode_variant = 3;
 
 // Grouped-GEMM kernels for larger T: 0 = register-staged (k_grouped_gemm)
 // for both products, 1 = LDS-pipelined (k_gemm_pipe) for both, 2 = chosen
@@ -326,6 +329,9 @@ moe_status moe_w4a16_route_forward(const float* d_logits, const uint16_t* d_x, i
     if (g_decode_variant == 1 && fused_decode_supported(T, k, H, I))
         return launch_decode_fused(a, d_logits, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots,
                                    d_slot_pos, L.sync, stream);
+    if (g_decode_variant == 3 && T == 1 && decode_path_supported(T, k, H, I))
+        return launch_forward_decode_routed(a, d_logits, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots,
+                                            d_slot_pos, stream);
     st = launch_route(d_logits, T, E, k, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots, d_slot_pos,
                       L.route, stream);
     if (st != MOE_OK) return st;
@@ -348,7 +354,7 @@ moe_status moe_debug_set_prefill_variant(int32_t variant) {
 }
 
 moe_status moe_debug_set_decode_variant(int32_t variant) {
-    if (variant < 0 || variant > 2) return MOE_ERR_INVALID_ARG;
+    if (variant < 0 || variant > 3) return MOE_ERR_INVALID_ARG;
     g_decode_variant = variant;
     return MOE_OK;
 }

@@ -73,6 +73,12 @@ moe_status launch_decode_fused(const FwdArgs& a, const float* logits, int32_t* i
 moe_status launch_decode_two(const FwdArgs& a, hipStream_t s);
 moe_status launch_zero_words(uint32_t* p, int n, hipStream_t s);
 moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s);
+// the same two kernels with the routing computed by the gate/up kernel from
+// the logits (it stores the routing outputs, which the down kernel reads);
+// one token only (MOE_ERR_UNSUPPORTED otherwise)
+moe_status launch_forward_decode_routed(const FwdArgs& a, const float* logits, int32_t* ids, float* w,
+                                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* pos,
+                                        hipStream_t s);
 // moe_prefill.hip: register-staged grouped GEMMs and the combine
 moe_status launch_gateup_grouped(const FwdArgs& a, hipStream_t s);
 moe_status launch_down_grouped(const FwdArgs& a, hipStream_t s);

@@ -29,6 +29,7 @@
 //     any of them is used.
 #include "device_common.h"
 #include "internal.h"
+#include "route_common.h"
 
 namespace moe {
 namespace {
@@ -53,20 +54,99 @@ constexpr int kXTokens = 2;             // activation rows staged in LDS at a ti
 // go straight to LDS, and the codes of all stages are requested before any
 // is used: stages are computed in order as they land (vector loads complete
 // in issue order).
-template <int CPL, int RW, int EPL>
-__global__ void __launch_bounds__(kGuThreads, 4)
+// Routing computed by the gate/up kernel itself, for one token (decode
+// variant 3): every workgroup recomputes the token's top-k from its E logits
+// and the expert order of the k slots, which replaces the lookup of the
+// routing outputs (one dependent load either way) and saves the route
+// launch; the workgroups of expert column 0 store the routing outputs for the
+// down kernel and the caller.  With more tokens every workgroup would repeat
+// all their top-k selections, so those shapes route in their own kernel.
+struct GuRoute {
+    const float* logits;        // [1][E]
+    int32_t* ids;               // [k]
+    float* w;                   // [k]
+    int32_t* counts;            // [E]
+    int32_t* offsets;           // [E + 1]
+    int32_t* sorted_slots;      // [k]
+    int32_t* slot_pos;          // [k]
+};
+
+template <int CPL, int RW, int EPL, bool ROUTE>
+__global__ void __launch_bounds__(kGuThreads, 3)
 k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slots,
              const uint8_t* gc, const uint8_t* gs, const float* __restrict__ gg,
              const uint8_t* uc, const uint8_t* us, const float* __restrict__ ug,
              const int32_t* __restrict__ counts, const int32_t* __restrict__ sorted_slots,
-             uint16_t* __restrict__ h) {
+             uint16_t* __restrict__ h, const GuRoute R) {
     extern __shared__ uint4 xs[];   // [kXTokens][H / 8]
+    __shared__ int s_ids[kDecodeMaxSlots], s_pos[kDecodeMaxSlots], s_sorted[kDecodeMaxSlots];
+    __shared__ float s_w[kDecodeMaxSlots];
+    __shared__ int s_list[kDecodeMaxSlots], s_ucnt[kDecodeMaxSlots], s_uoff[kDecodeMaxSlots];
+    __shared__ int s_U;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int my_slot = lane < slots ? sorted_slots[lane] : 0;   // slots <= 64 on this path
-    const ActiveExpert ae = nth_active_expert<EPL>(counts, E, blockIdx.y);
-    if (ae.e < 0) return;
-    const int e = ae.e, ne = ae.count, p0 = ae.first_row;
+    int my_slot, e, ne, p0, U = 0;
+    if constexpr (ROUTE) {
+        // nothing else is in flight while the logits load: the barriers below
+        // then wait for no memory traffic
+        if (wave == 0) {
+            int id;
+            float wt;
+            wave_topk_select<EPL>(R.logits, E, k, id, wt);
+            if (lane < k) {
+                s_ids[lane] = id;
+                s_w[lane] = wt;
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // rank of each slot by (expert, flat index): expert bits from the
+            // top, the lanes still equal so far split into smaller and equal
+            int nbits = 1;
+            while ((1 << nbits) < E) ++nbits;
+            const bool valid = lane < slots;
+            const int ex = valid ? s_ids[lane] : 0;
+            uint64_t eq = __ballot(valid), lessm = 0;
+            for (int b = nbits - 1; b >= 0; --b) {
+                const bool bit = (ex >> b) & 1;
+                const uint64_t B = __ballot(valid && bit);
+                if (bit) {
+                    lessm |= eq & ~B;
+                    eq &= B;
+                } else {
+                    eq &= ~B;
+                }
+            }
+            const int less = __popcll(lessm);
+            const uint64_t before = eq & lanemask_lt();
+            const bool first = valid && before == 0;
+            const uint64_t firsts = __ballot(first);
+            if (valid) {
+                const int pos = less + __popcll(before);
+                s_pos[lane] = pos;
+                s_sorted[pos] = lane;
+            }
+            if (first) {
+                const int u = __popcll(firsts & lessm);
+                s_list[u] = ex;
+                s_ucnt[u] = __popcll(eq);
+                s_uoff[u] = less;
+            }
+            if (lane == 0) s_U = __popcll(firsts);
+        }
+        __syncthreads();
+        U = s_U;
+        if ((int)blockIdx.y >= U) return;
+        e = s_list[blockIdx.y];
+        ne = s_ucnt[blockIdx.y];
+        p0 = s_uoff[blockIdx.y];
+        my_slot = lane < slots ? s_sorted[lane] : 0;
+    } else {
+        my_slot = lane < slots ? sorted_slots[lane] : 0;   // slots <= 64 on this path
+        const ActiveExpert ae = nth_active_expert<EPL>(counts, E, blockIdx.y);
+        if (ae.e < 0) return;
+        e = ae.e; ne = ae.count; p0 = ae.first_row;
+    }
     const int H8 = H / 8;
     constexpr int ncr = 32 * CPL;            // 32-wide chunks per weight row (H = 1024 * CPL)
 
@@ -84,41 +164,41 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
 
     const int nb = (blockIdx.x * kGuWaves + wave) * (2 * RW);   // first feature of this wave
     const float g_gate = gg[e], g_up = ug[e];
-    uint4 cg[2][CPL], cu[2][CPL];
-    uint32_t sg[2][CPL], su[2][CPL];
-#define MOE_GU_LOAD(r, b)                                                                       \
-    do {                                                                                        \
-        const int64_t row_ = (int64_t)e * I + min(nb + 2 * (r), I - 2);                         \
-        const uint4* gcr_ = reinterpret_cast<const uint4*>(gc + row_ * (H / 2));                \
-        const uint4* ucr_ = reinterpret_cast<const uint4*>(uc + row_ * (H / 2));                \
-        const uint16_t* gsr_ = reinterpret_cast<const uint16_t*>(gs + row_ * (H / 16));         \
-        const uint16_t* usr_ = reinterpret_cast<const uint16_t*>(us + row_ * (H / 16));         \
-        _Pragma("unroll") for (int j = 0; j < CPL; ++j) {                                       \
-            const int q = lane + kWave * j;                                                     \
-            cg[b][j] = gcr_[q];                                                                 \
-            cu[b][j] = ucr_[q];                                                                 \
-            sg[b][j] = gsr_[q];                                                                 \
-            su[b][j] = usr_[q];                                                                 \
-        }                                                                                       \
-        asm volatile("" ::: "memory");  /* issue here, not at the first use */                  \
-    } while (0)
-    MOE_GU_LOAD(0, 0);
-    wait_vmem_at_most<0>();                  // x rows (issued first) and stage 0's codes
+    // the codes of all RW stages are requested at once and stay in registers
+    // for every token of the expert
+    uint4 cg[RW][CPL], cu[RW][CPL];
+    uint32_t sg[RW][CPL], su[RW][CPL];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const int64_t row = (int64_t)e * I + min(nb + 2 * r, I - 2);
+        const uint4* gcr = reinterpret_cast<const uint4*>(gc + row * (H / 2));
+        const uint4* ucr = reinterpret_cast<const uint4*>(uc + row * (H / 2));
+        const uint16_t* gsr = reinterpret_cast<const uint16_t*>(gs + row * (H / 16));
+        const uint16_t* usr = reinterpret_cast<const uint16_t*>(us + row * (H / 16));
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int q = lane + kWave * j;
+            cg[r][j] = gcr[q];
+            cu[r][j] = ucr[q];
+            sg[r][j] = gsr[q];
+            su[r][j] = usr[q];
+        }
+    }
+    asm volatile("" ::: "memory");           // issue here, not at the first use
+    // x rows (issued first) and stage 0's codes; later stages stay in flight
+    wait_vmem_at_most<4 * CPL * (RW - 1)>();
     __builtin_amdgcn_s_barrier();            // plain barrier: a fence would wait for every load
 
 #pragma unroll 1
     for (int q0 = 0; q0 < ne; q0 += kXTokens) {
-        if (q0 > 0) {                        // next tokens: restage x, reload stage 0
+        if (q0 > 0) {                        // next tokens: restage x
             __syncthreads();
             stage_x(q0);
-            MOE_GU_LOAD(0, 0);
             wait_all_memory();
             __syncthreads();
         }
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
-            const int b = r & 1;
-            if (r + 1 < RW) MOE_GU_LOAD(r + 1, b ^ 1);
             const int n = nb + 2 * r;
 #pragma unroll 1
             for (int qt = q0; qt < min(ne, q0 + kXTokens); ++qt) {
@@ -132,8 +212,8 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
                     const uint4 x0 = xc[0], x1 = xc[1], x2 = xc[2], x3 = xc[3];
                     // opaque copies: keep the code decode inside the token loop instead
                     // of hoisting 2 x CPL x 16 decoded pairs into registers
-                    uint4 g4 = cg[b][j], u4 = cu[b][j];
-                    const uint32_t gsc = sg[b][j], usc = su[b][j];
+                    uint4 g4 = cg[r][j], u4 = cu[r][j];
+                    const uint32_t gsc = sg[r][j], usc = su[r][j];
                     asm volatile("" : "+v"(g4.x), "+v"(g4.y), "+v"(g4.z), "+v"(g4.w));
                     asm volatile("" : "+v"(u4.x), "+v"(u4.y), "+v"(u4.z), "+v"(u4.w));
                     const float dg_ = e4m3_byte_to_f32<0>(gsc) * group_dot(make_uint2(g4.x, g4.y), x0, x1) +
@@ -156,7 +236,31 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
             }
         }
     }
-#undef MOE_GU_LOAD
+
+    // routing outputs: workgroup (0, 0) the per-slot arrays, the workgroups
+    // of expert column 0 their share of the per-expert ones
+    if constexpr (ROUTE) {
+        if (blockIdx.y != 0) return;
+        if (blockIdx.x == 0 && threadIdx.x < slots) {
+            const int i = threadIdx.x, pos = s_pos[i];
+            R.ids[i] = s_ids[i];
+            R.w[i] = s_w[i];
+            R.slot_pos[i] = pos;
+            R.sorted_slots[pos] = i;
+        }
+        const int G = gridDim.x;
+        const int e0 = (int)((int64_t)blockIdx.x * E / G), e1 = (int)((int64_t)(blockIdx.x + 1) * E / G);
+        for (int ee = e0 + (int)threadIdx.x; ee < e1; ee += kGuThreads) {
+            int cnt = 0, off = 0;
+            for (int u = 0; u < U; ++u) {
+                if (s_list[u] < ee) off += s_ucnt[u];
+                if (s_list[u] == ee) cnt = s_ucnt[u];
+            }
+            R.counts[ee] = cnt;
+            R.offsets[ee] = off;
+        }
+        if (blockIdx.x == G - 1 && threadIdx.x == 0) R.offsets[E] = slots;
+    }
 }
 
 // GPL2 = 16-groups per half-wave lane along I (I = 512 * GPL2); MAXT tokens.
@@ -290,25 +394,27 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
     }
 }
 
-constexpr int kGuRowsPerWave = 1;      // stages of two features per gate/up wave
+constexpr int kGuRowsPerWave = 2;      // stages of two features per gate/up wave
 
-template <int CPL, int EPL>
-moe_status launch_gateup_epl(const FwdArgs& a, hipStream_t s) {
+template <int CPL, int EPL, bool ROUTE>
+moe_status launch_gateup_epl(const FwdArgs& a, const GuRoute& R, hipStream_t s) {
     const int rows_per_block = kGuWaves * 2 * kGuRowsPerWave;
     const dim3 grid((a.I + rows_per_block - 1) / rows_per_block, std::min(a.T * a.k, a.E));
     const size_t shmem = (size_t)std::min(a.T, kXTokens) * a.H * sizeof(uint16_t);
-    auto kern = k_dec_gateup<CPL, kGuRowsPerWave, EPL>;
+    auto kern = k_dec_gateup<CPL, kGuRowsPerWave, EPL, ROUTE>;
     if (allow_dynamic_lds(reinterpret_cast<const void*>(kern), shmem) != MOE_OK) return MOE_ERR_HIP;
-    MOE_LAUNCH("dec_gateup", kern, grid, dim3(kGuThreads), shmem, s, a.x, a.H, a.I, a.E, a.k, a.T * a.k,
-               (const uint8_t*)a.gate->codes, (const uint8_t*)a.gate->scales, (const float*)a.gate->global_scale,
-               (const uint8_t*)a.up->codes, (const uint8_t*)a.up->scales, (const float*)a.up->global_scale,
-               a.counts, a.sorted_slots, a.h);
+    MOE_LAUNCH(ROUTE ? "dec_gateup_route" : "dec_gateup", kern, grid, dim3(kGuThreads), shmem, s, a.x, a.H, a.I,
+               a.E, a.k, a.T * a.k, (const uint8_t*)a.gate->codes, (const uint8_t*)a.gate->scales,
+               (const float*)a.gate->global_scale, (const uint8_t*)a.up->codes, (const uint8_t*)a.up->scales,
+               (const float*)a.up->global_scale, a.counts, a.sorted_slots, a.h, R);
     return MOE_OK;
 }
 
 template <int CPL>
-moe_status launch_gateup_gpl(const FwdArgs& a, hipStream_t s) {
-    return a.E <= 256 ? launch_gateup_epl<CPL, 4>(a, s) : launch_gateup_epl<CPL, 16>(a, s);
+moe_status launch_gateup_gpl(const FwdArgs& a, const GuRoute* R, hipStream_t s) {
+    if (R) return a.E <= 256 ? launch_gateup_epl<CPL, 4, true>(a, *R, s) : launch_gateup_epl<CPL, 16, true>(a, *R, s);
+    const GuRoute none{};
+    return a.E <= 256 ? launch_gateup_epl<CPL, 4, false>(a, none, s) : launch_gateup_epl<CPL, 16, false>(a, none, s);
 }
 
 int down_waves_per_block(int H) {
@@ -350,17 +456,19 @@ bool decode_path_supported(int T, int k, int H, int I) {
            I / 512 <= 4;
 }
 
-moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s) {
+namespace {
+
+moe_status launch_decode_pair(const FwdArgs& a, const GuRoute* R, hipStream_t s) {
     moe_status st;
     switch (a.H / 1024) {
-        case 1: st = launch_gateup_gpl<1>(a, s); break;
-        case 2: st = launch_gateup_gpl<2>(a, s); break;
-        case 3: st = launch_gateup_gpl<3>(a, s); break;
-        case 4: st = launch_gateup_gpl<4>(a, s); break;
-        case 5: st = launch_gateup_gpl<5>(a, s); break;
-        case 6: st = launch_gateup_gpl<6>(a, s); break;
-        case 7: st = launch_gateup_gpl<7>(a, s); break;
-        case 8: st = launch_gateup_gpl<8>(a, s); break;
+        case 1: st = launch_gateup_gpl<1>(a, R, s); break;
+        case 2: st = launch_gateup_gpl<2>(a, R, s); break;
+        case 3: st = launch_gateup_gpl<3>(a, R, s); break;
+        case 4: st = launch_gateup_gpl<4>(a, R, s); break;
+        case 5: st = launch_gateup_gpl<5>(a, R, s); break;
+        case 6: st = launch_gateup_gpl<6>(a, R, s); break;
+        case 7: st = launch_gateup_gpl<7>(a, R, s); break;
+        case 8: st = launch_gateup_gpl<8>(a, R, s); break;
         default: return MOE_ERR_UNSUPPORTED;
     }
     if (st != MOE_OK) return st;
@@ -371,6 +479,18 @@ moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s) {
         case 4: return launch_down_gpl<4>(a, s);
         default: return MOE_ERR_UNSUPPORTED;
     }
+}
+
+}  // namespace
+
+moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s) { return launch_decode_pair(a, nullptr, s); }
+
+moe_status launch_forward_decode_routed(const FwdArgs& a, const float* logits, int32_t* ids, float* w,
+                                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* pos,
+                                        hipStream_t s) {
+    if (a.T != 1) return MOE_ERR_UNSUPPORTED;
+    const GuRoute R{logits, ids, w, counts, offsets, sorted, pos};
+    return launch_decode_pair(a, &R, s);
 }
 
 }  // namespace moe

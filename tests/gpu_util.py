@@ -17,6 +17,8 @@ from oracle import moe as omoe
 from nvfp4_weight_only_moe_amd import binding as B
 from nvfp4_weight_only_moe_amd import workloads as wls
 
+# decode-shape kernel set the library selects by default (moe_debug_set_decode_variant)
+DEFAULT_DECODE_VARIANT = 3
 DEV = "cuda:0"
 PROJ = ((wls.GATE, "gate"), (wls.UP, "up"), (wls.DOWN, "down"))
 THREADS = min(16, os.cpu_count() or 4)

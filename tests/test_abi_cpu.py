@@ -139,11 +139,11 @@ def test_workspace_init_and_size(L):
 
 
 def test_decode_variant_hook(L):
-    assert L.moe_debug_set_decode_variant(3) == -1
+    assert L.moe_debug_set_decode_variant(4) == -1
     assert L.moe_debug_set_decode_variant(-1) == -1
-    for v in (0, 1, 2):
+    for v in (0, 1, 2, 3):
         assert L.moe_debug_set_decode_variant(v) == 0
-    assert L.moe_debug_set_decode_variant(0) == 0
+    assert L.moe_debug_set_decode_variant(3) == 0    # the default
 
 
 def test_prefill_variant_hook(L):

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import DEV, Problem, bf16_bits_to_f64, compare_out, log, to_dev
+from gpu_util import DEFAULT_DECODE_VARIANT, DEV, Problem, bf16_bits_to_f64, compare_out, log, to_dev
 from nvfp4_weight_only_moe_amd import binding as B
 from nvfp4_weight_only_moe_amd import workloads as wls
 
@@ -147,10 +147,10 @@ def test_hip_graph_replay_matches_eager(T, H, I):
 @pytest.fixture
 def decode_variant(request):
     """Select the decode-shape kernels (moe_debug_set_decode_variant) for one
-    test; the default (0) is restored afterwards."""
+    test; the default is restored afterwards."""
     B.moe_debug_set_decode_variant(request.param)
     yield request.param
-    B.moe_debug_set_decode_variant(0)
+    B.moe_debug_set_decode_variant(DEFAULT_DECODE_VARIANT)
 
 
 DECODE_CASES = [
@@ -162,13 +162,13 @@ DECODE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("decode_variant", [0, 1, 2], indirect=True)
+@pytest.mark.parametrize("decode_variant", [0, 1, 2, 3], indirect=True)
 @pytest.mark.parametrize("T,H,I,E,k,seed", DECODE_CASES + [(40, 512, 256, 16, 4, 75)])
 def test_route_forward_matches_route_then_forward(T, H, I, E, k, seed, decode_variant):
     """moe_w4a16_route_forward stores exactly moe_route_topk's outputs and
-    exactly moe_w4a16_forward's result (with the single-launch variant the
-    route runs inside the layer's kernel), for every decode variant, and
-    matches the oracle."""
+    exactly moe_w4a16_forward's result (with variants 1 and 3 the route runs
+    inside the layer's kernels), for every decode variant, and matches the
+    oracle."""
     p = Problem(T, H, I, E, k, seed)
     gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
     lg, xb = to_dev(p.logits), to_dev(p.xb, torch.int16)
@@ -210,7 +210,7 @@ def test_decode_local_h_path_is_bit_identical(T, H, I, E, k, seed, decode_varian
     assert torch.equal(again, out_ref)
 
 
-@pytest.mark.parametrize("decode_variant", [1, 2], indirect=True)
+@pytest.mark.parametrize("decode_variant", [1, 2, 3], indirect=True)
 def test_workspace_reused_across_problems(decode_variant):
     """One workspace serves consecutive calls with different inputs, routings
     and shapes: no call reads another call's intermediate values, and
@@ -237,15 +237,15 @@ def test_workspace_reused_across_problems(decode_variant):
 
 @pytest.mark.parametrize("T,H,I,E,k,seed", DECODE_CASES)
 def test_decode_variants_agree(T, H, I, E, k, seed):
-    """The three decode-shape kernel sets each match the oracle, and agree
-    with one another to the forward's tolerance."""
+    """The decode-shape kernel sets each match the oracle, and agree with
+    one another to the forward's tolerance."""
     p = Problem(T, H, I, E, k, seed)
     gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
     lg, xb = to_dev(p.logits), to_dev(p.xb, torch.int16)
     ref = p.reference()
     outs = []
     try:
-        for v in (0, 1, 2):
+        for v in (0, 1, 2, 3):
             B.moe_debug_set_decode_variant(v)
             out, _ = B.moe_w4a16_route_forward(lg, xb, gate, up, down, k)
             torch.cuda.synchronize()
@@ -253,8 +253,8 @@ def test_decode_variants_agree(T, H, I, E, k, seed):
             compare_out(got, ref, f"variant {v} T{T}")
             outs.append(got)
     finally:
-        B.moe_debug_set_decode_variant(0)
-    for v in (1, 2):
+        B.moe_debug_set_decode_variant(DEFAULT_DECODE_VARIANT)
+    for v in (1, 2, 3):
         compare_out(outs[v], outs[0], f"variant {v} vs 0")
 
 

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from oracle import moe as omoe
-from gpu_util import (DEV, bf16_bits_to_f64, compare_out, full_layer_gpu, log, oracle_experts,
+from gpu_util import (DEFAULT_DECODE_VARIANT, DEV, bf16_bits_to_f64, compare_out, full_layer_gpu, log, oracle_experts,
                       packed_to_numpy, to_dev)
 from nvfp4_weight_only_moe_amd import binding as B
 from nvfp4_weight_only_moe_amd import workloads as wls
@@ -73,7 +73,7 @@ def test_fullsize_decode_8_tokens():
     check_tokens(2, list(range(8)))
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
 @pytest.mark.parametrize("cfg", [1, 2])
 def test_fullsize_route_forward_decode(cfg, variant):
     """At full size, for every decode variant: moe_w4a16_route_forward equals
@@ -83,7 +83,7 @@ def test_fullsize_route_forward_decode(cfg, variant):
     try:
         _route_forward_case(cfg)
     finally:
-        B.moe_debug_set_decode_variant(0)
+        B.moe_debug_set_decode_variant(DEFAULT_DECODE_VARIANT)
 
 
 def _route_forward_case(cfg):
