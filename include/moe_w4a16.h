@@ -233,9 +233,9 @@ moe_status moe_debug_set_decode_variant(int32_t variant);
  * decode kernels do not take.  0: operands staged through registers, one
  * K stage in flight, for both products; 1: operands streamed to LDS by DMA
  * through a four-stage ring (128 x 512 output tiles), for both products;
- * 2 (default): the LDS-streamed kernel for gate/up when the mean rows per
- * touched expert (T * k / min(E, T * k)) is at least 256, the
- * register-staged kernels otherwise.  All give results within the forward's
+ * 2 (default): the LDS-streamed kernels when the mean rows per touched
+ * expert (T * k / min(E, T * k)) is at least 256, the register-staged
+ * kernels otherwise.  All give results within the forward's
  * tolerance of each other; each is deterministic.  Shapes the LDS-streamed
  * kernel does not cover (H % 512 or I % 256 nonzero) use 0.  Process-wide.
  * Returns MOE_ERR_INVALID_ARG for other values.

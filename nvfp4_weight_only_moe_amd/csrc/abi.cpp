@@ -121,12 +121,11 @@ int g_decode_variant = 3;
 
 // Grouped-GEMM kernels for larger T: 0 = register-staged (k_grouped_gemm)
 // for both products, 1 = LDS-pipelined (k_gemm_pipe) for both, 2 = chosen
-// per product from the mean rows per touched expert (the default).  The
-// pipelined kernel's 128-row tiles pay off on gate/up once experts hold a few
-// hundred rows (16K tokens, top-8 of 256: 5.9 ms against 7.3 ms on MI355X);
-// with few rows per expert its padding costs more than it saves, and on down
-// (K = I, short) the register-staged kernel measured as fast or faster.
-// Chosen by moe_debug_set_prefill_variant.
+// from the mean rows per touched expert (the default).  The pipelined
+// kernel's 128-row tiles pay off once experts hold a few hundred rows (16K
+// tokens, top-8 of 256 on MI355X: gate/up 4.6 ms against 7.3, down 2.5 ms
+// against 4.1); with few rows per expert (1K tokens: about 32) its padding
+// costs more than it saves.  Chosen by moe_debug_set_prefill_variant.
 int g_prefill_variant = 2;
 constexpr int64_t kPipeMinRowsPerExpert = 256;
 
@@ -134,12 +133,11 @@ moe_status launch_prefill(const FwdArgs& a, hipStream_t stream) {
     const bool pipe_ok = prefill_pipe_supported(a.H, a.I);
     const int64_t slots = (int64_t)a.T * a.k;
     const int64_t per_expert = slots / std::max<int64_t>(1, std::min<int64_t>(a.E, slots));
-    const bool pipe_gateup =
+    const bool pipe =
         pipe_ok && (g_prefill_variant == 1 || (g_prefill_variant == 2 && per_expert >= kPipeMinRowsPerExpert));
-    const bool pipe_down = pipe_ok && g_prefill_variant == 1;
-    moe_status st = pipe_gateup ? launch_gateup_pipe(a, stream) : launch_gateup_grouped(a, stream);
+    moe_status st = pipe ? launch_gateup_pipe(a, stream) : launch_gateup_grouped(a, stream);
     if (st != MOE_OK) return st;
-    st = pipe_down ? launch_down_pipe(a, stream) : launch_down_grouped(a, stream);
+    st = pipe ? launch_down_pipe(a, stream) : launch_down_grouped(a, stream);
     if (st != MOE_OK) return st;
     return launch_combine(a, stream);
 }

@@ -14,11 +14,12 @@
 //   * a ring of kStages stages keeps kStages - 1 stages in flight while one
 //     is computed, across tile boundaries (a workgroup walks its tiles as one
 //     sequence of (tile, stage) steps);
+//   * eight waves, two per SIMD: each owns 64 weight columns for all 128
+//     rows (128 accumulator registers), so the decode of one wave's codes
+//     and its LDS reads overlap the other wave's MFMAs;
 //   * LDS layouts are XOR-swizzled in 16-byte units so that the MFMA
 //     fragment reads (8 consecutive lanes, 8 consecutive rows or columns)
-//     hit distinct banks;
-//   * 16-row subtiles past the tile's last row skip their MFMAs, so a tile of
-//     an expert with few tokens costs what its rows need.
+//     hit distinct banks.
 // The K order inside a stage is permuted identically for both operands:
 // lane group q of an MFMA takes k = 16 q + 8 s .. 16 q + 8 s + 7 at k-step
 // s, so one 8-byte read gives a lane its 16 codes (one E4M3 group) for both
@@ -29,10 +30,11 @@
 namespace moe {
 namespace {
 
-constexpr int kPT = 256;                        // threads (4 waves)
+constexpr int kPT = 512;                        // threads: 8 waves, two per SIMD
+constexpr int kWaves = kPT / 64;
 constexpr int kBM = 128;                        // rows per tile
 constexpr int kBN = 512;                        // weight columns per tile (gate/up: 256 + 256)
-constexpr int kNS = 8;                          // 16-column subtiles per wave (a wave owns kBN / 4 columns)
+constexpr int kNS = kBN / kWaves / 16;          // 16-column subtiles per wave (a wave owns 64 columns)
 constexpr int kBK = 64;                         // K per stage
 constexpr int kStages = 4;                      // LDS ring
 constexpr int kAhead = kStages - 1;             // stages in flight while one is computed
@@ -41,9 +43,16 @@ constexpr int kBBytes = kBN * kBK / 2;          // 16 KiB codes
 constexpr int kSBytes = kBN * kBK / 16;         // 2 KiB scales
 constexpr int kStageBytes = kABytes + kBBytes + kSBytes;
 constexpr int kMGroup = 8;                      // row tiles per scheduling group
-// vector-memory operations one wave issues per stage: 4 activation, 4 code
-// and 2 scale LDS-DMA
-constexpr int kOpsPerStage = 10;
+// Waves 0 .. kDmaWaves - 1 (one per SIMD) issue a stage's LDS-DMA
+// operations: 1 KiB activation and code runs, 256-byte scale runs.  The
+// other wave of each SIMD goes straight from the stage barrier to its MFMAs
+// while its partner issues.
+constexpr int kDmaWaves = 4;
+constexpr int kADma = kABytes / 1024 / kDmaWaves;
+constexpr int kBDma = kBBytes / 1024 / kDmaWaves;
+constexpr int kSDma = kSBytes / 256 / kDmaWaves;
+constexpr int kOpsPerStage = kADma + kBDma + kSDma;
+static_assert(kADma == 4 && kBDma == 4 && kSDma == 2 && kNS == 4, "stage split over the waves");
 
 struct PipeParams {
     const uint16_t* a;          // gate/up: x [T][K]; down: h [T*k][K]
@@ -64,16 +73,19 @@ struct Tile {
     int e, p0, rows, nt;
 };
 
+// 8 codes (one E2M1 nibble each, k order) times their E4M3 group scale, as
+// bf16: the products are exact in bf16, so keeping the top half of each fp32
+// product is exact too.
 __device__ __forceinline__ bf16x8 decode8s(uint32_t word, float s) {
     const floatx2 p0 = e2m1x2_to_f32<0>(word);
     const floatx2 p1 = e2m1x2_to_f32<1>(word);
     const floatx2 p2 = e2m1x2_to_f32<2>(word);
     const floatx2 p3 = e2m1x2_to_f32<3>(word);
     u32x4 r;
-    r[0] = pack_bf16x2_exact(p0[0] * s, p0[1] * s);
-    r[1] = pack_bf16x2_exact(p1[0] * s, p1[1] * s);
-    r[2] = pack_bf16x2_exact(p2[0] * s, p2[1] * s);
-    r[3] = pack_bf16x2_exact(p3[0] * s, p3[1] * s);
+    r[0] = __builtin_amdgcn_perm(__float_as_uint(p0[1] * s), __float_as_uint(p0[0] * s), 0x07060302u);
+    r[1] = __builtin_amdgcn_perm(__float_as_uint(p1[1] * s), __float_as_uint(p1[0] * s), 0x07060302u);
+    r[2] = __builtin_amdgcn_perm(__float_as_uint(p2[1] * s), __float_as_uint(p2[0] * s), 0x07060302u);
+    r[3] = __builtin_amdgcn_perm(__float_as_uint(p3[1] * s), __float_as_uint(p3[0] * s), 0x07060302u);
     return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -107,19 +119,72 @@ __device__ __forceinline__ Tile pipe_tile(const PipeParams& P, const int* s_pref
     return d;
 }
 
-// Wait until at most n (0 .. kAhead - 1 stages) of this wave's
-// vector-memory operations are outstanding, then a workgroup barrier that
-// also waits for this wave's LDS reads (the ring slot about to be refilled
-// is no longer read).
-__device__ __forceinline__ void stage_barrier(int stages_after) {
-    switch (stages_after) {
-        case 0: wait_vmem_at_most<0>(); break;
-        case 1: wait_vmem_at_most<1 * kOpsPerStage>(); break;
-        default: wait_vmem_at_most<2 * kOpsPerStage>(); break;
+// A DMA wave waits until at most n (0 .. kAhead - 1 stages) of its
+// vector-memory operations are outstanding; then every wave meets at a
+// workgroup barrier that also waits for its LDS reads (the ring slot about
+// to be refilled is no longer read).
+__device__ __forceinline__ void stage_barrier(bool dma_wave, int stages_after) {
+    if (dma_wave) {
+        switch (stages_after) {
+            case 0: wait_vmem_at_most<0>(); break;
+            case 1: wait_vmem_at_most<1 * kOpsPerStage>(); break;
+            default: wait_vmem_at_most<2 * kOpsPerStage>(); break;
+        }
     }
     wait_lds_barrier();
 }
 static_assert(kAhead == 3, "stage_barrier covers up to two stages after the awaited one");
+
+// One K stage of a wave's 128 x 64 block.  Per k-step the eight activation
+// fragments are read once and each of the wave's four weight subtiles is
+// decoded once and meets all of them; the decode of the next subtile is
+// interleaved with the MFMAs of the current one.  Every 16-row subtile is
+// computed, also past a short tile's last row: skipping them would need a
+// second copy of the loop, and the two copies' accumulators would no longer
+// stay in place.  dma(p), p = 0 .. 7, runs after the p-th subtile's MFMAs:
+// a DMA wave issues part of a later stage's loads there, so a stall on a
+// full load queue overlaps the MFMAs already issued and the other wave's.
+template <class Dma>
+__device__ __forceinline__ void stage_mfma(floatx4 (&acc)[8][kNS], const uint8_t* base, const int (&colb)[kNS],
+                                           int lcol, int kq, Dma&& dma) {
+    const uint8_t* Bs = base + kABytes;
+    const uint8_t* Ss = Bs + kBBytes;
+    uint2 cw[kNS];
+    float sc[kNS];
+#pragma unroll
+    for (int ns = 0; ns < kNS; ++ns) {
+        const int col = colb[ns] + lcol;
+        cw[ns] = *reinterpret_cast<const uint2*>(Bs + col * 32 + 16 * ((kq >> 1) ^ ((col >> 3) & 1)) + 8 * (kq & 1));
+        sc[ns] = e4m3_to_f32(Ss[col * 4 + kq]);
+    }
+    bf16x8 bnext = decode8s(cw[0].x, sc[0]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 af[8];
+#pragma unroll
+        for (int ms = 0; ms < 8; ++ms) {
+            const int row = ms * 16 + lcol;
+            af[ms] = *reinterpret_cast<const bf16x8*>(base + row * 128 + 16 * ((2 * kq + ks) ^ (row & 7)));
+        }
+#pragma unroll
+        for (int ns = 0; ns < kNS; ++ns) {
+            const bf16x8 bf = bnext;
+            const int nn = ns + 1 < kNS ? ns + 1 : 0;     // next subtile (of the next k-step after the last)
+            if (ks == 0 || ns + 1 < kNS) bnext = decode8s((ns + 1 < kNS ? ks : 1) ? cw[nn].y : cw[nn].x, sc[nn]);
+#pragma unroll
+            for (int ms = 0; ms < 8; ++ms)
+                acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
+            // each MFMA followed by two VALU instructions (the next
+            // subtile's decode), so the matrix pipe does not wait for it
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU
+            }
+            dma(ks * kNS + ns);
+        }
+    }
+}
 
 template <bool GATEUP>
 __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
@@ -128,7 +193,9 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
     __shared__ int s_cnt[MOE_MAX_EXPERTS], s_off[MOE_MAX_EXPERTS];   // per expert: rows, first sorted row
     __shared__ __align__(16) int32_t s_rows[2][128];          // sorted-slot values of two tiles (gate/up)
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool dma_wave = wave < kDmaWaves;
     const int lcol = lane & 15, kq = lane >> 4;
 
     // tiles per expert -> exclusive prefix (row tiles x column tiles)
@@ -163,20 +230,24 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
     const int slot = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : (int)blockIdx.x;
     const int ntiles = total > slot ? (total - slot + G - 1) / G : 0;
     const int nst = P.K / kBK;
-    const int64_t nsteps = (int64_t)ntiles * nst;
+    const int nsteps = ntiles * nst;
 
-    // per-lane sources of the tile being prefetched
-    int64_t a_off[4];               // activation row byte offsets (4 rows per lane)
-    const uint8_t* b_src[4];        // code column bases (4 DMA per stage)
-    const uint8_t* s_src[2];        // scale column bases (2 DMA per stage)
-    int pf_tile = -1;
+    // per-lane sources of the tile being prefetched: activation rows; the
+    // lane's first code and scale runs (its later runs are 32 and 64
+    // columns further on, in the same matrix)
+    int a_row[kADma];
+    const uint8_t* b_src;
+    const uint8_t* s_src;
+    const int64_t b_step = (int64_t)32 * (P.K / 2), s_step = (int64_t)64 * (P.K / 16);
+    // next (tile, stage) to prefetch and its ring slot
+    int iss_j = 0, iss_st = 0, iss_slot = 0;
 
     // gate/up: the sorted-slot values of tile j into s_rows[buf] (two dword
     // DMAs by wave 0; lanes past the tile's rows read its first slot)
 #define MOE_PIPE_ROWS(j, buf)                                                                   \
     do {                                                                                        \
         if (GATEUP && wave == 0 && (j) < ntiles) {                                              \
-            const Tile d_ = pipe_tile(P, s_prefix, s_cnt, s_off, (j) * G + slot);                             \
+            const Tile d_ = pipe_tile(P, s_prefix, s_cnt, s_off, (j) * G + slot);               \
             _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_) {                                  \
                 const int r_ = 64 * h_ + lane;                                                  \
                 lds_dma4(P.sorted_slots + d_.p0 + (r_ < d_.rows ? r_ : 0),                      \
@@ -188,56 +259,69 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
     // sources of tile j for this lane's DMAs
 #define MOE_PIPE_ENTER(j)                                                                       \
     do {                                                                                        \
-        const Tile d_ = pipe_tile(P, s_prefix, s_cnt, s_off, (j) * G + slot);                                 \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                      \
-            const int u_ = (wave * 4 + i_) * 64 + lane;                                         \
+        const Tile d_ = pipe_tile(P, s_prefix, s_cnt, s_off, (j) * G + slot);                   \
+        _Pragma("unroll") for (int i_ = 0; i_ < kADma; ++i_) {                                  \
+            const int u_ = (wave * kADma + i_) * 64 + lane;                                     \
             const int row_ = min(u_ >> 3, d_.rows - 1);   /* past the tile: repeat its last row */ \
-            const int64_t src_row_ = GATEUP ? (int64_t)(s_rows[(j) & 1][row_] / P.topk) : (int64_t)(d_.p0 + row_); \
-            a_off[i_] = src_row_ * P.K * 2;                                                     \
+            a_row[i_] = GATEUP ? s_rows[(j) & 1][row_] / P.topk : d_.p0 + row_;                 \
         }                                                                                       \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                      \
-            const int u_ = (wave * 4 + i_) * 64 + lane;                                         \
+        {                                                                                       \
+            const int u_ = wave * kBDma * 64 + lane;                                            \
             const int col_ = u_ >> 1, chunk_ = (u_ & 1) ^ ((col_ >> 3) & 1);                    \
             const uint8_t* cb_ = GATEUP ? (col_ < kBN / 2 ? P.c0 : P.c1) : P.c0;                \
             const int64_t n_ = (int64_t)d_.e * P.N +                                            \
                                (GATEUP ? d_.nt * (kBN / 2) + (col_ & (kBN / 2 - 1)) : d_.nt * kBN + col_); \
-            b_src[i_] = cb_ + n_ * (P.K / 2) + 16 * chunk_;                                     \
+            b_src = cb_ + n_ * (P.K / 2) + 16 * chunk_;                                         \
         }                                                                                       \
-        _Pragma("unroll") for (int i_ = 0; i_ < 2; ++i_) {                                      \
-            const int col_ = (wave * 2 + i_) * 64 + lane;                                       \
+        {                                                                                       \
+            const int col_ = wave * kSDma * 64 + lane;                                          \
             const uint8_t* sb_ = GATEUP ? (col_ < kBN / 2 ? P.s0 : P.s1) : P.s0;                \
             const int64_t n_ = (int64_t)d_.e * P.N +                                            \
                                (GATEUP ? d_.nt * (kBN / 2) + (col_ & (kBN / 2 - 1)) : d_.nt * kBN + col_); \
-            s_src[i_] = sb_ + n_ * (P.K / 16);                                                  \
+            s_src = sb_ + n_ * (P.K / 16);                                                      \
         }                                                                                       \
-        pf_tile = (j);                                                                          \
     } while (0)
 
-    // the loads of step g (tile g / nst, stage g % nst) into its ring slot
-#define MOE_PIPE_ISSUE(g)                                                                       \
+    // the loads of the next (tile, stage) into its ring slot, by the DMA
+    // waves: BEGIN sets up a new tile's sources, OP(p) issues op p (0 .. 3:
+    // activation runs, 4 .. 7: code runs, 8, 9: scale runs), END moves on
+#define MOE_PIPE_BEGIN()                                                                        \
     do {                                                                                        \
-        const int j_ = (int)((g) / nst), st_ = (int)((g) - (int64_t)j_ * nst);                  \
-        if (j_ != pf_tile) {                                                                    \
+        if (iss_st == 0) {                                                                      \
             if (GATEUP && nst <= kAhead) {  /* short K: the row table may still be in flight */ \
                 wait_all_memory();                                                              \
                 __builtin_amdgcn_s_barrier();                                                   \
             }                                                                                   \
-            MOE_PIPE_ENTER(j_);                                                                 \
-            MOE_PIPE_ROWS(j_ + 1, (j_ + 1) & 1);                                                \
+            MOE_PIPE_ENTER(iss_j);                                                              \
+            MOE_PIPE_ROWS(iss_j + 1, (iss_j + 1) & 1);                                          \
         }                                                                                       \
-        uint8_t* base_ = ring + (int)((g) % kStages) * kStageBytes;                             \
-        const int k0_ = st_ * kBK;                                                              \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                      \
-            const int u_ = (wave * 4 + i_) * 64 + lane;                                         \
-            const int row_ = u_ >> 3, c_ = (u_ & 7) ^ (row_ & 7);                               \
-            const uint8_t* src_ = reinterpret_cast<const uint8_t*>(P.a) + a_off[i_] + k0_ * 2 + 16 * c_; \
-            lds_dma16(src_, (lds_void*)(base_ + (wave * 4 + i_) * 1024));                        \
-        }                                                                                       \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                        \
-            lds_dma16(b_src[i_] + k0_ / 2, (lds_void*)(base_ + kABytes + (wave * 4 + i_) * 1024)); \
-        _Pragma("unroll") for (int i_ = 0; i_ < 2; ++i_)                                        \
-            lds_dma4(s_src[i_] + k0_ / 16, (lds_void*)(base_ + kABytes + kBBytes + (wave * 2 + i_) * 256)); \
     } while (0)
+#define MOE_PIPE_OP(p)                                                                          \
+    do {                                                                                        \
+        uint8_t* base_ = ring + iss_slot * kStageBytes;                                         \
+        const int k0_ = iss_st * kBK;                                                           \
+        if ((p) < kADma) {                                                                      \
+            const int i_ = (p), u_ = (wave * kADma + i_) * 64 + lane;                           \
+            lds_dma16(reinterpret_cast<const uint8_t*>(P.a) + (int64_t)a_row[i_] * (P.K * 2) +   \
+                          (k0_ * 2 + 16 * ((u_ & 7) ^ ((u_ >> 3) & 7))),                        \
+                      (lds_void*)(base_ + (wave * kADma + i_) * 1024));                         \
+        } else if ((p) < kADma + kBDma) {                                                       \
+            const int i_ = (p) - kADma;                                                         \
+            lds_dma16(b_src + (i_ * b_step + k0_ / 2), (lds_void*)(base_ + kABytes + (wave * kBDma + i_) * 1024)); \
+        } else {                                                                                \
+            const int i_ = (p) - kADma - kBDma;                                                 \
+            lds_dma4(s_src + (i_ * s_step + k0_ / 16), (lds_void*)(base_ + kABytes + kBBytes + (wave * kSDma + i_) * 256)); \
+        }                                                                                       \
+    } while (0)
+#define MOE_PIPE_END()                                                                          \
+    do {                                                                                        \
+        iss_slot = (iss_slot + 1) & (kStages - 1);                                              \
+        if (++iss_st == nst) {                                                                  \
+            iss_st = 0;                                                                         \
+            ++iss_j;                                                                            \
+        }                                                                                       \
+    } while (0)
+    static_assert((kStages & (kStages - 1)) == 0, "ring slots wrap with a mask");
 
     // prologue: row tables of the first two tiles, then the first stages
     if (GATEUP) {
@@ -246,16 +330,23 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
         wait_all_memory();
         __syncthreads();
     }
-    for (int64_t g = 0; g < (nsteps < kAhead ? nsteps : (int64_t)kAhead); ++g) MOE_PIPE_ISSUE(g);
+    if (dma_wave)
+        for (int g = 0; g < (nsteps < kAhead ? nsteps : kAhead); ++g) {
+            MOE_PIPE_BEGIN();
+#pragma unroll
+            for (int p = 0; p < kOpsPerStage; ++p) MOE_PIPE_OP(p);
+            MOE_PIPE_END();
+        }
 
     // columns of this wave's subtiles within the tile's kBN: gate/up waves
-    // own kBN / 8 gate and the same kBN / 8 up columns (SwiGLU pairs them)
+    // own kBN / 16 gate and the same kBN / 16 up columns (SwiGLU pairs them)
     int colb[kNS];
 #pragma unroll
     for (int ns = 0; ns < kNS; ++ns)
-        colb[ns] = GATEUP ? (ns < kNS / 2 ? (kBN / 8) * wave + 16 * ns : kBN / 2 + (kBN / 8) * wave + 16 * (ns - kNS / 2))
-                          : (kBN / 4) * wave + 16 * ns;
+        colb[ns] = GATEUP ? (ns < kNS / 2 ? 32 * wave + 16 * ns : kBN / 2 + 32 * wave + 16 * (ns - kNS / 2))
+                          : 64 * wave + 16 * ns;
 
+    int g = 0;            // (tile, stage) step being computed
 #pragma unroll 1
     for (int j = 0; j < ntiles; ++j) {
         const Tile cur = pipe_tile(P, s_prefix, s_cnt, s_off, j * G + slot);
@@ -265,52 +356,26 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
 #pragma unroll
             for (int n = 0; n < kNS; ++n) acc[i][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-        for (int st = 0; st < nst; ++st) {
-            const int64_t g = (int64_t)j * nst + st;
+        for (int st = 0; st < nst; ++st, ++g) {
             {
-                const int64_t after = nsteps - 1 - g;
-                stage_barrier(after < kAhead - 1 ? (int)after : kAhead - 1);
+                const int after = nsteps - 1 - g;
+                stage_barrier(dma_wave, after < kAhead - 1 ? after : kAhead - 1);
             }
-            if (g + kAhead < nsteps) MOE_PIPE_ISSUE(g + kAhead);
-
-            const uint8_t* base = ring + (int)(g % kStages) * kStageBytes;
-            const uint8_t* Bs = base + kABytes;
-            const uint8_t* Ss = Bs + kBBytes;
-            uint2 cw[kNS];
-            float sc[kNS];
-#pragma unroll
-            for (int ns = 0; ns < kNS; ++ns) {
-                const int col = colb[ns] + lcol;
-                cw[ns] = *reinterpret_cast<const uint2*>(Bs + col * 32 + 16 * ((kq >> 1) ^ ((col >> 3) & 1)) + 8 * (kq & 1));
-                sc[ns] = e4m3_to_f32(Ss[col * 4 + kq]);
-            }
-            // the stage's activation fragments, both k-steps, up front
-            bf16x8 af[2][8];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int ms = 0; ms < 8; ++ms) {
-                    const int row = ms * 16 + lcol;
-                    af[ks][ms] = *reinterpret_cast<const bf16x8*>(base + row * 128 + 16 * ((2 * kq + ks) ^ (row & 7)));
+            // a DMA wave spreads stage g + kAhead's loads over this stage's MFMAs
+            const bool issuing = dma_wave && g + kAhead < nsteps;
+            if (issuing) MOE_PIPE_BEGIN();
+            const uint8_t* base = ring + (g & (kStages - 1)) * kStageBytes;
+            stage_mfma(acc, base, colb, lcol, kq, [&](int p) {
+                if (issuing) {
+                    if (p < 6) {
+                        MOE_PIPE_OP(p);
+                    } else {           // 6: codes 2 + scales 0, 7: codes 3 + scales 1
+                        MOE_PIPE_OP(p);
+                        MOE_PIPE_OP(p + 2);
+                    }
                 }
-            // column by column: the decode of the next column overlaps the
-            // MFMAs of this one
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int ns = 0; ns < kNS; ++ns) {
-                    const bf16x8 bf = decode8s(ks ? cw[ns].y : cw[ns].x, sc[ns]);
-#pragma unroll
-                    for (int ms = 0; ms < 8; ++ms)
-                        acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][ms], bf, acc[ms][ns], 0, 0, 0);
-                }
-            // issue order: each MFMA followed by two VALU instructions (the
-            // next column's decode), so the matrix pipe never waits for it
-#pragma unroll
-            for (int i = 0; i < 2 * kNS * 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU
-            }
+            });
+            if (issuing) MOE_PIPE_END();
         }
 
         // epilogue: lane holds rows 4 kq + i (i < 4) of each 16-row subtile, column lcol
@@ -327,7 +392,7 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
                         for (int ns = 0; ns < kNS / 2; ++ns) {
                             const float av = gg * acc[ms][ns][i];
                             const float bv = gu * acc[ms][ns + kNS / 2][i];
-                            const int col = cur.nt * (kBN / 2) + (kBN / 8) * wave + 16 * ns + lcol;
+                            const int col = cur.nt * (kBN / 2) + 32 * wave + 16 * ns + lcol;
                             h[(int64_t)(cur.p0 + r) * P.N + col] = f32_to_bf16_rne(silu(av) * bv);
                         }
                     }
@@ -343,7 +408,7 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
                     if (r < cur.rows) {
 #pragma unroll
                         for (int ns = 0; ns < kNS; ++ns) {
-                            const int col = cur.nt * kBN + (kBN / 4) * wave + 16 * ns + lcol;
+                            const int col = cur.nt * kBN + 64 * wave + 16 * ns + lcol;
                             y[(int64_t)(cur.p0 + r) * P.N + col] = gd * acc[ms][ns][i];
                         }
                     }
@@ -352,7 +417,9 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
     }
 #undef MOE_PIPE_ROWS
 #undef MOE_PIPE_ENTER
-#undef MOE_PIPE_ISSUE
+#undef MOE_PIPE_BEGIN
+#undef MOE_PIPE_OP
+#undef MOE_PIPE_END
 }
 
 int cu_count_pipe() {
