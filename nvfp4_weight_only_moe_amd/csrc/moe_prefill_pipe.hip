@@ -18,8 +18,8 @@
 //     rows (128 accumulator registers), so the decode of one wave's codes
 //     and its LDS reads overlap the other wave's MFMAs;
 //   * LDS layouts are XOR-swizzled in 16-byte units so that the MFMA
-//     fragment reads (8 consecutive lanes, 8 consecutive rows or columns)
-//     hit distinct banks.
+//     fragment reads (consecutive lanes on consecutive rows or columns) hit
+//     distinct banks.
 // The K order inside a stage is permuted identically for both operands:
 // lane group q of an MFMA takes k = 16 q + 8 s .. 16 q + 8 s + 7 at k-step
 // s, so one 8-byte read gives a lane its 16 codes (one E4M3 group) for both
@@ -88,6 +88,13 @@ __device__ __forceinline__ bf16x8 decode8s(uint32_t word, float s) {
     r[3] = __builtin_amdgcn_perm(__float_as_uint(p3[1] * s), __float_as_uint(p3[0] * s), 0x07060302u);
     return __builtin_bit_cast(bf16x8, r);
 }
+
+// LDS slot of 16-byte unit c of activation row r: c ^ a_swz(r).  A
+// fragment read (16-byte lanes, rows r0 .. r0 + 15 of one unit) then hits
+// distinct banks whether the LDS serves 8 or 16 such lanes per cycle: the
+// swizzle differs across any 8 consecutive rows and across the 8 even (or
+// odd) rows of 16.
+__device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // Tile t of the launch: expert, first sorted row, rows, column tile.  Tiles
 // are numbered expert by expert (prefix over experts in s_prefix) and, inside
@@ -158,14 +165,16 @@ __device__ __forceinline__ void stage_mfma(floatx4 (&acc)[8][kNS], const uint8_t
         sc[ns] = e4m3_to_f32(Ss[col * 4 + kq]);
     }
     bf16x8 bnext = decode8s(cw[0].x, sc[0]);
+    // activation fragments: k-step 0 now, k-step 1 in two halves during the
+    // k-step 0 MFMAs (after subtiles 1 and 2), so their LDS latency is hidden
+    bf16x8 af[2][8];
+#pragma unroll
+    for (int ms = 0; ms < 8; ++ms) {
+        const int row = ms * 16 + lcol;
+        af[0][ms] = *reinterpret_cast<const bf16x8*>(base + row * 128 + 16 * ((2 * kq) ^ a_swz(row)));
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 af[8];
-#pragma unroll
-        for (int ms = 0; ms < 8; ++ms) {
-            const int row = ms * 16 + lcol;
-            af[ms] = *reinterpret_cast<const bf16x8*>(base + row * 128 + 16 * ((2 * kq + ks) ^ (row & 7)));
-        }
 #pragma unroll
         for (int ns = 0; ns < kNS; ++ns) {
             const bf16x8 bf = bnext;
@@ -173,7 +182,7 @@ __device__ __forceinline__ void stage_mfma(floatx4 (&acc)[8][kNS], const uint8_t
             if (ks == 0 || ns + 1 < kNS) bnext = decode8s((ns + 1 < kNS ? ks : 1) ? cw[nn].y : cw[nn].x, sc[nn]);
 #pragma unroll
             for (int ms = 0; ms < 8; ++ms)
-                acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
+                acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][ms], bf, acc[ms][ns], 0, 0, 0);
             // each MFMA followed by two VALU instructions (the next
             // subtile's decode), so the matrix pipe does not wait for it
 #pragma unroll
@@ -182,6 +191,13 @@ __device__ __forceinline__ void stage_mfma(floatx4 (&acc)[8][kNS], const uint8_t
                 __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU
             }
             dma(ks * kNS + ns);
+            if (ks == 0 && (ns == 1 || ns == 2)) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const int ms = (ns - 1) * 4 + h, row = ms * 16 + lcol;
+                    af[1][ms] = *reinterpret_cast<const bf16x8*>(base + row * 128 + 16 * ((2 * kq + 1) ^ a_swz(row)));
+                }
+            }
         }
     }
 }
@@ -303,7 +319,7 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
         if ((p) < kADma) {                                                                      \
             const int i_ = (p), u_ = (wave * kADma + i_) * 64 + lane;                           \
             lds_dma16(reinterpret_cast<const uint8_t*>(P.a) + (int64_t)a_row[i_] * (P.K * 2) +   \
-                          (k0_ * 2 + 16 * ((u_ & 7) ^ ((u_ >> 3) & 7))),                        \
+                          (k0_ * 2 + 16 * ((u_ & 7) ^ a_swz(u_ >> 3))),                         \
                       (lds_void*)(base_ + (wave * kADma + i_) * 1024));                         \
         } else if ((p) < kADma + kBDma) {                                                       \
             const int i_ = (p) - kADma;                                                         \
@@ -350,6 +366,13 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
 #pragma unroll 1
     for (int j = 0; j < ntiles; ++j) {
         const Tile cur = pipe_tile(P, s_prefix, s_cnt, s_off, j * G + slot);
+        // the expert's global scales, by scalar loads: a vector load would be
+        // ordered behind the DMA operations in flight, and one still counted
+        // as pending across the stage loop makes the compiler wait for all
+        // of them inside it
+        const int e_cur = __builtin_amdgcn_readfirstlane(cur.e);
+        const float g_a = ((const __attribute__((address_space(4))) float*)P.g0)[e_cur];
+        const float g_b = GATEUP ? ((const __attribute__((address_space(4))) float*)P.g1)[e_cur] : 0.0f;
         floatx4 acc[8][kNS];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -380,7 +403,7 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
 
         // epilogue: lane holds rows 4 kq + i (i < 4) of each 16-row subtile, column lcol
         if (GATEUP) {
-            const float gg = P.g0[cur.e], gu = P.g1[cur.e];
+            const float gg = g_a, gu = g_b;
             uint16_t* h = reinterpret_cast<uint16_t*>(P.out);
 #pragma unroll
             for (int ms = 0; ms < 8; ++ms)
@@ -398,7 +421,7 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
                     }
                 }
         } else {
-            const float gd = P.g0[cur.e];
+            const float gd = g_a;
             float* y = reinterpret_cast<float*>(P.out);
 #pragma unroll
             for (int ms = 0; ms < 8; ++ms)
