@@ -130,7 +130,7 @@ int g_prefill_variant = 2;
 constexpr int64_t kPipeMinRowsPerExpert = 256;
 
 moe_status launch_prefill(const FwdArgs& a, hipStream_t stream) {
-    const bool pipe_ok = prefill_pipe_supported(a.H, a.I);
+    const bool pipe_ok = prefill_pipe_supported(a.T, a.k, a.H, a.I);
     const int64_t slots = (int64_t)a.T * a.k;
     const int64_t per_expert = slots / std::max<int64_t>(1, std::min<int64_t>(a.E, slots));
     const bool pipe =

@@ -113,6 +113,17 @@ __device__ __forceinline__ void lds_dma4(const void* gsrc, lds_void* ldst) {
                  : "memory");
 }
 
+// The same with a wave-uniform 64-bit base (SGPR pair) and a 32-bit per-lane
+// byte offset: the base can move on by scalar arithmetic alone.
+__device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, lds_void* ldst) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                 "{m0}"((uint32_t)(uintptr_t)ldst) : "memory");
+}
+__device__ __forceinline__ void lds_dma4_sv(const void* sbase, uint32_t voff, lds_void* ldst) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
+                 "{m0}"((uint32_t)(uintptr_t)ldst) : "memory");
+}
+
 // Wait for every outstanding memory operation of this wave.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 

@@ -84,7 +84,7 @@ moe_status launch_gateup_grouped(const FwdArgs& a, hipStream_t s);
 moe_status launch_down_grouped(const FwdArgs& a, hipStream_t s);
 moe_status launch_combine(const FwdArgs& a, hipStream_t s);
 // moe_prefill_pipe.hip: LDS-pipelined grouped GEMMs
-bool prefill_pipe_supported(int H, int I);
+bool prefill_pipe_supported(int64_t T, int k, int H, int I);
 moe_status launch_gateup_pipe(const FwdArgs& a, hipStream_t s);
 moe_status launch_down_pipe(const FwdArgs& a, hipStream_t s);
 

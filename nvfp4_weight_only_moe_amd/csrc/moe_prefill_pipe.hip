@@ -42,6 +42,11 @@ constexpr int kABytes = kBM * kBK * 2;          // 16 KiB activations
 constexpr int kBBytes = kBN * kBK / 2;          // 16 KiB codes
 constexpr int kSBytes = kBN * kBK / 16;         // 2 KiB scales
 constexpr int kStageBytes = kABytes + kBBytes + kSBytes;
+// the ring is three rings, one per operand, so that every LDS read of a
+// stage is a per-stage base plus an immediate offset (all below 64 KiB)
+constexpr int kARing = 0;
+constexpr int kBRing = kStages * kABytes;
+constexpr int kSRing = kBRing + kStages * kBBytes;
 constexpr int kMGroup = 8;                      // row tiles per scheduling group
 // Waves 0 .. kDmaWaves - 1 (one per SIMD) issue a stage's LDS-DMA
 // operations: 1 KiB activation and code runs, 256-byte scale runs.  The
@@ -151,28 +156,32 @@ static_assert(kAhead == 3, "stage_barrier covers up to two stages after the awai
 // stay in place.  dma(p), p = 0 .. 7, runs after the p-th subtile's MFMAs:
 // a DMA wave issues part of a later stage's loads there, so a stall on a
 // full load queue overlaps the MFMAs already issued and the other wave's.
-template <class Dma>
-__device__ __forceinline__ void stage_mfma(floatx4 (&acc)[8][kNS], const uint8_t* base, const int (&colb)[kNS],
-                                           int lcol, int kq, Dma&& dma) {
-    const uint8_t* Bs = base + kABytes;
-    const uint8_t* Ss = Bs + kBBytes;
+// Lane offsets inside a stage's rings: activation fragment (k-step ks) of
+// row lcol (16-row subtile ms adds ms * 2048), codes and scale of column
+// lcol of the wave's first subtile (subtile ns adds cb[ns] columns).
+struct LaneLds {
+    int a[2], b, s;
+};
+
+template <bool GATEUP, class Dma>
+__device__ __forceinline__ void stage_mfma(floatx4 (&acc)[8][kNS], const uint8_t* as, const uint8_t* bs,
+                                           const uint8_t* ss, const LaneLds& o, Dma&& dma) {
+    // columns of the wave's subtiles relative to its first: gate/up waves
+    // own 32 gate columns and the same 32 up columns (SwiGLU pairs them)
+    constexpr int cb[kNS] = {0, 16, GATEUP ? kBN / 2 : 32, GATEUP ? kBN / 2 + 16 : 48};
     uint2 cw[kNS];
     float sc[kNS];
 #pragma unroll
     for (int ns = 0; ns < kNS; ++ns) {
-        const int col = colb[ns] + lcol;
-        cw[ns] = *reinterpret_cast<const uint2*>(Bs + col * 32 + 16 * ((kq >> 1) ^ ((col >> 3) & 1)) + 8 * (kq & 1));
-        sc[ns] = e4m3_to_f32(Ss[col * 4 + kq]);
+        cw[ns] = *reinterpret_cast<const uint2*>(bs + o.b + cb[ns] * 32);
+        sc[ns] = e4m3_to_f32(ss[o.s + cb[ns] * 4]);
     }
     bf16x8 bnext = decode8s(cw[0].x, sc[0]);
     // activation fragments: k-step 0 now, k-step 1 in two halves during the
     // k-step 0 MFMAs (after subtiles 1 and 2), so their LDS latency is hidden
     bf16x8 af[2][8];
 #pragma unroll
-    for (int ms = 0; ms < 8; ++ms) {
-        const int row = ms * 16 + lcol;
-        af[0][ms] = *reinterpret_cast<const bf16x8*>(base + row * 128 + 16 * ((2 * kq) ^ a_swz(row)));
-    }
+    for (int ms = 0; ms < 8; ++ms) af[0][ms] = *reinterpret_cast<const bf16x8*>(as + o.a[0] + ms * 2048);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -194,8 +203,8 @@ __device__ __forceinline__ void stage_mfma(floatx4 (&acc)[8][kNS], const uint8_t
             if (ks == 0 && (ns == 1 || ns == 2)) {
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
-                    const int ms = (ns - 1) * 4 + h, row = ms * 16 + lcol;
-                    af[1][ms] = *reinterpret_cast<const bf16x8*>(base + row * 128 + 16 * ((2 * kq + 1) ^ a_swz(row)));
+                    const int ms = (ns - 1) * 4 + h;
+                    af[1][ms] = *reinterpret_cast<const bf16x8*>(as + o.a[1] + ms * 2048);
                 }
             }
         }
@@ -204,7 +213,7 @@ __device__ __forceinline__ void stage_mfma(floatx4 (&acc)[8][kNS], const uint8_t
 
 template <bool GATEUP>
 __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
-    extern __shared__ __align__(16) uint8_t ring[];          // kStages x kStageBytes
+    extern __shared__ __align__(16) uint8_t ring[];          // activation, code and scale rings
     __shared__ int s_prefix[MOE_MAX_EXPERTS + 1];
     __shared__ int s_cnt[MOE_MAX_EXPERTS], s_off[MOE_MAX_EXPERTS];   // per expert: rows, first sorted row
     __shared__ __align__(16) int32_t s_rows[2][128];          // sorted-slot values of two tiles (gate/up)
@@ -248,12 +257,14 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
     const int nst = P.K / kBK;
     const int nsteps = ntiles * nst;
 
-    // per-lane sources of the tile being prefetched: activation rows; the
-    // lane's first code and scale runs (its later runs are 32 and 64
-    // columns further on, in the same matrix)
-    int a_row[kADma];
-    const uint8_t* b_src;
-    const uint8_t* s_src;
+    // DMA sources of the tile being prefetched: per-lane byte offsets of the
+    // activation runs (row and 16-byte unit), and the wave-uniform bases of
+    // its code and scale runs (their per-lane offsets never change)
+    uint32_t a_vo[kADma];
+    const uint8_t* b_base = nullptr;
+    const uint8_t* s_base = nullptr;
+    const uint32_t b_vo = (uint32_t)((lane >> 1) * (P.K / 2) + 16 * ((lane & 1) ^ ((lane >> 4) & 1)));
+    const uint32_t s_vo = (uint32_t)(lane * (P.K / 16));
     const int64_t b_step = (int64_t)32 * (P.K / 2), s_step = (int64_t)64 * (P.K / 16);
     // next (tile, stage) to prefetch and its ring slot
     int iss_j = 0, iss_st = 0, iss_slot = 0;
@@ -272,30 +283,22 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
         }                                                                                       \
     } while (0)
 
-    // sources of tile j for this lane's DMAs
+    // sources of tile j for this wave's DMAs (DMA waves)
 #define MOE_PIPE_ENTER(j)                                                                       \
     do {                                                                                        \
         const Tile d_ = pipe_tile(P, s_prefix, s_cnt, s_off, (j) * G + slot);                   \
+        const int e_ = __builtin_amdgcn_readfirstlane(d_.e), nt_ = __builtin_amdgcn_readfirstlane(d_.nt); \
+        const int rows_ = __builtin_amdgcn_readfirstlane(d_.rows), p0_ = __builtin_amdgcn_readfirstlane(d_.p0); \
         _Pragma("unroll") for (int i_ = 0; i_ < kADma; ++i_) {                                  \
             const int u_ = (wave * kADma + i_) * 64 + lane;                                     \
-            const int row_ = min(u_ >> 3, d_.rows - 1);   /* past the tile: repeat its last row */ \
-            a_row[i_] = GATEUP ? s_rows[(j) & 1][row_] / P.topk : d_.p0 + row_;                 \
+            const int row_ = min(u_ >> 3, rows_ - 1);   /* past the tile: repeat its last row */ \
+            const int src_ = GATEUP ? s_rows[(j) & 1][row_] / P.topk : p0_ + row_;              \
+            a_vo[i_] = (uint32_t)src_ * (uint32_t)(P.K * 2) + 16u * (uint32_t)((u_ & 7) ^ a_swz(u_ >> 3)); \
         }                                                                                       \
-        {                                                                                       \
-            const int u_ = wave * kBDma * 64 + lane;                                            \
-            const int col_ = u_ >> 1, chunk_ = (u_ & 1) ^ ((col_ >> 3) & 1);                    \
-            const uint8_t* cb_ = GATEUP ? (col_ < kBN / 2 ? P.c0 : P.c1) : P.c0;                \
-            const int64_t n_ = (int64_t)d_.e * P.N +                                            \
-                               (GATEUP ? d_.nt * (kBN / 2) + (col_ & (kBN / 2 - 1)) : d_.nt * kBN + col_); \
-            b_src = cb_ + n_ * (P.K / 2) + 16 * chunk_;                                         \
-        }                                                                                       \
-        {                                                                                       \
-            const int col_ = wave * kSDma * 64 + lane;                                          \
-            const uint8_t* sb_ = GATEUP ? (col_ < kBN / 2 ? P.s0 : P.s1) : P.s0;                \
-            const int64_t n_ = (int64_t)d_.e * P.N +                                            \
-                               (GATEUP ? d_.nt * (kBN / 2) + (col_ & (kBN / 2 - 1)) : d_.nt * kBN + col_); \
-            s_src = sb_ + n_ * (P.K / 16);                                                      \
-        }                                                                                       \
+        /* first column of the wave's code / scale runs within the expert's matrix */         \
+        const int64_t n0_ = (int64_t)e_ * P.N + (GATEUP ? nt_ * (kBN / 2) + (wave & 1) * 128 : nt_ * kBN + wave * 128); \
+        b_base = (GATEUP && wave >= 2 ? P.c1 : P.c0) + n0_ * (P.K / 2);                        \
+        s_base = (GATEUP && wave >= 2 ? P.s1 : P.s0) + n0_ * (P.K / 16);                       \
     } while (0)
 
     // the loads of the next (tile, stage) into its ring slot, by the DMA
@@ -314,19 +317,19 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
     } while (0)
 #define MOE_PIPE_OP(p)                                                                          \
     do {                                                                                        \
-        uint8_t* base_ = ring + iss_slot * kStageBytes;                                         \
         const int k0_ = iss_st * kBK;                                                           \
         if ((p) < kADma) {                                                                      \
-            const int i_ = (p), u_ = (wave * kADma + i_) * 64 + lane;                           \
-            lds_dma16(reinterpret_cast<const uint8_t*>(P.a) + (int64_t)a_row[i_] * (P.K * 2) +   \
-                          (k0_ * 2 + 16 * ((u_ & 7) ^ a_swz(u_ >> 3))),                         \
-                      (lds_void*)(base_ + (wave * kADma + i_) * 1024));                         \
+            const int i_ = (p);                                                                 \
+            lds_dma16_sv(reinterpret_cast<const uint8_t*>(P.a) + k0_ * 2, a_vo[i_],             \
+                         (lds_void*)(ring + kARing + iss_slot * kABytes + (wave * kADma + i_) * 1024)); \
         } else if ((p) < kADma + kBDma) {                                                       \
             const int i_ = (p) - kADma;                                                         \
-            lds_dma16(b_src + (i_ * b_step + k0_ / 2), (lds_void*)(base_ + kABytes + (wave * kBDma + i_) * 1024)); \
+            lds_dma16_sv(b_base + (i_ * b_step + k0_ / 2), b_vo,                                \
+                         (lds_void*)(ring + kBRing + iss_slot * kBBytes + (wave * kBDma + i_) * 1024)); \
         } else {                                                                                \
             const int i_ = (p) - kADma - kBDma;                                                 \
-            lds_dma4(s_src + (i_ * s_step + k0_ / 16), (lds_void*)(base_ + kABytes + kBBytes + (wave * kSDma + i_) * 256)); \
+            lds_dma4_sv(s_base + (i_ * s_step + k0_ / 16), s_vo,                                \
+                        (lds_void*)(ring + kSRing + iss_slot * kSBytes + (wave * kSDma + i_) * 256)); \
         }                                                                                       \
     } while (0)
 #define MOE_PIPE_END()                                                                          \
@@ -354,13 +357,16 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
             MOE_PIPE_END();
         }
 
-    // columns of this wave's subtiles within the tile's kBN: gate/up waves
-    // own kBN / 16 gate and the same kBN / 16 up columns (SwiGLU pairs them)
-    int colb[kNS];
-#pragma unroll
-    for (int ns = 0; ns < kNS; ++ns)
-        colb[ns] = GATEUP ? (ns < kNS / 2 ? 32 * wave + 16 * ns : kBN / 2 + 32 * wave + 16 * (ns - kNS / 2))
-                          : 64 * wave + 16 * ns;
+    // this lane's LDS offsets inside a stage (see LaneLds); the wave's first
+    // column is 32 w (gate/up: then 32 up columns at kBN / 2 + 32 w) or 64 w
+    LaneLds lo;
+    {
+        const int col = (GATEUP ? 32 : 64) * wave + lcol;
+        lo.a[0] = lcol * 128 + 16 * ((2 * kq) ^ a_swz(lcol));
+        lo.a[1] = lcol * 128 + 16 * ((2 * kq + 1) ^ a_swz(lcol));
+        lo.b = col * 32 + 16 * ((kq >> 1) ^ ((lcol >> 3) & 1)) + 8 * (kq & 1);
+        lo.s = col * 4 + kq;
+    }
 
     int g = 0;            // (tile, stage) step being computed
 #pragma unroll 1
@@ -387,8 +393,9 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
             // a DMA wave spreads stage g + kAhead's loads over this stage's MFMAs
             const bool issuing = dma_wave && g + kAhead < nsteps;
             if (issuing) MOE_PIPE_BEGIN();
-            const uint8_t* base = ring + (g & (kStages - 1)) * kStageBytes;
-            stage_mfma(acc, base, colb, lcol, kq, [&](int p) {
+            const int rs = g & (kStages - 1);
+            stage_mfma<GATEUP>(acc, ring + kARing + rs * kABytes, ring + kBRing + rs * kBBytes,
+                               ring + kSRing + rs * kSBytes, lo, [&](int p) {
                 if (issuing) {
                     if (p < 6) {
                         MOE_PIPE_OP(p);
@@ -467,7 +474,12 @@ moe_status launch_pipe(const PipeParams& P, int64_t slots, hipStream_t s) {
 
 }  // namespace
 
-bool prefill_pipe_supported(int H, int I) { return H % kBN == 0 && I % (kBN / 2) == 0 && I % kBK == 0; }
+// Shapes the kernels tile exactly; the activation DMAs address rows by a
+// 32-bit byte offset from the activation base (x for gate/up, h for down).
+bool prefill_pipe_supported(int64_t T, int k, int H, int I) {
+    return H % kBN == 0 && I % (kBN / 2) == 0 && I % kBK == 0 && T * H * 2 < (int64_t)1 << 32 &&
+           T * k * I * 2 < (int64_t)1 << 32;
+}
 
 moe_status launch_gateup_pipe(const FwdArgs& a, hipStream_t s) {
     PipeParams g{};
