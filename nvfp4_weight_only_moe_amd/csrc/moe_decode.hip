@@ -37,8 +37,12 @@ namespace {
 constexpr int kGuThreads = 256;         // gate/up workgroup
 constexpr int kGuWaves = kGuThreads / kWave;
 constexpr int kDownMaxWaves = 12;
-constexpr int kDownChunkExperts = 8;    // experts whose down codes are in flight together
-constexpr int kDownChunkSlots = 16;     // h rows staged in LDS per chunk
+// A chunk: experts whose down codes are requested in one sequence, and the
+// h rows staged in LDS for them.  One token touches k experts, so one chunk
+// holds them all; with more tokens larger chunks mean fewer restarts of the
+// load sequence (each costs a memory latency).
+template <int MAXT> constexpr int down_chunk_experts() { return MAXT == 1 ? 8 : 16; }
+template <int MAXT> constexpr int down_chunk_slots() { return MAXT == 1 ? 16 : 48; }
 constexpr int kDownAhead = 3;           // experts' down codes in flight ahead of the one computed
 constexpr int kDecodeMaxSlots = 64;     // T * k on the decode path
 constexpr int kXTokens = 2;             // activation rows staged in LDS at a time (gate/up)
@@ -72,7 +76,7 @@ struct GuRoute {
 };
 
 template <int CPL, int RW, int EPL, bool ROUTE>
-__global__ void __launch_bounds__(kGuThreads, 3)
+__global__ void __launch_bounds__(kGuThreads, RW == 1 ? 4 : 3)
 k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slots,
              const uint8_t* gc, const uint8_t* gs, const float* __restrict__ gg,
              const uint8_t* uc, const uint8_t* us, const float* __restrict__ ug,
@@ -269,8 +273,9 @@ __global__ void __launch_bounds__(kDownMaxWaves * kWave)
 k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
            const uint8_t* dc, const uint8_t* ds, const float* __restrict__ dg,
            const float* __restrict__ topk_w, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-           const int32_t* __restrict__ sorted_slots, uint16_t* __restrict__ out) {
-    extern __shared__ uint4 hs[];     // [kDownChunkSlots][I / 8]
+           const int32_t* __restrict__ sorted_slots, uint16_t* __restrict__ out, int slot_cap) {
+    constexpr int kDownChunkExperts = down_chunk_experts<MAXT>();
+    extern __shared__ uint4 hs[];     // [slot_cap][I / 8]
     __shared__ int s_cnt[MOE_MAX_EXPERTS], s_off[MOE_MAX_EXPERTS];
     __shared__ int s_list[MOE_MAX_EXPERTS];
     __shared__ float s_g[MOE_MAX_EXPERTS];
@@ -322,11 +327,11 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
 
     int u0 = 0;
     while (u0 < U) {
-        // chunk [u0, u1): at most kDownChunkExperts experts and kDownChunkSlots h rows
+        // chunk [u0, u1): at most kDownChunkExperts experts and slot_cap h rows
         const int pA = s_off[s_list[u0]];
         int u1 = u0 + 1;
         while (u1 < U && u1 - u0 < kDownChunkExperts &&
-               s_off[s_list[u1]] + s_cnt[s_list[u1]] - pA <= kDownChunkSlots)
+               s_off[s_list[u1]] + s_cnt[s_list[u1]] - pA <= slot_cap)
             ++u1;
         const int pB = s_off[s_list[u1 - 1]] + s_cnt[s_list[u1 - 1]];
 
@@ -394,14 +399,18 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
     }
 }
 
-constexpr int kGuRowsPerWave = 2;      // stages of two features per gate/up wave
-
-template <int CPL, int EPL, bool ROUTE>
+// Stages of two features per gate/up wave.  One token: two stages, so the
+// 768 workgroups of a 1536-feature, 8-expert layer are all resident at once
+// (143 VGPRs, 3 waves per SIMD).  More tokens: one stage; the grid is then
+// larger than one resident round anyway (a column per slot, most of them
+// empty after the lookup), and smaller workgroups start streaming sooner
+// (measured on MI355X at 8 tokens, 35 experts: 70 us against 75).
+template <int CPL, int RW, int EPL, bool ROUTE>
 moe_status launch_gateup_epl(const FwdArgs& a, const GuRoute& R, hipStream_t s) {
-    const int rows_per_block = kGuWaves * 2 * kGuRowsPerWave;
+    const int rows_per_block = kGuWaves * 2 * RW;
     const dim3 grid((a.I + rows_per_block - 1) / rows_per_block, std::min(a.T * a.k, a.E));
     const size_t shmem = (size_t)std::min(a.T, kXTokens) * a.H * sizeof(uint16_t);
-    auto kern = k_dec_gateup<CPL, kGuRowsPerWave, EPL, ROUTE>;
+    auto kern = k_dec_gateup<CPL, RW, EPL, ROUTE>;
     if (allow_dynamic_lds(reinterpret_cast<const void*>(kern), shmem) != MOE_OK) return MOE_ERR_HIP;
     MOE_LAUNCH(ROUTE ? "dec_gateup_route" : "dec_gateup", kern, grid, dim3(kGuThreads), shmem, s, a.x, a.H, a.I,
                a.E, a.k, a.T * a.k, (const uint8_t*)a.gate->codes, (const uint8_t*)a.gate->scales,
@@ -410,34 +419,47 @@ moe_status launch_gateup_epl(const FwdArgs& a, const GuRoute& R, hipStream_t s) 
     return MOE_OK;
 }
 
+template <int CPL, int RW>
+moe_status launch_gateup_rw(const FwdArgs& a, const GuRoute* R, hipStream_t s) {
+    if (R) return a.E <= 256 ? launch_gateup_epl<CPL, RW, 4, true>(a, *R, s) : launch_gateup_epl<CPL, RW, 16, true>(a, *R, s);
+    const GuRoute none{};
+    return a.E <= 256 ? launch_gateup_epl<CPL, RW, 4, false>(a, none, s)
+                      : launch_gateup_epl<CPL, RW, 16, false>(a, none, s);
+}
+
 template <int CPL>
 moe_status launch_gateup_gpl(const FwdArgs& a, const GuRoute* R, hipStream_t s) {
-    if (R) return a.E <= 256 ? launch_gateup_epl<CPL, 4, true>(a, *R, s) : launch_gateup_epl<CPL, 16, true>(a, *R, s);
-    const GuRoute none{};
-    return a.E <= 256 ? launch_gateup_epl<CPL, 4, false>(a, none, s) : launch_gateup_epl<CPL, 16, false>(a, none, s);
+    if (a.T == 1) return launch_gateup_rw<CPL, 2>(a, R, s);
+    const GuRoute none{};     // the in-kernel route is for one token only
+    return a.E <= 256 ? launch_gateup_epl<CPL, 1, 4, false>(a, none, s) : launch_gateup_epl<CPL, 1, 16, false>(a, none, s);
 }
 
 int down_waves_per_block(int H) {
     int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
         cus = 256;
     // one workgroup per CU when the rows divide evenly: 2 rows per wave
     int w = (H + 2 * cus - 1) / (2 * cus);
     return std::max(1, std::min(w, kDownMaxWaves));
 }
 
+// h rows staged per chunk: the chunk size, at most T * k, within a 128 KiB
+// LDS budget (an expert's rows, at most T <= 8, always fit: I <= 2048)
+constexpr int kDownLdsBudget = 128 * 1024;
+
 template <int GPL2, int MAXT>
 moe_status launch_down_t(const FwdArgs& a, hipStream_t s) {
-    static int waves = 0;
-    if (!waves) waves = down_waves_per_block(a.H);
+    const int waves = down_waves_per_block(a.H);
     const int rows_per_block = 2 * waves;
-    const size_t shmem = (size_t)kDownChunkSlots * a.I * sizeof(uint16_t);
+    const int slot_cap = std::min({down_chunk_slots<MAXT>(), a.T * a.k, kDownLdsBudget / (a.I * 2)});
+    const size_t shmem = (size_t)slot_cap * a.I * sizeof(uint16_t);
     if (allow_dynamic_lds(reinterpret_cast<const void*>(&k_dec_down<GPL2, MAXT>), shmem) != MOE_OK)
         return MOE_ERR_HIP;
     MOE_LAUNCH("dec_down", (k_dec_down<GPL2, MAXT>), dim3((a.H + rows_per_block - 1) / rows_per_block),
                dim3(waves * kWave), shmem, s, (const uint16_t*)a.h, a.T, a.H, a.I, a.E, a.k,
                (const uint8_t*)a.down->codes, (const uint8_t*)a.down->scales, (const float*)a.down->global_scale,
-               a.topk_w, a.counts, a.offsets, a.sorted_slots, a.out);
+               a.topk_w, a.counts, a.offsets, a.sorted_slots, a.out, slot_cap);
     return MOE_OK;
 }
 
