@@ -48,16 +48,27 @@ constexpr int kARing = 0;
 constexpr int kBRing = kStages * kABytes;
 constexpr int kSRing = kBRing + kStages * kBBytes;
 constexpr int kMGroup = 8;                      // row tiles per scheduling group
-// Waves 0 .. kDmaWaves - 1 (one per SIMD) issue a stage's LDS-DMA
-// operations: 1 KiB activation and code runs, 256-byte scale runs.  The
-// other wave of each SIMD goes straight from the stage barrier to its MFMAs
-// while its partner issues.
-constexpr int kDmaWaves = 4;
+#ifndef MOE_PIPE_DMA_WAVES
+#define MOE_PIPE_DMA_WAVES 4
+#endif
+// Waves 0 .. kDmaWaves - 1 issue a stage's LDS-DMA operations: 1 KiB
+// activation and code runs, 256-byte scale runs.  With 4 (one per SIMD, the
+// default) the other wave of each SIMD goes on with its MFMAs while its
+// partner issues; all 8 issuing measured 6 % slower on MI355X.
+constexpr int kDmaWaves = MOE_PIPE_DMA_WAVES;
 constexpr int kADma = kABytes / 1024 / kDmaWaves;
 constexpr int kBDma = kBBytes / 1024 / kDmaWaves;
 constexpr int kSDma = kSBytes / 256 / kDmaWaves;
 constexpr int kOpsPerStage = kADma + kBDma + kSDma;
-static_assert(kADma == 4 && kBDma == 4 && kSDma == 2 && kNS == 4, "stage split over the waves");
+constexpr int kDmaCols = kBN / kDmaWaves;       // weight columns one DMA wave brings in
+static_assert(kADma * kDmaWaves * 1024 == kABytes && kBDma * 32 == kDmaCols && kSDma * 64 == kDmaCols && kNS == 4,
+              "stage split over the waves");
+// point (0 .. 7: after which subtile's MFMAs) at which a DMA wave issues
+// op j of a stage; with 8 DMA waves the second wave of each SIMD is offset
+// so that the two do not stall on the load queue together
+__device__ __forceinline__ constexpr int dma_point(int j, int wave) {
+    return kDmaWaves == 4 ? (j < 6 ? j : (j < 8 ? j : j - 2)) : j + (wave >= 4 ? 3 : 0);
+}
 
 struct PipeParams {
     const uint16_t* a;          // gate/up: x [T][K]; down: h [T*k][K]
@@ -296,9 +307,10 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
             a_vo[i_] = (uint32_t)src_ * (uint32_t)(P.K * 2) + 16u * (uint32_t)((u_ & 7) ^ a_swz(u_ >> 3)); \
         }                                                                                       \
         /* first column of the wave's code / scale runs within the expert's matrix */         \
-        const int64_t n0_ = (int64_t)e_ * P.N + (GATEUP ? nt_ * (kBN / 2) + (wave & 1) * 128 : nt_ * kBN + wave * 128); \
-        b_base = (GATEUP && wave >= 2 ? P.c1 : P.c0) + n0_ * (P.K / 2);                        \
-        s_base = (GATEUP && wave >= 2 ? P.s1 : P.s0) + n0_ * (P.K / 16);                       \
+        const int64_t n0_ = (int64_t)e_ * P.N + (GATEUP ? nt_ * (kBN / 2) + (wave % (kDmaWaves / 2)) * kDmaCols \
+                                                        : nt_ * kBN + wave * kDmaCols);         \
+        b_base = (GATEUP && wave >= kDmaWaves / 2 ? P.c1 : P.c0) + n0_ * (P.K / 2);            \
+        s_base = (GATEUP && wave >= kDmaWaves / 2 ? P.s1 : P.s0) + n0_ * (P.K / 16);           \
     } while (0)
 
     // the loads of the next (tile, stage) into its ring slot, by the DMA
@@ -392,17 +404,14 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
             }
             // a DMA wave spreads stage g + kAhead's loads over this stage's MFMAs
             const bool issuing = dma_wave && g + kAhead < nsteps;
-            if (issuing) MOE_PIPE_BEGIN();
+            if (issuing) MOE_PIPE_BEGIN();   /* before the first op: it may set up a new tile */
             const int rs = g & (kStages - 1);
             stage_mfma<GATEUP>(acc, ring + kARing + rs * kABytes, ring + kBRing + rs * kBBytes,
                                ring + kSRing + rs * kSBytes, lo, [&](int p) {
                 if (issuing) {
-                    if (p < 6) {
-                        MOE_PIPE_OP(p);
-                    } else {           // 6: codes 2 + scales 0, 7: codes 3 + scales 1
-                        MOE_PIPE_OP(p);
-                        MOE_PIPE_OP(p + 2);
-                    }
+#pragma unroll
+                    for (int j = 0; j < kOpsPerStage; ++j)
+                        if (dma_point(j, wave) == p) MOE_PIPE_OP(j);
                 }
             });
             if (issuing) MOE_PIPE_END();
