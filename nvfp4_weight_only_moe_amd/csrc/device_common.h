@@ -211,6 +211,17 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Minimum over all 64 lanes, returned in every lane.
+__device__ __forceinline__ int wave_min_i32_dpp(int v) {
+    v = min(v, dpp_i32<kDppRowShr1>(INT_MAX, v));
+    v = min(v, dpp_i32<kDppRowShr2>(INT_MAX, v));
+    v = min(v, dpp_i32<kDppRowShr4>(INT_MAX, v));
+    v = min(v, dpp_i32<kDppRowShr8>(INT_MAX, v));
+    v = min(v, dpp_i32<kDppRowBcast15, 0xA>(INT_MAX, v));
+    v = min(v, dpp_i32<kDppRowBcast31, 0xC>(INT_MAX, v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);

@@ -84,23 +84,21 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
              uint16_t* __restrict__ h, const GuRoute R) {
     extern __shared__ uint4 xs[];   // [kXTokens][H / 8]
     __shared__ int s_ids[kDecodeMaxSlots], s_pos[kDecodeMaxSlots], s_sorted[kDecodeMaxSlots];
-    __shared__ float s_w[kDecodeMaxSlots];
     __shared__ int s_list[kDecodeMaxSlots], s_ucnt[kDecodeMaxSlots], s_uoff[kDecodeMaxSlots];
     __shared__ int s_U;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     int my_slot, e, ne, p0, U = 0;
+    float sel_logit = 0.0f;     // wave 0 of a routing workgroup: lane j < k holds the j-th selected logit
     if constexpr (ROUTE) {
         // nothing else is in flight while the logits load: the barriers below
         // then wait for no memory traffic
         if (wave == 0) {
+            // the selection only: the routing weights are needed for the
+            // stored outputs alone and are computed after the loads are out
             int id;
-            float wt;
-            wave_topk_select<EPL>(R.logits, E, k, id, wt);
-            if (lane < k) {
-                s_ids[lane] = id;
-                s_w[lane] = wt;
-            }
+            wave_topk_ids<EPL>(R.logits, E, k, id, sel_logit);
+            if (lane < k) s_ids[lane] = id;
         }
         __syncthreads();
         if (wave == 0) {
@@ -245,12 +243,15 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
     // of expert column 0 their share of the per-expert ones
     if constexpr (ROUTE) {
         if (blockIdx.y != 0) return;
-        if (blockIdx.x == 0 && threadIdx.x < slots) {
-            const int i = threadIdx.x, pos = s_pos[i];
-            R.ids[i] = s_ids[i];
-            R.w[i] = s_w[i];
-            R.slot_pos[i] = pos;
-            R.sorted_slots[pos] = i;
+        if (blockIdx.x == 0 && wave == 0) {
+            const float w = topk_softmax(sel_logit, k);
+            if (lane < slots) {
+                const int i = lane, pos = s_pos[i];
+                R.ids[i] = s_ids[i];
+                R.w[i] = w;
+                R.slot_pos[i] = pos;
+                R.sorted_slots[pos] = i;
+            }
         }
         const int G = gridDim.x;
         const int e0 = (int)((int64_t)blockIdx.x * E / G), e1 = (int)((int64_t)(blockIdx.x + 1) * E / G);

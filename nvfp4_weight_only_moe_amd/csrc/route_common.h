@@ -4,56 +4,96 @@
 #pragma once
 
 #include <float.h>
+#include <limits.h>
 
 #include "device_common.h"
 
 namespace moe {
 
+// Candidate order of the top-k: larger logit first, then the lower expert.
+__device__ __forceinline__ bool topk_before(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
 // One wave selects the top-k of one token's E logits.  EPL = logits per lane
-// (E <= 64 * EPL).  Each round finds the maximum with a DPP reduction, then
-// the lowest expert index holding it with one ballot per logit slot (slot i
-// covers indices 64i .. 64i+63, so the first slot and lane with a match is the
-// lowest index), and retires that logit.  On return lane j < k holds the j-th
-// selection and its weight, a softmax over the k selected logits.  -0.0 is
-// folded into +0.0 so that the two compare equal.
+// (E <= 64 * EPL); lane l holds experts l, l + 64, ...  Each lane first sorts
+// its EPL candidates (insertion network, best first), so a round only has to
+// find the best of the 64 lane heads: one DPP maximum, a ballot for the lanes
+// holding it and, when several do (equal logits), a DPP minimum of their
+// expert indices; the winning lane then drops its head.  On return lane j < k
+// holds the j-th selection (expert in id_out, logit in v_out).  -0.0 is
+// folded into +0.0 so that the two compare equal; a NaN logit ranks as -inf.
 template <int EPL>
-__device__ __forceinline__ void wave_topk_select(const float* __restrict__ row, int E, int k, int& id_out,
-                                                 float& w_out) {
+__device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int E, int k, int& id_out,
+                                              float& v_out) {
     const int lane = threadIdx.x & (kWave - 1);
     float v[EPL];
+    int ix[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int idx = lane + kWave * i;
-        v[i] = idx < E ? row[idx] + 0.0f : -INFINITY;
+        const float x = idx < E ? row[idx] + 0.0f : -INFINITY;
+        v[i] = x != x ? -INFINITY : x;
+        ix[i] = idx;
     }
+#pragma unroll
+    for (int a = 1; a < EPL; ++a)
+#pragma unroll
+        for (int b = a; b > 0; --b) {
+            const bool sw = topk_before(v[b], ix[b], v[b - 1], ix[b - 1]);
+            const float tv = v[b];
+            const int ti = ix[b];
+            v[b] = sw ? v[b - 1] : tv;
+            ix[b] = sw ? ix[b - 1] : ti;
+            v[b - 1] = sw ? tv : v[b - 1];
+            ix[b - 1] = sw ? ti : ix[b - 1];
+        }
     float my_v = 0.0f;
     int my_i = 0;
     for (int r = 0; r < k; ++r) {
-        float lm = v[0];
-#pragma unroll
-        for (int i = 1; i < EPL; ++i) lm = fmaxf(lm, v[i]);
-        const float m = wave_max_dpp(lm);
-        int sel = -1;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const uint64_t b = __ballot(v[i] == m);
-            if (sel < 0 && b) sel = kWave * i + __ffsll((unsigned long long)b) - 1;
+        const float m = wave_max_dpp(v[0]);
+        const uint64_t b = __ballot(v[0] == m);
+        int win = __ffsll((unsigned long long)b) - 1;
+        if (__popcll(b) > 1) {     // equal logits: the lowest expert index among the heads
+            const int mi = wave_min_i32_dpp(v[0] == m ? ix[0] : INT_MAX);
+            win = __ffsll((unsigned long long)__ballot(v[0] == m && ix[0] == mi)) - 1;
         }
-        if (lane == (sel & (kWave - 1))) {
+        const int sel = __builtin_amdgcn_readlane(ix[0], win);
+        if (lane == win) {
 #pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                if (i == sel / kWave) v[i] = -INFINITY;
+            for (int i = 0; i + 1 < EPL; ++i) {
+                v[i] = v[i + 1];
+                ix[i] = ix[i + 1];
+            }
+            v[EPL - 1] = -INFINITY;
+            ix[EPL - 1] = INT_MAX;
         }
         if (lane == r) {
             my_v = m;
             my_i = sel;
         }
     }
+    id_out = my_i;
+    v_out = my_v;
+}
+
+// Routing weights of a wave_topk_ids selection: softmax over the k selected
+// logits (lane j < k holds the j-th), computed from the largest.
+__device__ __forceinline__ float topk_softmax(float my_v, int k) {
+    const int lane = threadIdx.x & (kWave - 1);
     const float m0 = __shfl(my_v, 0, kWave);
     const float ex = lane < k ? expf(my_v - m0) : 0.0f;
     const float sum = wave_sum_dpp(ex);
-    id_out = my_i;
-    w_out = ex / sum;
+    return ex / sum;
+}
+
+// Top-k experts and their routing weights (lane j < k: j-th selection).
+template <int EPL>
+__device__ __forceinline__ void wave_topk_select(const float* __restrict__ row, int E, int k, int& id_out,
+                                                 float& w_out) {
+    float v;
+    wave_topk_ids<EPL>(row, E, k, id_out, v);
+    w_out = topk_softmax(v, k);
 }
 
 // Rank of this lane's expert id among the valid lanes below it holding the

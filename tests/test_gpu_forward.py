@@ -184,6 +184,28 @@ def test_route_forward_matches_route_then_forward(T, H, I, E, k, seed, decode_va
     compare_out(bf16_bits_to_f64(out), p.reference(), f"route_forward-T{T}")
 
 
+@pytest.mark.parametrize("decode_variant", [0, 1, 3], indirect=True)
+@pytest.mark.parametrize("E", [64, 256])
+def test_route_forward_ties(E, decode_variant):
+    """One token whose logits hold many exact ties (integers): the routing
+    computed inside the layer's kernels picks the same experts, in the same
+    order, as moe_route_topk and the oracle."""
+    T, H, I, k = 1, 1024, 512, 8
+    lg_np = np.random.default_rng(E).integers(-2, 3, size=(T, E)).astype(np.float32)
+    lg_np[0, 3] = -0.0
+    p = Problem(T, H, I, E, k, 300 + E, logits=lg_np)
+    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
+    lg, xb = to_dev(p.logits), to_dev(p.xb, torch.int16)
+    r_ref = B.moe_route_topk(lg, k)
+    out_ref = B.moe_w4a16_forward(xb, gate, up, down, r_ref)
+    out, r = B.moe_w4a16_route_forward(lg, xb, gate, up, down, k)
+    torch.cuda.synchronize()
+    for name in ("topk_ids", "topk_w", "counts", "offsets", "sorted_slots", "slot_pos"):
+        assert torch.equal(getattr(r, name), getattr(r_ref, name)), name
+    assert np.array_equal(r.topk_ids.cpu().numpy(), p.ids)
+    assert torch.equal(out, out_ref)
+
+
 @pytest.mark.parametrize("decode_variant", [1], indirect=True)
 @pytest.mark.parametrize("T,H,I,E,k,seed", DECODE_CASES[:3])
 def test_decode_local_h_path_is_bit_identical(T, H, I, E, k, seed, decode_variant):

@@ -42,14 +42,17 @@ def test_route_shapes(T, E, k):
     check_route(r.standard_normal((T, E)).astype(np.float32), k, f"random-{T}-{E}-{k}")
 
 
+@pytest.mark.parametrize("E", [64, 256, 300])
 @pytest.mark.parametrize("T", [5, 200])
-def test_route_ties_and_skew(T):
-    r = np.random.default_rng(T)
-    lg = r.integers(-2, 3, size=(T, 64)).astype(np.float32)    # many exact ties
+def test_route_ties_and_skew(T, E):
+    """Exact ties (several logits per lane of the selecting wave when E > 64),
+    signed zeros and a dominant expert."""
+    r = np.random.default_rng(T * 7 + E)
+    lg = r.integers(-2, 3, size=(T, E)).astype(np.float32)     # many exact ties
     lg[:, 0] = -0.0
     lg[:, 1] = 0.0
     check_route(lg, 8, f"ties-{T}")
-    sk = r.standard_normal((T, 64)).astype(np.float32)
+    sk = r.standard_normal((T, E)).astype(np.float32)
     sk[:, 5] += 50.0                                             # every token picks expert 5
     check_route(sk, 2, f"skew-{T}")
 
