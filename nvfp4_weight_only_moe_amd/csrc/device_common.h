@@ -124,6 +124,23 @@ __device__ __forceinline__ void lds_dma4_sv(const void* sbase, uint32_t voff, ld
                  "{m0}"((uint32_t)(uintptr_t)ldst) : "memory");
 }
 
+// Non-temporal 16- and 8-byte loads (the "nt" cache policy): for weights
+// that are read exactly once per step, so that streaming them does not evict
+// what stays hot between launches (kernel code, activations, routing data)
+// from L2 and the Infinity Cache.
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int nt_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load_stream16(const uint4* p) {
+    const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 load_stream8(const uint2* p) {
+    const nt_u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x2*>(p));
+    return make_uint2(v[0], v[1]);
+}
+template <class Tv>
+__device__ __forceinline__ Tv load_stream(const Tv* p) { return __builtin_nontemporal_load(p); }
+
 // Wait for every outstanding memory operation of this wave.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
