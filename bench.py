@@ -5,9 +5,10 @@
 A step is one pass of the hot path over one batch of synthetic input:
 router top-k + permutation and the layer forward (gate/up grouped GEMM +
 SwiGLU, down grouped GEMM, routing-weighted combine), issued as one
-moe_w4a16_route_forward call (on decode shapes a single kernel launch), or
-with --split as moe_route_topk followed by moe_w4a16_forward.  Quantization
-is load time and is not in a step.
+moe_w4a16_route_forward call (one token: two kernel launches, the route
+computed inside the gate/up kernel), or with --split as moe_route_topk
+followed by moe_w4a16_forward.  Quantization is load time and is not in a
+step.
 
 Default workload: decode, 1 token, hidden 5120, intermediate 1536, 256
 experts, top-8 (the "decode-t1" workload).  Inputs are resident in HBM before
@@ -17,8 +18,11 @@ weights (a model has one such layer per MoE block); the steps are replayed
 from a HIP graph that holds L consecutive steps.
 
 Prints one JSON line: the driver's fields plus "roofline" (dominant kernel,
-HIP-event timed on its own stream) and "cpu_baseline" (the CPU oracle timed
-on a bounded sample of the same workload).
+HIP-event timed on its own stream), "cpu_baseline" (the CPU oracle timed on a
+bounded sample of the same workload), "step_spread" (p10/p50/p90 of the step
+time over the graph replays, timed after the measured steps) and
+"achievable_peaks" (a 1 GiB device copy and an 8192^3 bf16 GEMM by the
+torch/ROCm libraries, for context beside the spec peaks).
 """
 import argparse
 import json
@@ -49,6 +53,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=None, help="layer copies cycled through (decode)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--decode-variant", type=int, default=3,
                     help="decode-shape kernels (moe_debug_set_decode_variant): 0 per-expert-block "
@@ -196,6 +201,7 @@ def main():
 
     # ---------------------------------------------------------------- graph timing
     graph_ms = None
+    step_spread = None
     if not args.no_graph:
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -220,6 +226,17 @@ def main():
             graph_ms = timed(lambda n: [g.replay() for _ in range(n)], reps) / copies
             assert torch.equal(out, ref_out)
             log(f"graph: {graph_ms * 1e3:.2f} us/step")
+            # spread: each replay (copies consecutive steps) timed on its own, after the timed region
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for a, b in evs:
+                a.record()
+                g.replay()
+                b.record()
+            torch.cuda.synchronize()
+            per = sorted(a.elapsed_time(b) / copies * 1e3 for a, b in evs)
+            q = lambda f: round(per[int(round(f * (len(per) - 1)))], 3)
+            step_spread = {"p10_us": q(0.1), "p50_us": q(0.5), "p90_us": q(0.9), "samples": len(per),
+                           "steps_per_sample": copies}
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
 
     # ---------------------------------------------------------------- per-kernel timing
@@ -276,6 +293,27 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 copies of 268435456 bytes (read 256 MiB, write 256 MiB each)")
 
+    # ---------------------------------------------------------------- achievable peaks
+    # what plain library work reaches on this GPU, beside the spec peaks the
+    # roofline uses: a 1 GiB device copy (read + write) and a bf16 GEMM
+    achievable = None
+    if not args.no_peaks:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        copy_ms = timed(lambda r: [dst.copy_(src) for _ in range(r)], 5)
+        del src, dst
+        m = 8192
+        ga = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+        gb = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+        gc = ga @ gb
+        mm_ms = timed(lambda r: [torch.matmul(ga, gb, out=gc) for _ in range(r)], 5)
+        del ga, gb, gc
+        achievable = {"hbm_copy_GBps": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
+                      "bf16_gemm_8192_TFLOPs": round(2.0 * m ** 3 / (mm_ms * 1e-3) / 1e12, 1)}
+        log(f"achievable: {achievable}")
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu:
@@ -297,6 +335,7 @@ def main():
         "step_TFLOPs": round(step_tflops, 3), "step_mfma_frac": round(step_tflops / BF16_PEAK_TFLOPS, 5),
         "eager_ms_per_step": round(eager_ms, 6), "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 6),
         "per_kernel_us": per_kernel_us, "quantize_pack_ms_total": round(quant_ms, 2),
+        "step_spread": step_spread, "achievable_peaks": achievable,
     }
     print(json.dumps(rec), flush=True)
 
