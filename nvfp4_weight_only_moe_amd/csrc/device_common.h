@@ -228,6 +228,18 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Maximum over all 64 lanes of unsigned keys, returned in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t u) {
+    int v = (int)u;
+    v = (int)max((uint32_t)v, (uint32_t)dpp_i32<kDppRowShr1>(0, v));
+    v = (int)max((uint32_t)v, (uint32_t)dpp_i32<kDppRowShr2>(0, v));
+    v = (int)max((uint32_t)v, (uint32_t)dpp_i32<kDppRowShr4>(0, v));
+    v = (int)max((uint32_t)v, (uint32_t)dpp_i32<kDppRowShr8>(0, v));
+    v = (int)max((uint32_t)v, (uint32_t)dpp_i32<kDppRowBcast15, 0xA>(0, v));
+    v = (int)max((uint32_t)v, (uint32_t)dpp_i32<kDppRowBcast31, 0xC>(0, v));
+    return (uint32_t)__builtin_amdgcn_readlane(v, 63);
+}
+
 // Minimum over all 64 lanes, returned in every lane.
 __device__ __forceinline__ int wave_min_i32_dpp(int v) {
     v = min(v, dpp_i32<kDppRowShr1>(INT_MAX, v));

@@ -10,66 +10,68 @@
 
 namespace moe {
 
-// Candidate order of the top-k: larger logit first, then the lower expert.
-__device__ __forceinline__ bool topk_before(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
+// Order-preserving unsigned key of a float (no NaN; -0.0 folded into +0.0
+// beforehand): larger float, larger key.  topk_key_value inverts it.
+__device__ __forceinline__ uint32_t topk_key(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return u ^ ((u >> 31) ? 0xFFFFFFFFu : 0x80000000u);
+}
+__device__ __forceinline__ float topk_key_value(uint32_t key) {
+    return __uint_as_float(key ^ ((key >> 31) ? 0x80000000u : 0xFFFFFFFFu));
 }
 
 // One wave selects the top-k of one token's E logits.  EPL = logits per lane
-// (E <= 64 * EPL); lane l holds experts l, l + 64, ...  Each lane first sorts
-// its EPL candidates (insertion network, best first), so a round only has to
-// find the best of the 64 lane heads: one DPP maximum, a ballot for the lanes
-// holding it and, when several do (equal logits), a DPP minimum of their
-// expert indices; the winning lane then drops its head.  On return lane j < k
-// holds the j-th selection (expert in id_out, logit in v_out).  -0.0 is
-// folded into +0.0 so that the two compare equal; a NaN logit ranks as -inf.
+// (E <= 64 * EPL); lane l holds experts l, l + 64, ...  Each candidate becomes
+// one 64-bit key: the order-preserving bits of its logit above the complement
+// of its expert index, so that a plain unsigned comparison is the selection
+// order (larger logit first, then the lower expert).  Each lane sorts its EPL
+// keys (insertion network, best first), so a round only has to find the best
+// of the 64 lane heads: one DPP maximum of the logit halves, a ballot for the
+// lanes holding it and, when several do (equal logits), a DPP minimum of
+// their expert indices; the winning lane then drops its head.  On return
+// lane j < k holds the j-th selection (expert in id_out, logit in v_out).
+// -0.0 is folded into +0.0 so that the two compare equal; a NaN logit ranks
+// as -inf.  A dropped head becomes key 0, below every candidate.
 template <int EPL>
 __device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int E, int k, int& id_out,
                                               float& v_out) {
     const int lane = threadIdx.x & (kWave - 1);
-    float v[EPL];
-    int ix[EPL];
+    uint64_t kk[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int idx = lane + kWave * i;
         const float x = idx < E ? row[idx] + 0.0f : -INFINITY;
-        v[i] = x != x ? -INFINITY : x;
-        ix[i] = idx;
+        kk[i] = ((uint64_t)topk_key(x != x ? -INFINITY : x) << 32) | (uint32_t)~idx;
     }
 #pragma unroll
     for (int a = 1; a < EPL; ++a)
 #pragma unroll
         for (int b = a; b > 0; --b) {
-            const bool sw = topk_before(v[b], ix[b], v[b - 1], ix[b - 1]);
-            const float tv = v[b];
-            const int ti = ix[b];
-            v[b] = sw ? v[b - 1] : tv;
-            ix[b] = sw ? ix[b - 1] : ti;
-            v[b - 1] = sw ? tv : v[b - 1];
-            ix[b - 1] = sw ? ti : ix[b - 1];
+            const uint64_t hi = kk[b] > kk[b - 1] ? kk[b] : kk[b - 1];
+            const uint64_t lo = kk[b] > kk[b - 1] ? kk[b - 1] : kk[b];
+            kk[b - 1] = hi;
+            kk[b] = lo;
         }
     float my_v = 0.0f;
     int my_i = 0;
     for (int r = 0; r < k; ++r) {
-        const float m = wave_max_dpp(v[0]);
-        const uint64_t b = __ballot(v[0] == m);
+        const uint32_t head = (uint32_t)(kk[0] >> 32);
+        const int head_ix = (int)~(uint32_t)kk[0];
+        const uint32_t m = wave_max_u32_dpp(head);
+        const uint64_t b = __ballot(head == m);
         int win = __ffsll((unsigned long long)b) - 1;
         if (__popcll(b) > 1) {     // equal logits: the lowest expert index among the heads
-            const int mi = wave_min_i32_dpp(v[0] == m ? ix[0] : INT_MAX);
-            win = __ffsll((unsigned long long)__ballot(v[0] == m && ix[0] == mi)) - 1;
+            const int mi = wave_min_i32_dpp(head == m ? head_ix : INT_MAX);
+            win = __ffsll((unsigned long long)__ballot(head == m && head_ix == mi)) - 1;
         }
-        const int sel = __builtin_amdgcn_readlane(ix[0], win);
+        const int sel = __builtin_amdgcn_readlane(head_ix, win);
         if (lane == win) {
 #pragma unroll
-            for (int i = 0; i + 1 < EPL; ++i) {
-                v[i] = v[i + 1];
-                ix[i] = ix[i + 1];
-            }
-            v[EPL - 1] = -INFINITY;
-            ix[EPL - 1] = INT_MAX;
+            for (int i = 0; i + 1 < EPL; ++i) kk[i] = kk[i + 1];
+            kk[EPL - 1] = 0u;
         }
         if (lane == r) {
-            my_v = m;
+            my_v = topk_key_value(m);
             my_i = sel;
         }
     }
