@@ -278,16 +278,15 @@ template <int GPL2, int MAXT>
 __global__ void __launch_bounds__(kDownMaxWaves * kWave)
 k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
            const uint8_t* dc, const uint8_t* ds, const float* __restrict__ dg,
-           const float* __restrict__ topk_w, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-           const int32_t* __restrict__ sorted_slots, uint16_t* __restrict__ out, int slot_cap) {
+           const int32_t* __restrict__ ids, const float* __restrict__ topk_w,
+           uint16_t* __restrict__ out, int slot_cap) {
     constexpr int kDownChunkExperts = down_chunk_experts<MAXT>();
     extern __shared__ uint4 hs[];     // [slot_cap][I / 8]
-    __shared__ int s_cnt[MOE_MAX_EXPERTS], s_off[MOE_MAX_EXPERTS];
-    __shared__ int s_list[MOE_MAX_EXPERTS];
-    __shared__ float s_g[MOE_MAX_EXPERTS];
-    __shared__ int s_slot[kDecodeMaxSlots], s_tok[kDecodeMaxSlots];
-    __shared__ float s_w[kDecodeMaxSlots], s_wgt[kDecodeMaxSlots];
-    __shared__ int s_U;
+    __shared__ int s_list[kDecodeMaxSlots], s_ucnt[kDecodeMaxSlots], s_uoff[kDecodeMaxSlots];
+    __shared__ int s_tok[kDecodeMaxSlots];
+    __shared__ float s_wgt[kDecodeMaxSlots];
+    __shared__ int s_cu[kDecodeMaxSlots + 1];   // chunk c: touched experts [s_cu[c], s_cu[c + 1])
+    __shared__ int s_U, s_NC;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int half = lane >> 5, l32 = lane & 31;
     const int waves = blockDim.x / kWave;
@@ -297,85 +296,131 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
     const int ngroups = I / 16, I8 = I / 8;
     const int slots = T * k;                                   // <= kDecodeMaxSlots on this path
 
-    // all small inputs in one batch of independent loads
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        s_cnt[e] = counts[e];
-        s_off[e] = offsets[e];
-        s_g[e] = dg[e];
-    }
-    if (threadIdx.x < slots) {
-        s_slot[threadIdx.x] = sorted_slots[threadIdx.x];
-        s_w[threadIdx.x] = topk_w[threadIdx.x];
-    }
-    __syncthreads();
-    if (threadIdx.x < slots) {
-        const int slot = s_slot[threadIdx.x];
-        s_tok[threadIdx.x] = slot / k;
-        s_wgt[threadIdx.x] = s_w[slot];
-    }
-    if (wave == 0) {    // compact list of touched experts, ascending
-        int U = 0;
-        for (int base = 0; base < E; base += kWave) {
-            const int e = base + lane;
-            const bool act = e < E && s_cnt[e] > 0;
-            const uint64_t m = __ballot(act);
-            if (act) s_list[U + __popcll(m & lanemask_lt())] = e;
-            U += __popcll(m);
+    // Wave 0 orders the slots by (expert, flat slot index) -- the order of
+    // the h rows -- from the top-k ids alone, in registers: one ballot per
+    // expert bit splits the lanes still equal so far into smaller and equal.
+    // It then groups the touched experts (ascending) into chunks.
+    if (wave == 0) {
+        const bool valid = lane < slots;
+        int ex = valid ? ids[lane] : 0;
+        const float wv = valid ? topk_w[lane] : 0.0f;
+        ex = min(max(ex, 0), E - 1);     // keeps every weight address inside the stacks
+        int nbits = 1;
+        while ((1 << nbits) < E) ++nbits;
+        uint64_t eq = __ballot(valid), lessm = 0;
+        for (int b = nbits - 1; b >= 0; --b) {
+            const bool bit = (ex >> b) & 1;
+            const uint64_t B = __ballot(valid && bit);
+            if (bit) {
+                lessm |= eq & ~B;
+                eq &= B;
+            } else {
+                eq &= ~B;
+            }
         }
-        if (lane == 0) s_U = U;
+        const int less = __popcll(lessm);                      // slots of smaller experts
+        const uint64_t before = eq & lanemask_lt();
+        const bool first = valid && before == 0;
+        const uint64_t firsts = __ballot(first);
+        const int uj = __popcll(firsts & lessm);               // rank of this slot's expert
+        const int endj = less + __popcll(eq);                  // sorted end of this slot's expert
+        if (valid) {
+            const int pos = less + __popcll(before);
+            s_tok[pos] = lane / k;
+            s_wgt[pos] = wv;
+        }
+        if (first) {
+            s_list[uj] = ex;
+            s_ucnt[uj] = __popcll(eq);
+            s_uoff[uj] = less;
+        }
+        const int U = __popcll(firsts);
+        int nc = 1;
+        if (U > kDownChunkExperts || slots > slot_cap) {
+            // greedy: a chunk takes experts while it holds at most
+            // kDownChunkExperts of them and slot_cap h rows
+            int c0 = 0, pA = 0;
+            for (int u = 1; u < U; ++u) {
+                const int src = __ffsll((unsigned long long)__ballot(first && uj == u)) - 1;
+                const int end_u = __builtin_amdgcn_readlane(endj, src);
+                if (u - c0 >= kDownChunkExperts || end_u - pA > slot_cap) {
+                    if (lane == 0) s_cu[nc] = u;
+                    ++nc;
+                    c0 = u;
+                    pA = __builtin_amdgcn_readlane(less, src);
+                }
+            }
+        }
+        if (lane == 0) {
+            s_cu[0] = 0;
+            s_cu[nc] = U;
+            s_U = U;
+            s_NC = nc;
+        }
     }
     __syncthreads();
-    const int U = s_U;
+    const int NC = s_NC;
+
+    // per-lane byte offsets inside one expert's down stack (rows of I / 2
+    // code bytes and I / 16 scale bytes); the expert base is wave-uniform
+    uint32_t voc[GPL2], vos[GPL2];
+#pragma unroll
+    for (int j = 0; j < GPL2; ++j) {
+        const int g = l32 + 32 * j;
+        voc[j] = (uint32_t)nr * (uint32_t)(I / 2) + (uint32_t)g * 8u;
+        vos[j] = (uint32_t)nr * (uint32_t)ngroups + (uint32_t)g;
+    }
+    const int64_t code_stride = (int64_t)H * (I / 2), scale_stride = (int64_t)H * ngroups;
 
     float acc[MAXT];
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) acc[t] = 0.0f;
 
-    int u0 = 0;
-    while (u0 < U) {
-        // chunk [u0, u1): at most kDownChunkExperts experts and slot_cap h rows
-        const int pA = s_off[s_list[u0]];
-        int u1 = u0 + 1;
-        while (u1 < U && u1 - u0 < kDownChunkExperts &&
-               s_off[s_list[u1]] + s_cnt[s_list[u1]] - pA <= slot_cap)
-            ++u1;
-        const int pB = s_off[s_list[u1 - 1]] + s_cnt[s_list[u1 - 1]];
+    for (int c = 0; c < NC; ++c) {
+        const int u0 = s_cu[c], u1 = s_cu[c + 1];
+        const int pA = s_uoff[u0];
+        const int pB = s_uoff[u1 - 1] + s_ucnt[u1 - 1];
 
         // h rows of the chunk straight to LDS (contiguous in sorted order)
-        __syncthreads();    // the previous chunk's LDS rows are no longer read
+        if (c > 0) __syncthreads();    // the previous chunk's LDS rows are no longer read
         {
             const uint4* hsrc = reinterpret_cast<const uint4*>(h + (int64_t)pA * I);
             const int nchunk = (pB - pA) * I8 / 64;       // I % 512 == 0 on this path
-            for (int c = wave; c < nchunk; c += waves) wave_copy_1k_to_lds(hsrc + c * 64, hs + c * 64);
+            for (int q = wave; q < nchunk; q += waves) wave_copy_1k_to_lds(hsrc + q * 64, hs + q * 64);
         }
         // codes of every chunk slot (slots past the chunk re-read its last
         // expert, so the number of loads in flight is fixed); kDownAhead
-        // experts are in flight while one is computed
+        // experts are in flight while one is computed.  The expert's global
+        // scale is one more (broadcast) vector load in the same sequence.
         uint2 cw[kDownChunkExperts][GPL2];
         uint32_t sw[kDownChunkExperts][GPL2];
+        float gv[kDownChunkExperts];
 #define MOE_DOWN_LOAD(u)                                                                        \
         do {                                                                                    \
-            const int64_t row_ = (int64_t)s_list[min(u0 + (u), u1 - 1)] * H + nr;               \
+            const int e_ = __builtin_amdgcn_readfirstlane(s_list[min(u0 + (u), u1 - 1)]);       \
+            const uint8_t* cb_ = dc + e_ * code_stride;                                         \
+            const uint8_t* sb_ = ds + e_ * scale_stride;                                        \
             _Pragma("unroll") for (int j = 0; j < GPL2; ++j) {                                  \
-                const int g = l32 + 32 * j;                                                     \
-                cw[u][j] = load_stream8(&reinterpret_cast<const uint2*>(dc + row_ * (I / 2))[g]); \
-                sw[u][j] = load_stream(&ds[row_ * ngroups + g]);                                \
+                cw[u][j] = load_stream8(reinterpret_cast<const uint2*>(cb_ + voc[j]));          \
+                sw[u][j] = load_stream(sb_ + vos[j]);                                           \
             }                                                                                   \
+            int ev_ = e_;                                                                       \
+            asm volatile("v_mov_b32 %0, %1" : "=v"(ev_) : "v"(ev_)); /* a vector load */        \
+            gv[u] = dg[ev_];                                                                    \
             asm volatile("" ::: "memory");  /* issue here, not at the first use */              \
         } while (0)
 #pragma unroll
         for (int u = 0; u < kDownAhead; ++u) MOE_DOWN_LOAD(u);
         // this wave's h rows and its first expert's codes have landed
-        wait_vmem_at_most<2 * GPL2 * (kDownAhead - 1)>();
+        wait_vmem_at_most<(2 * GPL2 + 1) * (kDownAhead - 1)>();
         __builtin_amdgcn_s_barrier();   // plain barrier: a fence here would wait for every load
 
 #pragma unroll
         for (int u = 0; u < kDownChunkExperts; ++u) {
             if (u + kDownAhead < kDownChunkExperts) MOE_DOWN_LOAD(u + kDownAhead);
             if (u0 + u < u1) {
-                const int e = s_list[u0 + u];
-                const float ge = s_g[e];
-                const int q0 = s_off[e] - pA, ne = s_cnt[e];
+                const float ge = gv[u];
+                const int q0 = s_uoff[u0 + u] - pA, ne = s_ucnt[u0 + u];
                 float sc[GPL2];
 #pragma unroll
                 for (int j = 0; j < GPL2; ++j) sc[j] = e4m3_to_f32(sw[u][j]);
@@ -396,7 +441,6 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
             }
         }
 #undef MOE_DOWN_LOAD
-        u0 = u1;
     }
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) {
@@ -465,7 +509,7 @@ moe_status launch_down_t(const FwdArgs& a, hipStream_t s) {
     MOE_LAUNCH("dec_down", (k_dec_down<GPL2, MAXT>), dim3((a.H + rows_per_block - 1) / rows_per_block),
                dim3(waves * kWave), shmem, s, (const uint16_t*)a.h, a.T, a.H, a.I, a.E, a.k,
                (const uint8_t*)a.down->codes, (const uint8_t*)a.down->scales, (const float*)a.down->global_scale,
-               a.topk_w, a.counts, a.offsets, a.sorted_slots, a.out, slot_cap);
+               a.ids, a.topk_w, a.out, slot_cap);
     return MOE_OK;
 }
 
