@@ -28,10 +28,14 @@
 //     two rows (one per half-wave) and loops over every touched expert in
 //     ascending order and every token of that expert, so the
 //     routing-weighted combine happens in registers (fp32, fixed order, no
-//     atomics) and out is written once in bf16.  The h rows of a chunk of
-//     experts (contiguous in sorted order) are staged in LDS once per
-//     workgroup, and the weight codes of the whole chunk are loaded before
-//     any of them is used.
+//     atomics) and out is written once in bf16.  Wave 0 orders the slots
+//     from the top-k ids alone (ballots on the expert bits), so the weight
+//     loads wait for one small load only.  A lane reads adjacent group
+//     pairs (16-byte code loads) and the row's scales as whole dwords handed
+//     out by ds_bpermute.  The h rows of a chunk of experts (contiguous in
+//     sorted order) are staged in LDS once per workgroup, permuted so that
+//     every LDS read is 32 consecutive 16-byte slots, and the weight codes of
+//     the whole chunk are loaded before any of them is used.
 #include "device_common.h"
 #include "internal.h"
 #include "route_common.h"
@@ -49,6 +53,7 @@ constexpr int kDownMaxWaves = 12;
 template <int MAXT> constexpr int down_chunk_experts() { return MAXT == 1 ? 8 : 16; }
 template <int MAXT> constexpr int down_chunk_slots() { return MAXT == 1 ? 16 : 48; }
 constexpr int kDownAhead = 3;           // experts' down codes in flight ahead of the one computed
+constexpr int kDownRows = 1;            // output rows per half-wave (more: fewer waves, measured slower)
 constexpr int kDecodeMaxSlots = 64;     // T * k on the decode path
 constexpr int kXTokens = 2;             // activation rows staged in LDS at a time (gate/up)
 
@@ -287,12 +292,11 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
     __shared__ float s_wgt[kDecodeMaxSlots];
     __shared__ int s_cu[kDecodeMaxSlots + 1];   // chunk c: touched experts [s_cu[c], s_cu[c + 1])
     __shared__ int s_U, s_NC;
+    constexpr int R = kDownRows;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int half = lane >> 5, l32 = lane & 31;
     const int waves = blockDim.x / kWave;
-    const int n = (blockIdx.x * waves + wave) * 2 + half;      // output row of H
-    const bool row_ok = n < H;
-    const int nr = row_ok ? n : H - 1;
+    const int n0 = ((blockIdx.x * waves + wave) * 2 + half) * R;   // first output row of H
     const int ngroups = I / 16, I8 = I / 8;
     const int slots = T * k;                                   // <= kDecodeMaxSlots on this path
 
@@ -361,92 +365,152 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
     __syncthreads();
     const int NC = s_NC;
 
-    // per-lane byte offsets inside one expert's down stack (rows of I / 2
-    // code bytes and I / 16 scale bytes); the expert base is wave-uniform
-    uint32_t voc[GPL2], vos[GPL2];
+    // Lane l of a half-wave owns, in its row, the group pairs (64 p + 2 l,
+    // 64 p + 2 l + 1), p < NP (one 16-byte code load each), and, when GPL2 is
+    // odd, the single group 64 NP + l (one 8-byte load): every wave load is a
+    // contiguous 512 B or 256 B run per row.  The row's scale bytes are
+    // requested as whole dwords (lane m: dword m) and handed to their lanes
+    // with ds_bpermute, so one expert costs NP + ODD + 1 vector loads per wave.
+    constexpr int NP = GPL2 / 2, ODD = GPL2 & 1, NCHUNK = NP + ODD;
+    constexpr int kLoadsPerExpert = (NCHUNK + 1) * kDownRows;
+    uint32_t voc[R][NCHUNK], vos[R];
 #pragma unroll
-    for (int j = 0; j < GPL2; ++j) {
-        const int g = l32 + 32 * j;
-        voc[j] = (uint32_t)nr * (uint32_t)(I / 2) + (uint32_t)g * 8u;
-        vos[j] = (uint32_t)nr * (uint32_t)ngroups + (uint32_t)g;
+    for (int r = 0; r < R; ++r) {
+        const uint32_t nr = (uint32_t)min(n0 + r, H - 1);
+#pragma unroll
+        for (int p = 0; p < NCHUNK; ++p)
+            voc[r][p] = nr * (uint32_t)(I / 2) + (uint32_t)(512 * p) + (uint32_t)l32 * (p < NP ? 16u : 8u);
+        vos[r] = nr * (uint32_t)ngroups + 4u * (uint32_t)min(l32, 8 * GPL2 - 1);
     }
+    int src_pair[NP > 0 ? NP : 1];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) src_pair[p] = (half * 32 + 16 * p + (l32 >> 1)) * 4;
+    const int src_single = (half * 32 + 16 * NP + (l32 >> 2)) * 4;
+    const int sh_pair = 16 * (l32 & 1), sh_single = 8 * (l32 & 3);
     const int64_t code_stride = (int64_t)H * (I / 2), scale_stride = (int64_t)H * ngroups;
 
-    float acc[MAXT];
+    // every touched expert's global scale in one vector load (lane u: expert u)
+    const float gvv = dg[s_list[min(lane, s_U - 1)]];
+
+    float acc[MAXT][R];
 #pragma unroll
-    for (int t = 0; t < MAXT; ++t) acc[t] = 0.0f;
+    for (int t = 0; t < MAXT; ++t)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[t][r] = 0.0f;
 
     for (int c = 0; c < NC; ++c) {
         const int u0 = s_cu[c], u1 = s_cu[c + 1];
         const int pA = s_uoff[u0];
         const int pB = s_uoff[u1 - 1] + s_ucnt[u1 - 1];
 
-        // h rows of the chunk straight to LDS (contiguous in sorted order)
+        // h rows of the chunk straight to LDS (contiguous in sorted order).
+        // Inside a row the 16-byte chunks are stored transposed to the order
+        // in which the lanes read them: chunk 128 p + 4 l + i (pair p, lane l,
+        // i < 4) at 128 p + 32 i + l, chunk 128 NP + 2 l + i at
+        // 128 NP + 32 i + l, so that every LDS read of the loop is 32
+        // consecutive 16-byte slots.  The DMA gathers: the lane that writes
+        // slot P loads the chunk that belongs there.
         if (c > 0) __syncthreads();    // the previous chunk's LDS rows are no longer read
         {
-            const uint4* hsrc = reinterpret_cast<const uint4*>(h + (int64_t)pA * I);
-            const int nchunk = (pB - pA) * I8 / 64;       // I % 512 == 0 on this path
-            for (int q = wave; q < nchunk; q += waves) wave_copy_1k_to_lds(hsrc + q * 64, hs + q * 64);
+            const int rc = 64 * GPL2;                      // 16-byte chunks per h row
+            const int nq = (pB - pA) * GPL2;               // 1 KiB wave copies
+            for (int q = wave; q < nq; q += waves) {
+                const int slot = q * 64 + lane;
+                const int row = slot / rc, P = slot - row * rc;
+                const int blk = P >> 7, r = P & 127, i = r >> 5, l = r & 31;
+                const int chunk = blk < NP ? 128 * blk + 4 * l + i : 128 * NP + 2 * l + i;
+                const uint4* src = reinterpret_cast<const uint4*>(h + (int64_t)(pA + row) * I) + chunk;
+                __builtin_amdgcn_global_load_lds(src, (lds_void*)(hs + q * 64), 16, 0, 0);
+            }
         }
         // codes of every chunk slot (slots past the chunk re-read its last
         // expert, so the number of loads in flight is fixed); kDownAhead
-        // experts are in flight while one is computed.  The expert's global
-        // scale is one more (broadcast) vector load in the same sequence.
-        uint2 cw[kDownChunkExperts][GPL2];
-        uint32_t sw[kDownChunkExperts][GPL2];
-        float gv[kDownChunkExperts];
+        // experts are in flight while one is computed
+        uint4 cw[kDownChunkExperts][R][NP > 0 ? NP : 1];
+        uint2 cs[kDownChunkExperts][R];
+        uint32_t sw[kDownChunkExperts][R];
 #define MOE_DOWN_LOAD(u)                                                                        \
         do {                                                                                    \
             const int e_ = __builtin_amdgcn_readfirstlane(s_list[min(u0 + (u), u1 - 1)]);       \
             const uint8_t* cb_ = dc + e_ * code_stride;                                         \
             const uint8_t* sb_ = ds + e_ * scale_stride;                                        \
-            _Pragma("unroll") for (int j = 0; j < GPL2; ++j) {                                  \
-                cw[u][j] = load_stream8(reinterpret_cast<const uint2*>(cb_ + voc[j]));          \
-                sw[u][j] = load_stream(sb_ + vos[j]);                                           \
+            _Pragma("unroll") for (int r = 0; r < R; ++r) {                                     \
+                _Pragma("unroll") for (int p = 0; p < NP; ++p)                                  \
+                    cw[u][r][p] = load_stream16(reinterpret_cast<const uint4*>(cb_ + voc[r][p])); \
+                if constexpr (ODD)                                                              \
+                    cs[u][r] = load_stream8(reinterpret_cast<const uint2*>(cb_ + voc[r][NP]));   \
+                sw[u][r] = load_stream(reinterpret_cast<const uint32_t*>(sb_ + vos[r]));        \
             }                                                                                   \
-            int ev_ = e_;                                                                       \
-            asm volatile("v_mov_b32 %0, %1" : "=v"(ev_) : "v"(ev_)); /* a vector load */        \
-            gv[u] = dg[ev_];                                                                    \
             asm volatile("" ::: "memory");  /* issue here, not at the first use */              \
         } while (0)
 #pragma unroll
         for (int u = 0; u < kDownAhead; ++u) MOE_DOWN_LOAD(u);
         // this wave's h rows and its first expert's codes have landed
-        wait_vmem_at_most<(2 * GPL2 + 1) * (kDownAhead - 1)>();
+        wait_vmem_at_most<kLoadsPerExpert * (kDownAhead - 1)>();
         __builtin_amdgcn_s_barrier();   // plain barrier: a fence here would wait for every load
 
 #pragma unroll
         for (int u = 0; u < kDownChunkExperts; ++u) {
             if (u + kDownAhead < kDownChunkExperts) MOE_DOWN_LOAD(u + kDownAhead);
             if (u0 + u < u1) {
-                const float ge = gv[u];
+                const float ge = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gvv), u0 + u));
                 const int q0 = s_uoff[u0 + u] - pA, ne = s_ucnt[u0 + u];
-                float sc[GPL2];
+                float sp0[R][NP > 0 ? NP : 1], sp1[R][NP > 0 ? NP : 1], s1[R];
 #pragma unroll
-                for (int j = 0; j < GPL2; ++j) sc[j] = e4m3_to_f32(sw[u][j]);
+                for (int r = 0; r < R; ++r) {
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        const uint32_t w =
+                            (uint32_t)__builtin_amdgcn_ds_bpermute(src_pair[p], (int)sw[u][r]) >> sh_pair;
+                        sp0[r][p] = e4m3_byte_to_f32<0>(w);
+                        sp1[r][p] = e4m3_byte_to_f32<1>(w);
+                    }
+                    s1[r] = ODD ? e4m3_to_f32((uint32_t)__builtin_amdgcn_ds_bpermute(src_single, (int)sw[u][r]) >>
+                                              sh_single)
+                                : 0.0f;
+                }
                 for (int q = q0; q < q0 + ne; ++q) {
                     const int t = s_tok[pA + q];
                     const float wgt = s_wgt[pA + q] * ge;
-                    const uint4* hr = hs + q * I8;
-                    float a = 0.0f;
+                    const uint4* hr = hs + q * I8 + l32;
+                    float a[R];
 #pragma unroll
-                    for (int j = 0; j < GPL2; ++j) {
-                        const int g = l32 + 32 * j;
-                        a += sc[j] * group_dot(cw[u][j], hr[2 * g], hr[2 * g + 1]);
+                    for (int r = 0; r < R; ++r) a[r] = 0.0f;
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        const uint4* hp = hr + 128 * p;
+                        const uint4 x0 = hp[0], x1 = hp[32], x2 = hp[64], x3 = hp[96];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            a[r] += sp0[r][p] * group_dot(make_uint2(cw[u][r][p].x, cw[u][r][p].y), x0, x1);
+                            a[r] += sp1[r][p] * group_dot(make_uint2(cw[u][r][p].z, cw[u][r][p].w), x2, x3);
+                        }
+                    }
+                    if constexpr (ODD) {
+                        const uint4* hp = hr + 128 * NP;
+                        const uint4 y0 = hp[0], y1 = hp[32];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) a[r] += s1[r] * group_dot(cs[u][r], y0, y1);
                     }
 #pragma unroll
                     for (int tt = 0; tt < MAXT; ++tt)
-                        if (tt == t) acc[tt] += wgt * a;
+                        if (tt == t) {
+#pragma unroll
+                            for (int r = 0; r < R; ++r) acc[tt][r] += wgt * a[r];
+                        }
                 }
             }
         }
 #undef MOE_DOWN_LOAD
     }
 #pragma unroll
-    for (int t = 0; t < MAXT; ++t) {
-        const float v = half_wave_sum_dpp(acc[t]);
-        if (t < T && l32 == 0 && row_ok) out[(int64_t)t * H + n] = f32_to_bf16_rne(v);
-    }
+    for (int t = 0; t < MAXT; ++t)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float v = half_wave_sum_dpp(acc[t][r]);
+            if (t < T && l32 == 0 && n0 + r < H) out[(int64_t)t * H + n0 + r] = f32_to_bf16_rne(v);
+        }
 }
 
 // Stages of two features per gate/up wave.  One token: two stages, so the
@@ -489,8 +553,8 @@ int down_waves_per_block(int H) {
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         cus = 256;
-    // one workgroup per CU when the rows divide evenly: 2 rows per wave
-    int w = (H + 2 * cus - 1) / (2 * cus);
+    // one workgroup per CU when the rows divide evenly: 2 * kDownRows rows per wave
+    int w = (H + 2 * kDownRows * cus - 1) / (2 * kDownRows * cus);
     return std::max(1, std::min(w, kDownMaxWaves));
 }
 
@@ -501,7 +565,7 @@ constexpr int kDownLdsBudget = 128 * 1024;
 template <int GPL2, int MAXT>
 moe_status launch_down_t(const FwdArgs& a, hipStream_t s) {
     const int waves = down_waves_per_block(a.H);
-    const int rows_per_block = 2 * waves;
+    const int rows_per_block = 2 * kDownRows * waves;
     const int slot_cap = std::min({down_chunk_slots<MAXT>(), a.T * a.k, kDownLdsBudget / (a.I * 2)});
     const size_t shmem = (size_t)slot_cap * a.I * sizeof(uint16_t);
     if (allow_dynamic_lds(reinterpret_cast<const void*>(&k_dec_down<GPL2, MAXT>), shmem) != MOE_OK)
