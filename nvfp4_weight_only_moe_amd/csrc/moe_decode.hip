@@ -288,7 +288,7 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
     constexpr int kDownChunkExperts = down_chunk_experts<MAXT>();
     extern __shared__ uint4 hs[];     // [slot_cap][I / 8]
     __shared__ int s_list[kDecodeMaxSlots], s_ucnt[kDecodeMaxSlots], s_uoff[kDecodeMaxSlots];
-    __shared__ int s_tok[kDecodeMaxSlots];
+    __shared__ uint32_t s_tmask[kDecodeMaxSlots];   // tokens routed to touched expert u (bit t)
     __shared__ float s_wgt[kDecodeMaxSlots];
     __shared__ int s_cu[kDecodeMaxSlots + 1];   // chunk c: touched experts [s_cu[c], s_cu[c + 1])
     __shared__ int s_U, s_NC;
@@ -328,15 +328,16 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
         const uint64_t firsts = __ballot(first);
         const int uj = __popcll(firsts & lessm);               // rank of this slot's expert
         const int endj = less + __popcll(eq);                  // sorted end of this slot's expert
-        if (valid) {
-            const int pos = less + __popcll(before);
-            s_tok[pos] = lane / k;
-            s_wgt[pos] = wv;
-        }
+        if (valid) s_wgt[less + __popcll(before)] = wv;
         if (first) {
+            // a token routes to an expert at most once: its slots t*k .. t*k+k-1
+            uint32_t tm = 0;
+            const uint64_t km = k < 64 ? (1ull << k) - 1 : ~0ull;
+            for (int t = 0; t < T; ++t) tm |= ((eq >> (t * k)) & km) ? 1u << t : 0u;
             s_list[uj] = ex;
             s_ucnt[uj] = __popcll(eq);
             s_uoff[uj] = less;
+            s_tmask[uj] = tm;
         }
         const int U = __popcll(firsts);
         int nc = 1;
@@ -455,7 +456,7 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
             if (u0 + u < u1) {
                 const float ge = __builtin_bit_cast(
                     float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gvv), u0 + u));
-                const int q0 = s_uoff[u0 + u] - pA, ne = s_ucnt[u0 + u];
+                const int q0 = s_uoff[u0 + u] - pA;
                 float sp0[R][NP > 0 ? NP : 1], sp1[R][NP > 0 ? NP : 1], s1[R];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
@@ -470,9 +471,16 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
                                               sh_single)
                                 : 0.0f;
                 }
-                for (int q = q0; q < q0 + ne; ++q) {
-                    const int t = s_tok[pA + q];
-                    const float wgt = s_wgt[pA + q] * ge;
+                // the expert's tokens in ascending order (its h rows q0, q0 + 1,
+                // ...): a static loop over the token index with wave-uniform
+                // branches, so each token's accumulator is a fixed register
+                const uint32_t tmask = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_tmask[u0 + u]);
+                int q = q0;
+#pragma unroll
+                for (int t = 0; t < MAXT; ++t) {
+                    if (!((tmask >> t) & 1u)) continue;
+                    const float wgt = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s_wgt[pA + q]))) * ge;
                     const uint4* hr = hs + q * I8 + l32;
                     float a[R];
 #pragma unroll
@@ -494,11 +502,8 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
                         for (int r = 0; r < R; ++r) a[r] += s1[r] * group_dot(cs[u][r], y0, y1);
                     }
 #pragma unroll
-                    for (int tt = 0; tt < MAXT; ++tt)
-                        if (tt == t) {
-#pragma unroll
-                            for (int r = 0; r < R; ++r) acc[tt][r] += wgt * a[r];
-                        }
+                    for (int r = 0; r < R; ++r) acc[t][r] += wgt * a[r];
+                    ++q;
                 }
             }
         }
