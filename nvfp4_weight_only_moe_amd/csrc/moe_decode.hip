@@ -112,39 +112,20 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
         }
         __syncthreads();
         if (wave == 0) {
-            // rank of each slot by (expert, flat index): expert bits from the
-            // top, the lanes still equal so far split into smaller and equal
-            int nbits = 1;
-            while ((1 << nbits) < E) ++nbits;
+            // rank of each slot by (expert, flat index)
             const bool valid = lane < slots;
             const int ex = valid ? s_ids[lane] : 0;
-            uint64_t eq = __ballot(valid), lessm = 0;
-            for (int b = nbits - 1; b >= 0; --b) {
-                const bool bit = (ex >> b) & 1;
-                const uint64_t B = __ballot(valid && bit);
-                if (bit) {
-                    lessm |= eq & ~B;
-                    eq &= B;
-                } else {
-                    eq &= ~B;
-                }
-            }
-            const int less = __popcll(lessm);
-            const uint64_t before = eq & lanemask_lt();
-            const bool first = valid && before == 0;
-            const uint64_t firsts = __ballot(first);
+            const SlotOrder o = wave_slot_order(ex, valid, E);
             if (valid) {
-                const int pos = less + __popcll(before);
-                s_pos[lane] = pos;
-                s_sorted[pos] = lane;
+                s_pos[lane] = o.pos;
+                s_sorted[o.pos] = lane;
             }
-            if (first) {
-                const int u = __popcll(firsts & lessm);
-                s_list[u] = ex;
-                s_ucnt[u] = __popcll(eq);
-                s_uoff[u] = less;
+            if (o.first) {
+                s_list[o.u] = ex;
+                s_ucnt[o.u] = __popcll(o.eq);
+                s_uoff[o.u] = o.less;
             }
-            if (lane == 0) s_U = __popcll(firsts);
+            if (lane == 0) s_U = o.U;
         }
         __syncthreads();
         U = s_U;
@@ -309,26 +290,12 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
         int ex = valid ? ids[lane] : 0;
         const float wv = valid ? topk_w[lane] : 0.0f;
         ex = min(max(ex, 0), E - 1);     // keeps every weight address inside the stacks
-        int nbits = 1;
-        while ((1 << nbits) < E) ++nbits;
-        uint64_t eq = __ballot(valid), lessm = 0;
-        for (int b = nbits - 1; b >= 0; --b) {
-            const bool bit = (ex >> b) & 1;
-            const uint64_t B = __ballot(valid && bit);
-            if (bit) {
-                lessm |= eq & ~B;
-                eq &= B;
-            } else {
-                eq &= ~B;
-            }
-        }
-        const int less = __popcll(lessm);                      // slots of smaller experts
-        const uint64_t before = eq & lanemask_lt();
-        const bool first = valid && before == 0;
-        const uint64_t firsts = __ballot(first);
-        const int uj = __popcll(firsts & lessm);               // rank of this slot's expert
+        const SlotOrder o = wave_slot_order(ex, valid, E);
+        const uint64_t eq = o.eq;
+        const int less = o.less, uj = o.u;                     // uj: rank of this slot's expert
+        const bool first = o.first;
         const int endj = less + __popcll(eq);                  // sorted end of this slot's expert
-        if (valid) s_wgt[less + __popcll(before)] = wv;
+        if (valid) s_wgt[o.pos] = wv;
         if (first) {
             // a token routes to an expert at most once: its slots t*k .. t*k+k-1
             uint32_t tm = 0;
@@ -339,7 +306,7 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
             s_uoff[uj] = less;
             s_tmask[uj] = tm;
         }
-        const int U = __popcll(firsts);
+        const int U = o.U;
         int nc = 1;
         if (U > kDownChunkExperts || slots > slot_cap) {
             // greedy: a chunk takes experts while it holds at most

@@ -11,6 +11,7 @@
 // histograms); positions come from ballots and prefix sums, so the result is
 // deterministic.
 //
+//   decode T (T * k <= 64, T <= 16; one workgroup):  k_route_tiny   (1 launch)
 //   small T (one workgroup):  k_route_small                 (1 launch)
 //   large T:  k_route_topk_hist -> k_route_colscan -> k_route_scatter
 #include <float.h>
@@ -130,6 +131,63 @@ __global__ void __launch_bounds__(kRT) k_route_small(const float* __restrict__ l
     block_scatter(s_ids, 0, n, s_off, E, s_hist, sorted_slots, slot_pos);
 }
 
+// Decode-sized route (T * k <= 64 slots, T <= 16 tokens): one wave per token
+// selects its top-k, then one wave orders all the slots at once by ballots on
+// the expert bits (wave_slot_order: the same order as the counting sort),
+// and every thread fills the per-expert counts and offsets of its experts by
+// a binary search over the touched experts (ascending).
+constexpr int kTinyMaxSlots = 64, kTinyMaxTokens = 16;
+
+template <int EPL>
+__global__ void __launch_bounds__(kTinyMaxTokens * kWave)
+k_route_tiny(const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
+             float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+             int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_pos) {
+    __shared__ int s_ids[kTinyMaxSlots];
+    __shared__ int s_list[kTinyMaxSlots], s_ucnt[kTinyMaxSlots], s_uoff[kTinyMaxSlots];
+    __shared__ int s_U;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int slots = T * k;
+    if (wave < T) {
+        int id;
+        float wt;
+        wave_topk_select<EPL>(logits + (int64_t)wave * E, E, k, id, wt);
+        if (lane < k) {
+            ids[wave * k + lane] = id;
+            w[wave * k + lane] = wt;
+            s_ids[wave * k + lane] = id;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const bool valid = lane < slots;
+        const int ex = valid ? s_ids[lane] : 0;
+        const SlotOrder o = wave_slot_order(ex, valid, E);
+        if (valid) {
+            sorted_slots[o.pos] = lane;
+            slot_pos[lane] = o.pos;
+        }
+        if (o.first) {
+            s_list[o.u] = ex;
+            s_ucnt[o.u] = __popcll(o.eq);
+            s_uoff[o.u] = o.less;
+        }
+        if (lane == 0) s_U = o.U;
+    }
+    __syncthreads();
+    const int U = s_U;
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+        int lo = 0, hi = U;                  // first touched expert >= e
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (s_list[mid] < e) lo = mid + 1;
+            else hi = mid;
+        }
+        if (e < E) counts[e] = lo < U && s_list[lo] == e ? s_ucnt[lo] : 0;
+        offsets[e] = lo < U ? s_uoff[lo] : slots;
+    }
+}
+
 // Large T, step 1: top-k per token and a per-workgroup expert histogram.
 __global__ void __launch_bounds__(kRT) k_route_topk_hist(const float* __restrict__ logits, int T, int E, int k,
                                                          int32_t* __restrict__ ids, float* __restrict__ w,
@@ -202,6 +260,20 @@ size_t route_workspace_bytes(int T, int E, int k) {
 
 moe_status launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_slots, int32_t* slot_pos, void* ws, hipStream_t s) {
+    if (T <= kTinyMaxTokens && T * k <= kTinyMaxSlots) {
+        const dim3 block(kWave * std::max(T, 4));
+        if (E <= 64) MOE_LAUNCH("route_tiny", k_route_tiny<1>, dim3(1), block, 0, s, logits, T, E, k, ids, w, counts,
+                                offsets, sorted_slots, slot_pos);
+        else if (E <= 128) MOE_LAUNCH("route_tiny", k_route_tiny<2>, dim3(1), block, 0, s, logits, T, E, k, ids, w,
+                                      counts, offsets, sorted_slots, slot_pos);
+        else if (E <= 256) MOE_LAUNCH("route_tiny", k_route_tiny<4>, dim3(1), block, 0, s, logits, T, E, k, ids, w,
+                                      counts, offsets, sorted_slots, slot_pos);
+        else if (E <= 512) MOE_LAUNCH("route_tiny", k_route_tiny<8>, dim3(1), block, 0, s, logits, T, E, k, ids, w,
+                                      counts, offsets, sorted_slots, slot_pos);
+        else MOE_LAUNCH("route_tiny", k_route_tiny<16>, dim3(1), block, 0, s, logits, T, E, k, ids, w, counts, offsets,
+                        sorted_slots, slot_pos);
+        return MOE_OK;
+    }
     if (T <= kTokensPerBlock) {
         MOE_LAUNCH("route_small", k_route_small, dim3(1), dim3(kRT), 0, s, logits, T, E, k, ids, w, counts,
                    offsets, sorted_slots, slot_pos);

@@ -98,6 +98,44 @@ __device__ __forceinline__ void wave_topk_select(const float* __restrict__ row, 
     w_out = topk_softmax(v, k);
 }
 
+// The order of the slots of a few tokens (one slot per lane, at most 64) by
+// (expert, flat slot index) -- the order of moe_route_topk's stable counting
+// sort -- from one ballot per expert bit: the lanes still equal so far split
+// into smaller and equal.  For a valid lane: pos = its sorted position,
+// eq = the lanes with its expert, less = how many slots hold smaller experts
+// (its expert's first position), first = the lowest lane of its expert,
+// u = its expert's rank among the touched experts; U = touched experts.
+struct SlotOrder {
+    uint64_t eq;
+    int less, pos, u, U;
+    bool first;
+};
+__device__ __forceinline__ SlotOrder wave_slot_order(int ex, bool valid, int E) {
+    int nbits = 1;
+    while ((1 << nbits) < E) ++nbits;
+    uint64_t eq = __ballot(valid), lessm = 0;
+    for (int b = nbits - 1; b >= 0; --b) {
+        const bool bit = (ex >> b) & 1;
+        const uint64_t B = __ballot(valid && bit);
+        if (bit) {
+            lessm |= eq & ~B;
+            eq &= B;
+        } else {
+            eq &= ~B;
+        }
+    }
+    SlotOrder o;
+    const uint64_t before = eq & lanemask_lt();
+    o.eq = eq;
+    o.less = __popcll(lessm);
+    o.pos = o.less + __popcll(before);
+    o.first = valid && before == 0;
+    const uint64_t firsts = __ballot(o.first);
+    o.u = __popcll(firsts & lessm);
+    o.U = __popcll(firsts);
+    return o;
+}
+
 // Rank of this lane's expert id among the valid lanes below it holding the
 // same id ("match any" from one ballot per id bit), and how many valid lanes
 // hold it.
