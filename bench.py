@@ -77,9 +77,9 @@ def packed_bytes(N, K):
 # profiles/traffic.json are only reported while these files are unchanged.
 KERNEL_SOURCES = {
     "dec_fused": ["decode_fused_kernel.h", "device_common.h", "route_common.h"],
-    "dec_gateup": ["moe_decode.hip", "device_common.h"],
+    "dec_gateup": ["moe_decode.hip", "device_common.h", "route_common.h"],
     "dec_gateup_route": ["moe_decode.hip", "device_common.h", "route_common.h"],
-    "dec_down": ["moe_decode.hip", "device_common.h"],
+    "dec_down": ["moe_decode.hip", "device_common.h", "route_common.h"],
     "gemm_gateup": ["moe_prefill.hip", "moe_prefill_pipe.hip", "device_common.h"],
     "gemm_down": ["moe_prefill.hip", "moe_prefill_pipe.hip", "device_common.h"],
 }

@@ -178,10 +178,12 @@ moe_status moe_w4a16_forward(const uint16_t *d_x, int32_t T, int32_t H, int32_t 
 /*
  * Route and layer in one call: moe_route_topk on d_logits (fp32 [T][E]),
  * storing every routing output exactly as moe_route_topk does, followed by
- * moe_w4a16_forward on that routing.  For decode shapes (1 <= T <= 8,
- * T*k <= 64, H % 1024 == 0, H <= 8192, I % 512 == 0, I <= 2048) everything
- * runs in a single kernel launch; otherwise it is the route kernels followed
- * by the forward kernels.  Same workspace as moe_w4a16_forward.
+ * moe_w4a16_forward on that routing.  Decode shapes (1 <= T <= 8, T*k <= 64,
+ * H % 1024 == 0, H <= 8192, I % 512 == 0, I <= 2048): with one token the
+ * gate/up kernel routes itself (two launches in all), with more tokens a
+ * single-workgroup route launch precedes the two decode kernels; other shapes
+ * run the route kernels followed by the forward kernels.  Same workspace as
+ * moe_w4a16_forward.
  */
 moe_status moe_w4a16_route_forward(const float *d_logits, const uint16_t *d_x,
                                    int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
