@@ -68,8 +68,12 @@ __device__ __forceinline__ bf16x8 decode8(uint32_t word, float s) {
     return __builtin_bit_cast(bf16x8, r);
 }
 
+// Workgroups per CU: the 32-row tiles fit three (164 VGPRs), which keeps
+// more weight loads in flight at the few rows per expert they serve.
+template <int BM> constexpr int gemm_wg_per_cu() { return BM >= 128 ? 1 : BM == 32 ? 3 : 2; }
+
 template <bool GATEUP, int BM>
-__global__ void __launch_bounds__(kGThreads, BM >= 128 ? 1 : 2) k_grouped_gemm(GemmParams P) {
+__global__ void __launch_bounds__(kGThreads, gemm_wg_per_cu<BM>()) k_grouped_gemm(GemmParams P) {
     constexpr int MS = BM / 16;                 // row subtiles
     constexpr int NS = 4;                       // column subtiles per wave
     constexpr int APASS = BM / 16;              // 16 rows per pass of the A loader
@@ -283,8 +287,8 @@ int num_cus() {
     return cached[dev];
 }
 
-int persistent_grid(int64_t tiles_ub) {
-    int64_t g = std::min<int64_t>(tiles_ub, (int64_t)num_cus() * 2);
+int persistent_grid(int64_t tiles_ub, int per_cu = 2) {
+    int64_t g = std::min<int64_t>(tiles_ub, (int64_t)num_cus() * per_cu);
     if (g >= 8) g = (g + 7) / 8 * 8;
     return (int)std::max<int64_t>(g, 1);
 }
@@ -296,7 +300,8 @@ moe_status launch_gemm(const GemmParams& P, int64_t slots, int E, hipStream_t s)
     if (allow_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm<GATEUP, BM>), shmem) != MOE_OK)
         return MOE_ERR_HIP;
     const char* name = GATEUP ? "gemm_gateup" : "gemm_down";
-    MOE_LAUNCH(name, (k_grouped_gemm<GATEUP, BM>), dim3(persistent_grid(tiles_ub)), dim3(kGThreads), shmem, s, P);
+    MOE_LAUNCH(name, (k_grouped_gemm<GATEUP, BM>), dim3(persistent_grid(tiles_ub, gemm_wg_per_cu<BM>())),
+               dim3(kGThreads), shmem, s, P);
     return MOE_OK;
 }
 
