@@ -305,10 +305,15 @@ moe_status launch_gemm(const GemmParams& P, int64_t slots, int E, hipStream_t s)
     return MOE_OK;
 }
 
+// Row tile by the mean rows per touched expert.  A weight tile is decoded once
+// per row tile, so tiles that hold a whole typical expert pay off even with
+// padding: at 1K tokens, top-8 of 256 (about 32 rows per expert, many with
+// 33-45) 64-row tiles take the layer from 1.61 to 1.32 ms against 32-row
+// tiles; 128-row tiles (one workgroup per CU) take 2.38 ms.
 template <bool GATEUP>
 moe_status launch_gemm_bm(const GemmParams& P, int64_t slots, int E, hipStream_t s) {
     const int64_t avg = slots / std::max<int64_t>(1, std::min<int64_t>(E, slots));
-    if (avg <= 32) return launch_gemm<GATEUP, 32>(P, slots, E, s);
+    if (avg <= 16) return launch_gemm<GATEUP, 32>(P, slots, E, s);
     if (avg <= 64) return launch_gemm<GATEUP, 64>(P, slots, E, s);
     return launch_gemm<GATEUP, 128>(P, slots, E, s);
 }
