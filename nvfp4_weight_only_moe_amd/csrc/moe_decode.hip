@@ -487,7 +487,7 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
 
 // Stages of two features per gate/up wave.  One token: two stages, so the
 // 768 workgroups of a 1536-feature, 8-expert layer are all resident at once
-// (143 VGPRs, 3 waves per SIMD).  More tokens: one stage; the grid is then
+// (145 VGPRs, 3 waves per SIMD).  More tokens: one stage; the grid is then
 // larger than one resident round anyway (a column per slot, most of them
 // empty after the lookup), and smaller workgroups start streaming sooner
 // (measured on MI355X at 8 tokens, 35 experts: 70 us against 75).

@@ -36,7 +36,11 @@ def test_route_workloads(cfg):
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 8, 1), (7, 64, 4), (64, 256, 8), (65, 256, 8), (300, 100, 3),
-                                   (129, 1024, 32), (50, 32, 32), (1000, 16, 2)])
+                                   (129, 1024, 32), (50, 32, 32), (1000, 16, 2),
+                                   # the decode-sized route (T <= 16, T * k <= 64) at its limits and
+                                   # for every logits-per-lane variant, and just past them
+                                   (16, 1024, 4), (2, 128, 32), (16, 100, 1), (3, 513, 5), (1, 1024, 8),
+                                   (17, 64, 2), (9, 256, 8)])
 def test_route_shapes(T, E, k):
     r = np.random.default_rng(T * 1000 + E)
     check_route(r.standard_normal((T, E)).astype(np.float32), k, f"random-{T}-{E}-{k}")
