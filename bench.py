@@ -22,7 +22,9 @@ HIP-event timed on its own stream), "cpu_baseline" (the CPU oracle timed on a
 bounded sample of the same workload), "step_spread" (p10/p50/p90 of the step
 time over the graph replays, timed after the measured steps) and
 "achievable_peaks" (a 1 GiB device copy and an 8192^3 bf16 GEMM by the
-torch/ROCm libraries, for context beside the spec peaks).
+torch/ROCm libraries, for context beside the spec peaks), with the host CPU
+model in "cpu_baseline" and the GPU clocks rocm-smi reports right after the
+timed region ("gpu_clocks_after_timing").
 """
 import argparse
 import json
@@ -293,6 +295,8 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 copies of 268435456 bytes (read 256 MiB, write 256 MiB each)")
 
+    clocks = gpu_clocks()
+
     # ---------------------------------------------------------------- achievable peaks
     # what plain library work reaches on this GPU, beside the spec peaks the
     # roofline uses: a 1 GiB device copy (read + write) and a bf16 GEMM
@@ -335,7 +339,7 @@ def main():
         "step_TFLOPs": round(step_tflops, 3), "step_mfma_frac": round(step_tflops / BF16_PEAK_TFLOPS, 5),
         "eager_ms_per_step": round(eager_ms, 6), "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 6),
         "per_kernel_us": per_kernel_us, "quantize_pack_ms_total": round(quant_ms, 2),
-        "step_spread": step_spread, "achievable_peaks": achievable,
+        "step_spread": step_spread, "achievable_peaks": achievable, "gpu_clocks_after_timing": clocks,
     }
     print(json.dumps(rec), flush=True)
 
@@ -375,7 +379,33 @@ def cpu_baseline(wl, logits, budget_s):
     return {"value": round(n_tok / per_run, 4), "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"{n_tok} token(s) of {wl.name}: route + SwiGLU FFN of {len(experts)} experts (dequantize "
                       f"+ fp64) + combine, {runs} runs, {t_total:.1f} s; expert quantization excluded",
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    """The host CPU's model name (the oracle baseline depends on it)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def gpu_clocks():
+    """Current shader and memory clocks as rocm-smi reports them right after the
+    timed region (context only; None when the tool is unavailable)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                             timeout=20).stdout
+        card = next(iter(json.loads(out).values()))
+        pick = lambda key: next((v for k, v in card.items() if key in k.lower()), None)
+        return {"sclk": pick("sclk"), "mclk": pick("mclk")}
+    except Exception:
+        return None
 
 
 if __name__ == "__main__":
