@@ -85,3 +85,24 @@ def moe_forward(x, layer, ids, weights, tokens=None, round_h_bf16=False):
         y = expert_ffn(x[toks], wg, wu, wd, round_h_bf16=round_h_bf16)
         out[toks] += weights[toks, slots][:, None] * y
     return out
+
+
+def linear(x, codes, scales, g):
+    """Dense projection in fp64: rows of ``x`` [M, K] times the transposed
+    dequantized [N, K] weight -> [M, N].  The dense layers (attention
+    linears, shared experts, lm_head) quantized to W4A16 NVFP4 like the
+    experts: "GLM-5.3-Flash-NVFP4-h -- W4A16 dense-side quantization", its
+    opening.  Pinned against an exactly representable weight and one-hot rows
+    (tests/test_oracle_moe.py)."""
+    w = np.asarray(dequantize(codes, scales, g), dtype=np.float64)
+    return np.asarray(x, dtype=np.float64) @ w.T
+
+
+def shared_expert_forward(x, layer, round_h_bf16=False):
+    """The shared expert: the SwiGLU FFN of expert 0 of ``layer`` for every
+    row, with weight 1 (the model's single shared expert runs for every token
+    beside the routed ones: "GLM-5.3-Flash on Blackwell", "The model loaded,
+    served an API, and produced garbage").  Equal to ``moe_forward`` with
+    E = 1, k = 1; pinned against a textbook SwiGLU MLP."""
+    wg, wu, wd = dequantize_expert(layer, 0)
+    return expert_ffn(x, wg, wu, wd, round_h_bf16=round_h_bf16)

@@ -321,3 +321,38 @@ def pin_magnitude(x, layer, ids, w, ms):
     rel = float(np.linalg.norm(out - ref) / np.linalg.norm(ref))
     assert rel < 0.25, rel
     return ratio, rel
+
+
+def pin_linear_exact(seed=0):
+    """The dense projection of an exactly representable weight equals x . W^T
+    computed from that weight directly (no dequantization involved), and
+    one-hot rows read out its columns (orientation and K indexing)."""
+    w, _, _, _ = representable_tensor(seed)
+    packed, scales, g = onv.quantize(w)
+    r = np.random.default_rng(seed + 1)
+    x = r.standard_normal((5, w.shape[1]))
+    ref = x @ w.astype(np.float64).T
+    got = omoe.linear(x, packed, scales, g)
+    assert got.shape == (5, w.shape[0])
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+    eye = np.eye(w.shape[1])
+    assert np.array_equal(omoe.linear(eye, packed, scales, g), w.astype(np.float64).T)
+
+
+def pin_shared_expert_textbook(seed=0, H=64, I=32, T=5):
+    """The shared expert is a plain SwiGLU MLP (torch fp64 on the CPU) and the
+    same as the routed layer with one expert, k = 1, weight 1."""
+    r = np.random.default_rng(seed)
+    ms = [(0.05 * r.standard_normal((1,) + s)).astype(np.float32)
+          for s in ((I, H), (I, H), (H, I))]
+    layer = _pack_layer(ms)
+    x = r.standard_normal((T, H)).astype(np.float32)
+    out = omoe.shared_expert_forward(x, layer)
+    wg, wu, wd = (torch.from_numpy(onv.dequantize(*[layer[p][i][0] for i in range(2)], layer[p][2][0])).double()
+                  for p in ("gate", "up", "down"))
+    xt = torch.from_numpy(x).double()
+    ref = torch.nn.functional.linear(
+        torch.nn.functional.silu(torch.nn.functional.linear(xt, wg)) * torch.nn.functional.linear(xt, wu), wd)
+    assert torch.allclose(torch.from_numpy(out), ref, rtol=1e-12, atol=1e-14)
+    routed = omoe.moe_forward(x, layer, np.zeros((T, 1), np.int32), np.ones((T, 1)))
+    assert np.array_equal(out, routed)

@@ -42,3 +42,12 @@ def test_token_subset_matches_full():
     # BLAS may block differently for fewer rows: equal up to fp64 rounding
     assert np.allclose(part[[0, 3, 11]], full[[0, 3, 11]], rtol=1e-13, atol=1e-16)
     assert not part[1].any()
+
+
+def test_linear_of_representable_weight():
+    pins.pin_linear_exact()
+    pins.pin_linear_exact(seed=3)
+
+
+def test_shared_expert_is_textbook_mlp():
+    pins.pin_shared_expert_textbook()
