@@ -196,6 +196,45 @@ moe_status moe_w4a16_route_forward(const float *d_logits, const uint16_t *d_x,
                                    hipStream_t stream);
 
 /*
+ * Dense NVFP4 weight-only projection of T tokens: out = bf16(g * x . Wd^T),
+ * Wd the dequantized [N][K] weight (E2M1 code * E4M3 group scale), g its
+ * FP32 global scale, products accumulated in fp32 and rounded once (the dense
+ * linears -- attention projections, shared experts, lm_head -- quantized to
+ * W4A16 NVFP4 like the routed experts: "GLM-5.3-Flash-NVFP4-h -- W4A16
+ * dense-side quantization", its opening).
+ *   d_x    bf16 [T][K];  w  an NVFP4 tensor with E = 1, N rows, K columns
+ *   d_out  bf16 [T][N] (must not overlap d_x or the workspace)
+ *   d_ws   workspace of moe_w4a16_linear_workspace_size(T, K, N) bytes
+ * Shapes: 1-8 tokens with K % 1024 == 0, K <= 8192 stream the weights once
+ * (the decode gate/up kernel with one stack); otherwise N % 256 == 0 and
+ * K % 128 == 0 (the grouped down GEMM with one expert, then the combine).
+ * MOE_ERR_SHAPE for other shapes.  T == 0 is a no-op.
+ */
+size_t moe_w4a16_linear_workspace_size(int32_t T, int32_t K, int32_t N);
+moe_status moe_w4a16_linear(const uint16_t *d_x, int32_t T, int32_t K, int32_t N,
+                            const moe_nvfp4_tensor *w, uint16_t *d_out,
+                            void *d_ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The shared expert: one always-on SwiGLU FFN applied to every token,
+ * out = bf16( g_d * h . Dd^T ), h = bf16( silu(g_g * x . Gd^T) * (g_u * x . Ud^T) )
+ * -- moe_w4a16_forward with E = 1, k = 1 and routing weight 1, with the same
+ * arithmetic (the model's single shared expert runs for every token beside
+ * the routed experts: "GLM-5.3-Flash on Blackwell", "The model loaded, served
+ * an API, and produced garbage"; quantized as in "GLM-5.3-Flash-NVFP4-h --
+ * W4A16 dense-side quantization"; the caller adds the two outputs).
+ *   gate, up  NVFP4 with E = 1, N = I, K = H;  down  E = 1, N = H, K = I
+ *   same shape rules as moe_w4a16_forward; d_ws of
+ *   moe_w4a16_shared_expert_workspace_size(T, H, I) bytes (no initialization
+ *   needed).  T == 0 is a no-op.
+ */
+size_t moe_w4a16_shared_expert_workspace_size(int32_t T, int32_t H, int32_t I);
+moe_status moe_w4a16_shared_expert(const uint16_t *d_x, int32_t T, int32_t H, int32_t I,
+                                   const moe_nvfp4_tensor *gate, const moe_nvfp4_tensor *up,
+                                   const moe_nvfp4_tensor *down, uint16_t *d_out,
+                                   void *d_ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Prepare a forward workspace for first use: zeroes its first 256 bytes, the
  * words through which the workgroups of the single-launch decode path hand
  * the SwiGLU output over to the down projection.  A workspace must start

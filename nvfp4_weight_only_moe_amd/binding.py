@@ -54,6 +54,10 @@ _SIGS = {
     "moe_w4a16_route_forward": (_I, [_P, _P, _I, _I, _I, _I, _I, _TP, _TP, _TP, _P, _P, _P, _P, _P, _P, _P, _P,
                                      _S, _P]),
     "moe_w4a16_workspace_init": (_I, [_P, _S, _P]),
+    "moe_w4a16_linear_workspace_size": (_S, [_I, _I, _I]),
+    "moe_w4a16_linear": (_I, [_P, _I, _I, _I, _TP, _P, _P, _S, _P]),
+    "moe_w4a16_shared_expert_workspace_size": (_S, [_I, _I, _I]),
+    "moe_w4a16_shared_expert": (_I, [_P, _I, _I, _I, _TP, _TP, _TP, _P, _P, _S, _P]),
     "moe_debug_set_decode_wait_limit": (None, [_I]),
     "moe_debug_set_decode_variant": (_I, [_I]),
     "moe_debug_set_prefill_variant": (_I, [_I]),
@@ -232,7 +236,8 @@ def moe_w4a16_forward(x_bits, gate, up, down, routing, out=None, ws=None, stream
 
 def moe_w4a16_route_forward(logits, x_bits, gate, up, down, k, routing=None, out=None, ws=None, stream=None):
     """Route (as moe_route_topk, outputs stored in `routing`) and run the
-    layer; decode shapes run as one kernel launch.  Returns (out, routing)."""
+    layer (with one token the gate/up kernel routes itself).  Returns
+    (out, routing)."""
     T, H = x_bits.shape
     E, I, _ = gate.shape
     assert logits.shape == (T, E)
@@ -260,3 +265,36 @@ def moe_profile_end(max_names=64):
     n = lib().moe_profile_end(ctypes.cast(names, ctypes.c_void_p), ctypes.cast(counts, ctypes.c_void_p),
                               ctypes.cast(ms, ctypes.c_void_p), max_names)
     return {names[i].value.decode(): (int(counts[i]), float(ms[i])) for i in range(n)}
+
+
+def moe_w4a16_linear(x_bits, w, out=None, ws=None, stream=None):
+    """Dense projection: bf16 bits [T, K] and an NVFP4 tensor with E = 1,
+    shape [1, N, K] -> bf16 bits [T, N] (int16 tensor)."""
+    T, K = x_bits.shape
+    E, N, K2 = w.shape
+    assert E == 1 and K2 == K
+    out = torch.empty((T, N), dtype=torch.int16, device=x_bits.device) if out is None else out
+    if ws is None:
+        ws = torch.empty((max(lib().moe_w4a16_linear_workspace_size(max(T, 1), K, N), 256),), dtype=torch.uint8,
+                         device=x_bits.device)
+    c = w.cstruct()
+    _check(lib().moe_w4a16_linear(_ptr(x_bits), T, K, N, ctypes.byref(c), _ptr(out), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "moe_w4a16_linear")
+    return out
+
+
+def moe_w4a16_shared_expert(x_bits, gate, up, down, out=None, ws=None, stream=None):
+    """The shared expert (one SwiGLU FFN for every token): bf16 bits [T, H]
+    and NVFP4 tensors with E = 1 -> bf16 bits [T, H] (int16 tensor)."""
+    T, H = x_bits.shape
+    E, I, _ = gate.shape
+    assert E == 1
+    out = torch.empty((T, H), dtype=torch.int16, device=x_bits.device) if out is None else out
+    if ws is None:
+        ws = torch.empty((max(lib().moe_w4a16_shared_expert_workspace_size(max(T, 1), H, I), 256),),
+                         dtype=torch.uint8, device=x_bits.device)
+    g, u, d = gate.cstruct(), up.cstruct(), down.cstruct()
+    _check(lib().moe_w4a16_shared_expert(_ptr(x_bits), T, H, I, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                                         _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_w4a16_shared_expert")
+    return out

@@ -201,6 +201,43 @@ FwdArgs make_args(const uint16_t* d_x, int32_t T, int32_t H, int32_t I, int32_t 
     return a;
 }
 
+// Single-expert entry points (dense linear, shared expert): the workspace
+// starts with the identity routing of T tokens (ids, weights, sorted slots
+// and slot positions: T each; counts and offsets: 1 and 2), then what the
+// chosen path needs.
+struct IdRoute {
+    int32_t* ids;
+    float* w;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* sorted;
+    int32_t* pos;
+    uint8_t* rest;
+};
+
+size_t id_route_bytes(int T) { return 4 * round_up((size_t)T * 4, kAlign) + kAlign; }
+
+IdRoute id_route_layout(void* d_ws, int T) {
+    uint8_t* p = static_cast<uint8_t*>(d_ws);
+    const size_t tb = round_up((size_t)T * 4, kAlign);
+    IdRoute r;
+    r.ids = reinterpret_cast<int32_t*>(p);
+    r.w = reinterpret_cast<float*>(p + tb);
+    r.sorted = reinterpret_cast<int32_t*>(p + 2 * tb);
+    r.pos = reinterpret_cast<int32_t*>(p + 3 * tb);
+    r.counts = reinterpret_cast<int32_t*>(p + 4 * tb);
+    r.offsets = r.counts + 4;
+    r.rest = p + 4 * tb + kAlign;
+    return r;
+}
+
+size_t linear_workspace_bytes(int T, int K, int N) {
+    (void)K;
+    return id_route_bytes(T) + round_up((size_t)T * N * sizeof(float), kAlign);
+}
+
+size_t shared_workspace_bytes(int T, int H, int I) { return id_route_bytes(T) + forward_workspace_bytes(T, H, I, 1, 1); }
+
 }  // namespace moe
 
 using namespace moe;
@@ -334,6 +371,83 @@ moe_status moe_w4a16_route_forward(const float* d_logits, const uint16_t* d_x, i
                       L.route, stream);
     if (st != MOE_OK) return st;
     return launch_decode_forward(a, L.sync, stream);
+}
+
+size_t moe_w4a16_linear_workspace_size(int32_t T, int32_t K, int32_t N) {
+    if (T <= 0 || K <= 0 || N <= 0) return 0;
+    return linear_workspace_bytes(T, K, N);
+}
+
+moe_status moe_w4a16_linear(const uint16_t* d_x, int32_t T, int32_t K, int32_t N, const moe_nvfp4_tensor* w,
+                            uint16_t* d_out, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+    if (T < 0 || K < 1 || N < 1) return MOE_ERR_SHAPE;
+    if ((int64_t)T * N > (int64_t)INT32_MAX / 2 || (int64_t)T * K > (int64_t)INT32_MAX / 2) return MOE_ERR_SHAPE;
+    if (!w) return MOE_ERR_INVALID_ARG;
+    moe_status st = check_tensor(w, 1, N, K);
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    const bool decode = linear_decode_supported(T, K, N);
+    if (!decode && (N % 256 || K % 128)) return MOE_ERR_SHAPE;   // grouped-GEMM tiles
+    if (!d_x || !d_out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(d_x) || !aligned16(d_out)) return MOE_ERR_ALIGN;
+    if (!d_ws) return MOE_ERR_WORKSPACE;
+    if (!aligned16(d_ws)) return MOE_ERR_ALIGN;
+    const size_t need = linear_workspace_bytes(T, K, N);
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    const size_t xb = (size_t)T * K * sizeof(uint16_t), ob = (size_t)T * N * sizeof(uint16_t);
+    if (ranges_overlap(d_x, xb, d_out, ob) || ranges_overlap(d_ws, need, d_out, ob) ||
+        ranges_overlap(d_ws, need, d_x, xb))
+        return MOE_ERR_INVALID_ARG;
+    const IdRoute R = id_route_layout(d_ws, T);
+    st = launch_route_identity(T, R.ids, R.w, R.counts, R.offsets, R.sorted, R.pos, stream);
+    if (st != MOE_OK) return st;
+    FwdArgs a{};
+    a.T = T; a.E = 1; a.k = 1;
+    a.gate = a.up = a.down = w;
+    a.ids = R.ids; a.topk_w = R.w; a.counts = R.counts; a.offsets = R.offsets;
+    a.sorted_slots = R.sorted; a.slot_pos = R.pos;
+    a.out = d_out;
+    if (decode) {
+        // the gate/up kernel's streaming with one stack: K = a.H, N = a.I, out through a.h
+        a.x = d_x; a.H = K; a.I = N; a.h = d_out;
+        return launch_linear_decode(a, stream);
+    }
+    // the down GEMM (x as its A operand, fp32 rows in the workspace) and the
+    // combine with one slot of weight 1
+    a.H = N; a.I = K;
+    a.h = const_cast<uint16_t*>(d_x);
+    a.y = reinterpret_cast<float*>(R.rest);
+    const bool pipe = prefill_pipe_supported(T, 1, N, K) && T >= kPipeMinRowsPerExpert;
+    st = pipe ? launch_down_pipe(a, stream) : launch_down_grouped(a, stream);
+    if (st != MOE_OK) return st;
+    return launch_combine(a, stream);
+}
+
+size_t moe_w4a16_shared_expert_workspace_size(int32_t T, int32_t H, int32_t I) {
+    if (T <= 0 || H <= 0 || I <= 0) return 0;
+    return shared_workspace_bytes(T, H, I);
+}
+
+moe_status moe_w4a16_shared_expert(const uint16_t* d_x, int32_t T, int32_t H, int32_t I,
+                                   const moe_nvfp4_tensor* gate, const moe_nvfp4_tensor* up,
+                                   const moe_nvfp4_tensor* down, uint16_t* d_out, void* d_ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+    if (T < 0) return MOE_ERR_SHAPE;
+    const size_t idb = T > 0 ? id_route_bytes(T) : 0;
+    if (T > 0 && d_ws && ws_bytes < idb) return MOE_ERR_WORKSPACE;
+    void* fws = d_ws && T > 0 ? static_cast<uint8_t*>(d_ws) + idb : d_ws;
+    moe_status st = check_forward(d_x, T, H, I, 1, 1, gate, up, down, nullptr, 0, d_out, fws,
+                                  T > 0 && d_ws ? ws_bytes - idb : ws_bytes);
+    if (st != MOE_OK || T == 0) return st;
+    const size_t xb = (size_t)T * H * sizeof(uint16_t);
+    if (ranges_overlap(d_ws, idb, d_x, xb) || ranges_overlap(d_ws, idb, d_out, xb)) return MOE_ERR_INVALID_ARG;
+    const IdRoute R = id_route_layout(d_ws, T);
+    st = launch_route_identity(T, R.ids, R.w, R.counts, R.offsets, R.sorted, R.pos, stream);
+    if (st != MOE_OK) return st;
+    const WsLayout L = ws_layout(R.rest, T, H, I, 1);
+    const FwdArgs a = make_args(d_x, T, H, I, 1, 1, gate, up, down, R.ids, R.w, R.counts, R.offsets, R.sorted,
+                                R.pos, d_out, L);
+    return decode_path_supported(T, 1, H, I) ? launch_forward_decode(a, stream) : launch_prefill(a, stream);
 }
 
 moe_status moe_w4a16_workspace_init(void* d_ws, size_t ws_bytes, hipStream_t stream) {

@@ -44,6 +44,9 @@ size_t route_workspace_bytes(int T, int E, int k);
 moe_status launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                         int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
                         int32_t* slot_pos, void* ws, hipStream_t s);
+// routing of one always-on expert (E = 1, k = 1, weight 1; sorted order = token order)
+moe_status launch_route_identity(int T, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                                 int32_t* sorted_slots, int32_t* slot_pos, hipStream_t s);
 
 // ---- forward (moe_decode.hip / moe_prefill.hip)
 struct FwdArgs {
@@ -79,6 +82,11 @@ moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s);
 moe_status launch_forward_decode_routed(const FwdArgs& a, const float* logits, int32_t* ids, float* w,
                                         int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* pos,
                                         hipStream_t s);
+// a dense projection out = bf16(g * x . W^T) of a few tokens by the gate/up
+// kernel's streaming with one weight stack (a.gate, E = 1, identity routing,
+// K = a.H, N = a.I, out written through a.h)
+bool linear_decode_supported(int T, int K, int N);
+moe_status launch_linear_decode(const FwdArgs& a, hipStream_t s);
 // moe_prefill.hip: register-staged grouped GEMMs and the combine
 moe_status launch_gateup_grouped(const FwdArgs& a, hipStream_t s);
 moe_status launch_down_grouped(const FwdArgs& a, hipStream_t s);

@@ -85,7 +85,9 @@ struct GuRoute {
     int32_t* slot_pos;          // [k]
 };
 
-template <int CPL, int RW, int EPL, bool ROUTE>
+// LINEAR: one weight stack only (gc/gs/gg), no SwiGLU: the row sums times
+// the global scale go out as bf16 (a dense projection; h is then the output).
+template <int CPL, int RW, int EPL, bool ROUTE, bool LINEAR = false>
 __global__ void __launch_bounds__(kGuThreads, RW == 1 ? 4 : 3)
 k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slots,
              const uint8_t* gc, const uint8_t* gs, const float* __restrict__ gg,
@@ -156,7 +158,8 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
     stage_x(0);
 
     const int nb = (blockIdx.x * kGuWaves + wave) * (2 * RW);   // first feature of this wave
-    const float g_gate = gg[e], g_up = ug[e];
+    const float g_gate = gg[e], g_up = LINEAR ? 0.0f : ug[e];
+    constexpr int kLoadsPerChunk = LINEAR ? 2 : 4;
     // the codes of all RW stages are requested at once and stay in registers
     // for every token of the expert
     uint4 cg[RW][CPL], cu[RW][CPL];
@@ -172,14 +175,16 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
         for (int j = 0; j < CPL; ++j) {
             const int q = lane + kWave * j;
             cg[r][j] = load_stream16(&gcr[q]);
-            cu[r][j] = load_stream16(&ucr[q]);
+            if constexpr (!LINEAR) cu[r][j] = load_stream16(&ucr[q]);
+            else cu[r][j] = make_uint4(0, 0, 0, 0);
             sg[r][j] = load_stream(&gsr[q]);
-            su[r][j] = load_stream(&usr[q]);
+            if constexpr (!LINEAR) su[r][j] = load_stream(&usr[q]);
+            else su[r][j] = 0;
         }
     }
     asm volatile("" ::: "memory");           // issue here, not at the first use
     // x rows (issued first) and stage 0's codes; later stages stay in flight
-    wait_vmem_at_most<4 * CPL * (RW - 1)>();
+    wait_vmem_at_most<kLoadsPerChunk * CPL * (RW - 1)>();
     __builtin_amdgcn_s_barrier();            // plain barrier: a fence would wait for every load
 
 #pragma unroll 1
@@ -211,8 +216,9 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
                     asm volatile("" : "+v"(u4.x), "+v"(u4.y), "+v"(u4.z), "+v"(u4.w));
                     const float dg_ = e4m3_byte_to_f32<0>(gsc) * group_dot(make_uint2(g4.x, g4.y), x0, x1) +
                                       e4m3_byte_to_f32<1>(gsc) * group_dot(make_uint2(g4.z, g4.w), x2, x3);
-                    const float du_ = e4m3_byte_to_f32<0>(usc) * group_dot(make_uint2(u4.x, u4.y), x0, x1) +
-                                      e4m3_byte_to_f32<1>(usc) * group_dot(make_uint2(u4.z, u4.w), x2, x3);
+                    const float du_ = LINEAR ? 0.0f
+                                             : e4m3_byte_to_f32<0>(usc) * group_dot(make_uint2(u4.x, u4.y), x0, x1) +
+                                                   e4m3_byte_to_f32<1>(usc) * group_dot(make_uint2(u4.z, u4.w), x2, x3);
                     a0 += second ? 0.0f : dg_;
                     a1 += second ? dg_ : 0.0f;
                     b0 += second ? 0.0f : du_;
@@ -220,11 +226,14 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
                 }
                 a0 = wave_sum_dpp(a0);
                 a1 = wave_sum_dpp(a1);
-                b0 = wave_sum_dpp(b0);
-                b1 = wave_sum_dpp(b1);
+                if constexpr (!LINEAR) {
+                    b0 = wave_sum_dpp(b0);
+                    b1 = wave_sum_dpp(b1);
+                }
                 if (lane < 2 && n + lane < I) {
                     const float av = lane ? a1 : a0, bv = lane ? b1 : b0;
-                    h[(int64_t)(p0 + qt) * I + n + lane] = f32_to_bf16_rne(silu(g_gate * av) * (g_up * bv));
+                    h[(int64_t)(p0 + qt) * I + n + lane] =
+                        LINEAR ? f32_to_bf16_rne(g_gate * av) : f32_to_bf16_rne(silu(g_gate * av) * (g_up * bv));
                 }
             }
         }
@@ -592,6 +601,49 @@ moe_status launch_decode_pair(const FwdArgs& a, const GuRoute* R, hipStream_t s)
 }  // namespace
 
 moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s) { return launch_decode_pair(a, nullptr, s); }
+
+namespace {
+
+template <int CPL, int RW>
+moe_status launch_linear_rw(const FwdArgs& a, hipStream_t s) {
+    const int rows_per_block = kGuWaves * 2 * RW;
+    const dim3 grid((a.I + rows_per_block - 1) / rows_per_block, 1);
+    const size_t shmem = (size_t)std::min(a.T, kXTokens) * a.H * sizeof(uint16_t);
+    auto kern = k_dec_gateup<CPL, RW, 4, false, true>;
+    if (allow_dynamic_lds(reinterpret_cast<const void*>(kern), shmem) != MOE_OK) return MOE_ERR_HIP;
+    const GuRoute none{};
+    MOE_LAUNCH("dec_linear", kern, grid, dim3(kGuThreads), shmem, s, a.x, a.H, a.I, 1, 1, a.T,
+               (const uint8_t*)a.gate->codes, (const uint8_t*)a.gate->scales, (const float*)a.gate->global_scale,
+               (const uint8_t*)a.gate->codes, (const uint8_t*)a.gate->scales, (const float*)a.gate->global_scale,
+               a.counts, a.sorted_slots, a.h, none);
+    return MOE_OK;
+}
+
+template <int CPL>
+moe_status launch_linear_cpl(const FwdArgs& a, hipStream_t s) {
+    return a.T == 1 ? launch_linear_rw<CPL, 2>(a, s) : launch_linear_rw<CPL, 1>(a, s);
+}
+
+}  // namespace
+
+bool linear_decode_supported(int T, int K, int N) {
+    return T >= 1 && T <= 8 && K % 1024 == 0 && K / 1024 >= 1 && K / 1024 <= 8 && N >= 2;
+}
+
+moe_status launch_linear_decode(const FwdArgs& a, hipStream_t s) {
+    if (a.E != 1 || a.k != 1 || !linear_decode_supported(a.T, a.H, a.I)) return MOE_ERR_UNSUPPORTED;
+    switch (a.H / 1024) {
+        case 1: return launch_linear_cpl<1>(a, s);
+        case 2: return launch_linear_cpl<2>(a, s);
+        case 3: return launch_linear_cpl<3>(a, s);
+        case 4: return launch_linear_cpl<4>(a, s);
+        case 5: return launch_linear_cpl<5>(a, s);
+        case 6: return launch_linear_cpl<6>(a, s);
+        case 7: return launch_linear_cpl<7>(a, s);
+        case 8: return launch_linear_cpl<8>(a, s);
+        default: return MOE_ERR_UNSUPPORTED;
+    }
+}
 
 moe_status launch_forward_decode_routed(const FwdArgs& a, const float* logits, int32_t* ids, float* w,
                                         int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* pos,

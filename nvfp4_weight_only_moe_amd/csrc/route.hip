@@ -249,6 +249,26 @@ __global__ void __launch_bounds__(kRT) k_route_scatter(const int32_t* __restrict
     block_scatter(ids, t0 * k, t1 * k, s_off, E, s_hist, sorted_slots, slot_pos);
 }
 
+// The routing of a single always-on expert (E = 1, k = 1, weight 1): every
+// token's one slot goes to expert 0 and the sorted order is the token order.
+__global__ void __launch_bounds__(256) k_route_identity(int T, int32_t* __restrict__ ids, float* __restrict__ w,
+                                                        int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ sorted_slots,
+                                                        int32_t* __restrict__ slot_pos) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < T) {
+        ids[i] = 0;
+        w[i] = 1.0f;
+        sorted_slots[i] = i;
+        slot_pos[i] = i;
+    }
+    if (i == 0) {
+        counts[0] = T;
+        offsets[0] = 0;
+        offsets[1] = T;
+    }
+}
+
 }  // namespace
 
 size_t route_workspace_bytes(int T, int E, int k) {
@@ -256,6 +276,13 @@ size_t route_workspace_bytes(int T, int E, int k) {
     if (T <= kTokensPerBlock) return 0;
     const int64_t B = (T + kTokensPerBlock - 1) / kTokensPerBlock;
     return (size_t)(B * E * sizeof(int32_t));
+}
+
+moe_status launch_route_identity(int T, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                                 int32_t* sorted_slots, int32_t* slot_pos, hipStream_t s) {
+    MOE_LAUNCH("route_identity", k_route_identity, dim3((std::max(T, 1) + 255) / 256), dim3(256), 0, s, T, ids, w,
+               counts, offsets, sorted_slots, slot_pos);
+    return MOE_OK;
 }
 
 moe_status launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* counts,
