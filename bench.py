@@ -68,6 +68,10 @@ def parse():
                     help="step = moe_route_topk + moe_w4a16_forward (two calls) instead of route_forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM counter scaling)")
+    ap.add_argument("--op", choices=("moe", "linear", "shared"), default="moe",
+                    help="moe: the routed layer (default); linear: a dense H x H NVFP4 projection "
+                         "(moe_w4a16_linear); shared: the shared expert (moe_w4a16_shared_expert), "
+                         "both at the workload's token count and shapes")
     return ap.parse_args()
 
 
@@ -114,7 +118,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer fits one MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+              "(the layer fits one MI355X)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -122,6 +126,8 @@ def main():
     from nvfp4_weight_only_moe_amd import workloads as wls
 
     wl = wls.WORKLOADS[args.config]
+    if args.op != "moe":
+        return bench_single(args, wl)
     B.moe_debug_set_decode_variant(args.decode_variant)
     B.moe_debug_set_prefill_variant(args.prefill_variant)
     decode = wl.T <= 8
@@ -380,6 +386,140 @@ def cpu_baseline(wl, logits, budget_s):
             "sample": f"{n_tok} token(s) of {wl.name}: route + SwiGLU FFN of {len(experts)} experts (dequantize "
                       f"+ fp64) + combine, {runs} runs, {t_total:.1f} s; expert quantization excluded",
             "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+
+
+def bench_single(args, wl):
+    """One always-on expert: the dense projection (K = N = H) or the shared
+    expert (H, I), at the workload's T.  Weights of several copies are
+    cycled (more than the 256 MB Infinity Cache holds) inside one HIP graph."""
+    import torch
+    from nvfp4_weight_only_moe_amd import binding as B
+    from nvfp4_weight_only_moe_amd import workloads as wls
+    from oracle import moe as omoe
+    import oracle
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    T, H, I = wl.T, wl.H, wl.I
+    decode = T <= 8
+    _, ms, xb, x, _ = wls.random_problem(7, T, H, H if args.op == "linear" else I, 1, 1)
+    if args.op == "linear":
+        ms = ms[:1]                                       # [1, H, H]
+        w_bytes = packed_bytes(H, H)
+    else:
+        w_bytes = 2 * packed_bytes(I, H) + packed_bytes(H, I)
+    base = [B.moe_w4a16_quantize_pack(torch.from_numpy(m).to(dev)) for m in ms]
+    copies = args.copies or (max(1, -(-(1 << 30) // w_bytes)) if decode else 1)
+    sets = [base] + [[B.NVFP4Tensor(t.codes.clone(), t.scales.clone(), t.global_scale.clone()) for t in base]
+                     for _ in range(copies - 1)]
+    x_d = torch.from_numpy(xb.view(np.int16)).to(dev)
+    out = torch.empty((T, H), dtype=torch.int16, device=dev)
+    if args.op == "linear":
+        ws = torch.empty((B.lib().moe_w4a16_linear_workspace_size(T, H, H),), dtype=torch.uint8, device=dev)
+        step = lambda i: B.moe_w4a16_linear(x_d, sets[i % copies][0], out=out, ws=ws)
+    else:
+        ws = torch.empty((B.lib().moe_w4a16_shared_expert_workspace_size(T, H, I),), dtype=torch.uint8, device=dev)
+        step = lambda i: B.moe_w4a16_shared_expert(x_d, *sets[i % copies], out=out, ws=ws)
+    steps = args.steps or (400 if decode else 20)
+    warmup = args.warmup if args.warmup is not None else (40 if decode else 3)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(n)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    eager_ms = timed(lambda n: [step(i) for i in range(n)], steps)
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step(0)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(copies):
+                step(i)
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if torch.equal(out, ref_out):
+            reps = max(1, steps // copies)
+            graph_ms = timed(lambda n: [g.replay() for _ in range(n)], reps) / copies
+            assert torch.equal(out, ref_out)
+        else:
+            log("graph replay output differs from eager: graph timing discarded")
+    ms_per_step = graph_ms if graph_ms is not None else eager_ms
+
+    B.moe_profile_begin(64 * max(steps, 1))
+    for i in range(steps):
+        step(i)
+    prof = B.moe_profile_end()
+    per_kernel_us = {k: round(v[1] / v[0] * 1e3, 3) for k, v in prof.items()}
+    dominant = max(prof, key=lambda k: prof[k][1])
+    dom_us = prof[dominant][1] / prof[dominant][0] * 1e3
+    if args.op == "linear":
+        work = {"dec_linear": ("hbm", w_bytes + T * H * 2 * 2), "gemm_down": ("mfma", 2.0 * T * H * H)}
+        alg_bytes, flops = w_bytes + T * H * 2 * 2, 2.0 * T * H * H
+    else:
+        work = {"dec_gateup": ("hbm", 2 * packed_bytes(I, H) + T * H * 2),
+                "dec_down": ("hbm", packed_bytes(H, I) + T * H * 2),
+                "gemm_gateup": ("mfma", 4.0 * T * H * I), "gemm_down": ("mfma", 2.0 * T * H * I)}
+        alg_bytes, flops = w_bytes + T * H * 2 * 2, 6.0 * T * H * I
+    bound, wk = work.get(dominant, ("hbm", alg_bytes))
+    if bound == "hbm":
+        ach = wk / (dom_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dominant,
+                    "kernel_avg_us": round(dom_us, 3), "algorithmic_bytes_per_launch": int(wk)}
+    else:
+        ach = wk / (dom_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": dominant,
+                    "kernel_avg_us": round(dom_us, 3), "algorithmic_flops_per_launch": wk}
+    cpu = None
+    if not args.no_cpu:
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            threads = 1
+        packed = [oracle.quantize_layer(m) for m in ms]
+        n_tok = min(T, 64)
+        t0 = time.perf_counter()
+        if args.op == "linear":
+            omoe.linear(x[:n_tok], packed[0][0][0], packed[0][1][0], packed[0][2][0])
+        else:
+            layer = {nm: p for nm, p in zip(("gate", "up", "down"), packed)}
+            omoe.shared_expert_forward(x[:n_tok], layer)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(n_tok / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n_tok} token(s): dequantize + fp64 {'projection' if args.op == 'linear' else 'SwiGLU FFN'}"
+                         f", 1 run, {dt:.1f} s; quantization excluded",
+               "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+    rec = {
+        "metric": METRIC, "value": round(T / (ms_per_step * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.op}-t{T}-h{H}" + (f"-n{H}" if args.op == "linear" else f"-i{I}"),
+                   "T": T, "H": H, "I": H if args.op == "linear" else I, "copies": copies,
+                   "hip_graph": graph_ms is not None},
+        "roofline": roofline, "cpu_baseline": cpu,
+        "step_algorithmic_GBps": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_TFLOPs": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "eager_ms_per_step": round(eager_ms, 6), "per_kernel_us": per_kernel_us,
+    }
+    print(json.dumps(rec), flush=True)
 
 
 def cpu_model():

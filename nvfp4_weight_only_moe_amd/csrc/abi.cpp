@@ -399,8 +399,6 @@ moe_status moe_w4a16_linear(const uint16_t* d_x, int32_t T, int32_t K, int32_t N
         ranges_overlap(d_ws, need, d_x, xb))
         return MOE_ERR_INVALID_ARG;
     const IdRoute R = id_route_layout(d_ws, T);
-    st = launch_route_identity(T, R.ids, R.w, R.counts, R.offsets, R.sorted, R.pos, stream);
-    if (st != MOE_OK) return st;
     FwdArgs a{};
     a.T = T; a.E = 1; a.k = 1;
     a.gate = a.up = a.down = w;
@@ -408,10 +406,13 @@ moe_status moe_w4a16_linear(const uint16_t* d_x, int32_t T, int32_t K, int32_t N
     a.sorted_slots = R.sorted; a.slot_pos = R.pos;
     a.out = d_out;
     if (decode) {
-        // the gate/up kernel's streaming with one stack: K = a.H, N = a.I, out through a.h
+        // the gate/up kernel's streaming with one stack (tokens in order, no
+        // routing arrays): K = a.H, N = a.I, out through a.h
         a.x = d_x; a.H = K; a.I = N; a.h = d_out;
         return launch_linear_decode(a, stream);
     }
+    st = launch_route_identity(T, R.ids, R.w, R.counts, R.offsets, R.sorted, R.pos, stream);
+    if (st != MOE_OK) return st;
     // the down GEMM (x as its A operand, fp32 rows in the workspace) and the
     // combine with one slot of weight 1
     a.H = N; a.I = K;

@@ -83,8 +83,8 @@ moe_status launch_forward_decode_routed(const FwdArgs& a, const float* logits, i
                                         int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* pos,
                                         hipStream_t s);
 // a dense projection out = bf16(g * x . W^T) of a few tokens by the gate/up
-// kernel's streaming with one weight stack (a.gate, E = 1, identity routing,
-// K = a.H, N = a.I, out written through a.h)
+// kernel's streaming with one weight stack (a.gate, E = 1, tokens in order --
+// no routing arrays are read -- K = a.H, N = a.I, out written through a.h)
 bool linear_decode_supported(int T, int K, int N);
 moe_status launch_linear_decode(const FwdArgs& a, hipStream_t s);
 // moe_prefill.hip: register-staged grouped GEMMs and the combine

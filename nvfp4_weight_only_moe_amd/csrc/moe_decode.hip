@@ -137,10 +137,15 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
         p0 = s_uoff[blockIdx.y];
         my_slot = lane < slots ? s_sorted[lane] : 0;
     } else {
-        my_slot = lane < slots ? sorted_slots[lane] : 0;   // slots <= 64 on this path
-        const ActiveExpert ae = nth_active_expert<EPL>(counts, E, blockIdx.y);
-        if (ae.e < 0) return;
-        e = ae.e; ne = ae.count; p0 = ae.first_row;
+        if constexpr (LINEAR) {     // one always-on stack: token order, no routing arrays
+            my_slot = lane;
+            e = 0; ne = slots; p0 = 0;
+        } else {
+            my_slot = lane < slots ? sorted_slots[lane] : 0;   // slots <= 64 on this path
+            const ActiveExpert ae = nth_active_expert<EPL>(counts, E, blockIdx.y);
+            if (ae.e < 0) return;
+            e = ae.e; ne = ae.count; p0 = ae.first_row;
+        }
     }
     const int H8 = H / 8;
     constexpr int ncr = 32 * CPL;            // 32-wide chunks per weight row (H = 1024 * CPL)
