@@ -529,7 +529,10 @@ moe_status launch_gateup_rw(const FwdArgs& a, const GuRoute* R, hipStream_t s) {
 
 template <int CPL>
 moe_status launch_gateup_gpl(const FwdArgs& a, const GuRoute* R, hipStream_t s) {
-    if (a.T == 1) return launch_gateup_rw<CPL, 2>(a, R, s);
+    // two stages per wave when enough expert columns fill the chip with
+    // resident workgroups; with one or two experts (a shared expert) one
+    // stage, which doubles the workgroups streaming at once
+    if (a.T == 1 && (R || std::min(a.T * a.k, a.E) >= 4)) return launch_gateup_rw<CPL, 2>(a, R, s);
     const GuRoute none{};     // the in-kernel route is for one token only
     return a.E <= 256 ? launch_gateup_epl<CPL, 1, 4, false>(a, none, s) : launch_gateup_epl<CPL, 1, 16, false>(a, none, s);
 }
@@ -626,7 +629,7 @@ moe_status launch_linear_rw(const FwdArgs& a, hipStream_t s) {
 
 template <int CPL>
 moe_status launch_linear_cpl(const FwdArgs& a, hipStream_t s) {
-    return a.T == 1 ? launch_linear_rw<CPL, 2>(a, s) : launch_linear_rw<CPL, 1>(a, s);
+    return launch_linear_rw<CPL, 1>(a, s);   // one stack: one stage per wave, twice the workgroups
 }
 
 }  // namespace
