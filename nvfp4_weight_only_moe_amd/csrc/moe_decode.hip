@@ -56,6 +56,8 @@ constexpr int kDownAhead = 3;           // experts' down codes in flight ahead o
 constexpr int kDownRows = 1;            // output rows per half-wave (more: fewer waves, measured slower)
 constexpr int kDecodeMaxSlots = 64;     // T * k on the decode path
 constexpr int kXTokens = 2;             // activation rows staged in LDS at a time (gate/up)
+constexpr int kXTokensLinear = 4;       // the same for the one-stack projection (few registers, 4 per CU fit)
+template <bool LINEAR> constexpr int x_stage_tokens() { return LINEAR ? kXTokensLinear : kXTokens; }
 
 // A wave computes two consecutive output features n, n + 1 per stage.  Their
 // gate rows are one contiguous run of H codes (H / 16 chunks of 32), as are
@@ -94,7 +96,8 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
              const uint8_t* uc, const uint8_t* us, const float* __restrict__ ug,
              const int32_t* __restrict__ counts, const int32_t* __restrict__ sorted_slots,
              uint16_t* __restrict__ h, const GuRoute R) {
-    extern __shared__ uint4 xs[];   // [kXTokens][H / 8]
+    constexpr int kXT = x_stage_tokens<LINEAR>();
+    extern __shared__ uint4 xs[];   // [kXT][H / 8]
     __shared__ int s_ids[kDecodeMaxSlots], s_pos[kDecodeMaxSlots], s_sorted[kDecodeMaxSlots];
     __shared__ int s_list[kDecodeMaxSlots], s_ucnt[kDecodeMaxSlots], s_uoff[kDecodeMaxSlots];
     __shared__ int s_U;
@@ -150,10 +153,10 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
     const int H8 = H / 8;
     constexpr int ncr = 32 * CPL;            // 32-wide chunks per weight row (H = 1024 * CPL)
 
-    // activation rows of up to kXTokens tokens at a time live in LDS
+    // activation rows of up to kXT tokens at a time live in LDS
     const int nchunk = H8 / 64;              // H % 512 == 0 on this path
     auto stage_x = [&](int q0) {
-        for (int q = q0; q < min(ne, q0 + kXTokens); ++q) {
+        for (int q = q0; q < min(ne, q0 + kXT); ++q) {
             const int t = __builtin_amdgcn_readlane(my_slot, p0 + q) / k;
             const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * H);
             for (int c = wave; c < nchunk; c += kGuWaves)
@@ -193,7 +196,7 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
     __builtin_amdgcn_s_barrier();            // plain barrier: a fence would wait for every load
 
 #pragma unroll 1
-    for (int q0 = 0; q0 < ne; q0 += kXTokens) {
+    for (int q0 = 0; q0 < ne; q0 += kXT) {
         if (q0 > 0) {                        // next tokens: restage x
             __syncthreads();
             stage_x(q0);
@@ -204,7 +207,7 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
         for (int r = 0; r < RW; ++r) {
             const int n = nb + 2 * r;
 #pragma unroll 1
-            for (int qt = q0; qt < min(ne, q0 + kXTokens); ++qt) {
+            for (int qt = q0; qt < min(ne, q0 + kXT); ++qt) {
                 const uint4* xq = xs + (qt - q0) * H8;
                 float a0 = 0.0f, a1 = 0.0f, b0 = 0.0f, b1 = 0.0f;
 #pragma unroll
@@ -616,7 +619,7 @@ template <int CPL, int RW>
 moe_status launch_linear_rw(const FwdArgs& a, hipStream_t s) {
     const int rows_per_block = kGuWaves * 2 * RW;
     const dim3 grid((a.I + rows_per_block - 1) / rows_per_block, 1);
-    const size_t shmem = (size_t)std::min(a.T, kXTokens) * a.H * sizeof(uint16_t);
+    const size_t shmem = (size_t)std::min(a.T, kXTokensLinear) * a.H * sizeof(uint16_t);
     auto kern = k_dec_gateup<CPL, RW, 4, false, true>;
     if (allow_dynamic_lds(reinterpret_cast<const void*>(kern), shmem) != MOE_OK) return MOE_ERR_HIP;
     const GuRoute none{};
