@@ -152,3 +152,48 @@ def test_prefill_variant_hook(L):
     assert L.moe_debug_set_prefill_variant(0) == 0
     assert L.moe_debug_set_prefill_variant(1) == 0
     assert L.moe_debug_set_prefill_variant(2) == 0
+
+
+def lin(L, x=A, T=4, K=1024, N=512, w=None, out=A + 0x800000, ws=A + 0x900000, ws_bytes=1 << 30):
+    w = w or T_(1, N, K, A + 0x1000000)
+    return L.moe_w4a16_linear(x, T, K, N, ctypes.byref(w), out, ws, ws_bytes, None)
+
+
+def test_linear_argument_errors(L):
+    assert lin(L, T=0) == b.MOE_OK                                 # no-op, any path
+    assert lin(L, T=0, N=100, K=1536) == b.MOE_OK
+    assert lin(L, T=-1) == -2                                      # SHAPE
+    assert lin(L, K=0) == -2
+    assert lin(L, w=T_(2, 512, 1024)) == -2                        # a stack of 2: not E = 1
+    assert lin(L, w=T_(1, 256, 1024)) == -2                        # N does not match the tensor
+    assert lin(L, T=2, K=1536, N=100) == -2                        # GEMM path needs N % 256
+    assert lin(L, T=9, K=1000, N=512,
+               w=T_(1, 512, 1000)) != b.MOE_OK                     # K not a multiple of 32 (tensor)
+    assert lin(L, x=0) == -1                                       # null x
+    assert lin(L, x=A + 4) == -3                                   # misaligned
+    assert lin(L, out=A) == -1                                     # out overlaps x
+    assert lin(L, ws=0) == -7                                      # no workspace
+    assert lin(L, ws_bytes=16) == -7                               # workspace too small
+    assert L.moe_w4a16_linear_workspace_size(4, 1024, 512) >= 4 * 512 * 4
+    assert L.moe_w4a16_linear_workspace_size(0, 1024, 512) == 0
+
+
+def shx(L, x=A, T=4, H=256, I=128, out=A + 0x800000, ws=A + 0x900000, ws_bytes=1 << 30, gate=None):
+    gate = gate or T_(1, I, H)
+    up = T_(1, I, H, A + 0x1000000)
+    down = T_(1, H, I, A + 0x2000000)
+    return L.moe_w4a16_shared_expert(x, T, H, I, ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down),
+                                     out, ws, ws_bytes, None)
+
+
+def test_shared_expert_argument_errors(L):
+    assert shx(L, T=0) == b.MOE_OK
+    assert shx(L, T=-1) == -2
+    assert shx(L, H=200) == -2                                     # H % 256
+    assert shx(L, gate=T_(2, 128, 256)) == -2                      # not one expert
+    assert shx(L, x=0) == -1
+    assert shx(L, out=A) == -1                                     # out aliases x
+    assert shx(L, ws=0) == -7
+    assert shx(L, ws_bytes=1024) == -7
+    need = L.moe_w4a16_shared_expert_workspace_size(4, 256, 128)
+    assert need > L.moe_w4a16_workspace_size(4, 256, 128, 1, 1)  # identity routing in front
