@@ -226,7 +226,9 @@ moe_status moe_w4a16_linear(const uint16_t *d_x, int32_t T, int32_t K, int32_t N
  *   gate, up  NVFP4 with E = 1, N = I, K = H;  down  E = 1, N = H, K = I
  *   same shape rules as moe_w4a16_forward; d_ws of
  *   moe_w4a16_shared_expert_workspace_size(T, H, I) bytes (no initialization
- *   needed).  T == 0 is a no-op.
+ *   needed).  T == 0 is a no-op.  With 1-8 tokens the decode kernels run in a
+ *   one-expert mode that reads no routing arrays (two launches); with more,
+ *   an identity routing is written to d_ws first and the prefill kernels run.
  */
 size_t moe_w4a16_shared_expert_workspace_size(int32_t T, int32_t H, int32_t I);
 moe_status moe_w4a16_shared_expert(const uint16_t *d_x, int32_t T, int32_t H, int32_t I,

@@ -443,12 +443,14 @@ moe_status moe_w4a16_shared_expert(const uint16_t* d_x, int32_t T, int32_t H, in
     const size_t xb = (size_t)T * H * sizeof(uint16_t);
     if (ranges_overlap(d_ws, idb, d_x, xb) || ranges_overlap(d_ws, idb, d_out, xb)) return MOE_ERR_INVALID_ARG;
     const IdRoute R = id_route_layout(d_ws, T);
-    st = launch_route_identity(T, R.ids, R.w, R.counts, R.offsets, R.sorted, R.pos, stream);
-    if (st != MOE_OK) return st;
     const WsLayout L = ws_layout(R.rest, T, H, I, 1);
     const FwdArgs a = make_args(d_x, T, H, I, 1, 1, gate, up, down, R.ids, R.w, R.counts, R.offsets, R.sorted,
                                 R.pos, d_out, L);
-    return decode_path_supported(T, 1, H, I) ? launch_forward_decode(a, stream) : launch_prefill(a, stream);
+    // decode shapes: the decode kernels in their one-expert mode read no routing arrays
+    if (decode_path_supported(T, 1, H, I)) return launch_forward_decode_one(a, stream);
+    st = launch_route_identity(T, R.ids, R.w, R.counts, R.offsets, R.sorted, R.pos, stream);
+    if (st != MOE_OK) return st;
+    return launch_prefill(a, stream);
 }
 
 moe_status moe_w4a16_workspace_init(void* d_ws, size_t ws_bytes, hipStream_t stream) {

@@ -76,6 +76,9 @@ moe_status launch_decode_fused(const FwdArgs& a, const float* logits, int32_t* i
 moe_status launch_decode_two(const FwdArgs& a, hipStream_t s);
 moe_status launch_zero_words(uint32_t* p, int n, hipStream_t s);
 moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s);
+// the same kernels for one always-on expert (E = 1, k = 1, weight 1, tokens
+// in order): no routing arrays are read
+moe_status launch_forward_decode_one(const FwdArgs& a, hipStream_t s);
 // the same two kernels with the routing computed by the gate/up kernel from
 // the logits (it stores the routing outputs, which the down kernel reads);
 // one token only (MOE_ERR_UNSUPPORTED otherwise)

@@ -89,7 +89,9 @@ struct GuRoute {
 
 // LINEAR: one weight stack only (gc/gs/gg), no SwiGLU: the row sums times
 // the global scale go out as bf16 (a dense projection; h is then the output).
-template <int CPL, int RW, int EPL, bool ROUTE, bool LINEAR = false>
+// ONE: a single always-on expert (a shared expert): tokens in order, no
+// routing arrays read (LINEAR implies it).
+template <int CPL, int RW, int EPL, bool ROUTE, bool LINEAR = false, bool ONE = false>
 __global__ void __launch_bounds__(kGuThreads, RW == 1 ? 4 : 3)
 k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slots,
              const uint8_t* gc, const uint8_t* gs, const float* __restrict__ gg,
@@ -140,7 +142,7 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
         p0 = s_uoff[blockIdx.y];
         my_slot = lane < slots ? s_sorted[lane] : 0;
     } else {
-        if constexpr (LINEAR) {     // one always-on stack: token order, no routing arrays
+        if constexpr (LINEAR || ONE) {   // one always-on stack: token order, no routing arrays
             my_slot = lane;
             e = 0; ne = slots; p0 = 0;
         } else {
@@ -277,7 +279,8 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
 }
 
 // GPL2 = 16-groups per half-wave lane along I (I = 512 * GPL2); MAXT tokens.
-template <int GPL2, int MAXT>
+// ONE: a single always-on expert, weight 1 (ids and weights are not read).
+template <int GPL2, int MAXT, bool ONE = false>
 __global__ void __launch_bounds__(kDownMaxWaves * kWave)
 k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
            const uint8_t* dc, const uint8_t* ds, const float* __restrict__ dg,
@@ -304,8 +307,12 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
     // It then groups the touched experts (ascending) into chunks.
     if (wave == 0) {
         const bool valid = lane < slots;
-        int ex = valid ? ids[lane] : 0;
-        const float wv = valid ? topk_w[lane] : 0.0f;
+        int ex = 0;
+        float wv = valid ? 1.0f : 0.0f;
+        if constexpr (!ONE) {
+            ex = valid ? ids[lane] : 0;
+            wv = valid ? topk_w[lane] : 0.0f;
+        }
         ex = min(max(ex, 0), E - 1);     // keeps every weight address inside the stacks
         const SlotOrder o = wave_slot_order(ex, valid, E);
         const uint64_t eq = o.eq;
@@ -508,12 +515,12 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
 // larger than one resident round anyway (a column per slot, most of them
 // empty after the lookup), and smaller workgroups start streaming sooner
 // (measured on MI355X at 8 tokens, 35 experts: 70 us against 75).
-template <int CPL, int RW, int EPL, bool ROUTE>
+template <int CPL, int RW, int EPL, bool ROUTE, bool ONE = false>
 moe_status launch_gateup_epl(const FwdArgs& a, const GuRoute& R, hipStream_t s) {
     const int rows_per_block = kGuWaves * 2 * RW;
     const dim3 grid((a.I + rows_per_block - 1) / rows_per_block, std::min(a.T * a.k, a.E));
     const size_t shmem = (size_t)std::min(a.T, kXTokens) * a.H * sizeof(uint16_t);
-    auto kern = k_dec_gateup<CPL, RW, EPL, ROUTE>;
+    auto kern = k_dec_gateup<CPL, RW, EPL, ROUTE, false, ONE>;
     if (allow_dynamic_lds(reinterpret_cast<const void*>(kern), shmem) != MOE_OK) return MOE_ERR_HIP;
     MOE_LAUNCH(ROUTE ? "dec_gateup_route" : "dec_gateup", kern, grid, dim3(kGuThreads), shmem, s, a.x, a.H, a.I,
                a.E, a.k, a.T * a.k, (const uint8_t*)a.gate->codes, (const uint8_t*)a.gate->scales,
@@ -531,7 +538,8 @@ moe_status launch_gateup_rw(const FwdArgs& a, const GuRoute* R, hipStream_t s) {
 }
 
 template <int CPL>
-moe_status launch_gateup_gpl(const FwdArgs& a, const GuRoute* R, hipStream_t s) {
+moe_status launch_gateup_gpl(const FwdArgs& a, const GuRoute* R, hipStream_t s, bool one) {
+    if (one) return launch_gateup_epl<CPL, 1, 4, false, true>(a, GuRoute{}, s);
     // two stages per wave when enough expert columns fill the chip with
     // resident workgroups; with one or two experts (a shared expert) one
     // stage, which doubles the workgroups streaming at once
@@ -554,27 +562,32 @@ int down_waves_per_block(int H) {
 // LDS budget (an expert's rows, at most T <= 8, always fit: I <= 2048)
 constexpr int kDownLdsBudget = 128 * 1024;
 
-template <int GPL2, int MAXT>
+template <int GPL2, int MAXT, bool ONE>
 moe_status launch_down_t(const FwdArgs& a, hipStream_t s) {
     const int waves = down_waves_per_block(a.H);
     const int rows_per_block = 2 * kDownRows * waves;
     const int slot_cap = std::min({down_chunk_slots<MAXT>(), a.T * a.k, kDownLdsBudget / (a.I * 2)});
     const size_t shmem = (size_t)slot_cap * a.I * sizeof(uint16_t);
-    if (allow_dynamic_lds(reinterpret_cast<const void*>(&k_dec_down<GPL2, MAXT>), shmem) != MOE_OK)
+    if (allow_dynamic_lds(reinterpret_cast<const void*>(&k_dec_down<GPL2, MAXT, ONE>), shmem) != MOE_OK)
         return MOE_ERR_HIP;
-    MOE_LAUNCH("dec_down", (k_dec_down<GPL2, MAXT>), dim3((a.H + rows_per_block - 1) / rows_per_block),
+    MOE_LAUNCH("dec_down", (k_dec_down<GPL2, MAXT, ONE>), dim3((a.H + rows_per_block - 1) / rows_per_block),
                dim3(waves * kWave), shmem, s, (const uint16_t*)a.h, a.T, a.H, a.I, a.E, a.k,
                (const uint8_t*)a.down->codes, (const uint8_t*)a.down->scales, (const float*)a.down->global_scale,
                a.ids, a.topk_w, a.out, slot_cap);
     return MOE_OK;
 }
 
+template <int GPL2, bool ONE>
+moe_status launch_down_tt(const FwdArgs& a, hipStream_t s) {
+    if (a.T <= 1) return launch_down_t<GPL2, 1, ONE>(a, s);
+    if (a.T <= 2) return launch_down_t<GPL2, 2, ONE>(a, s);
+    if (a.T <= 4) return launch_down_t<GPL2, 4, ONE>(a, s);
+    return launch_down_t<GPL2, 8, ONE>(a, s);
+}
+
 template <int GPL2>
-moe_status launch_down_gpl(const FwdArgs& a, hipStream_t s) {
-    if (a.T <= 1) return launch_down_t<GPL2, 1>(a, s);
-    if (a.T <= 2) return launch_down_t<GPL2, 2>(a, s);
-    if (a.T <= 4) return launch_down_t<GPL2, 4>(a, s);
-    return launch_down_t<GPL2, 8>(a, s);
+moe_status launch_down_gpl(const FwdArgs& a, hipStream_t s, bool one) {
+    return one ? launch_down_tt<GPL2, true>(a, s) : launch_down_tt<GPL2, false>(a, s);
 }
 
 }  // namespace
@@ -586,25 +599,25 @@ bool decode_path_supported(int T, int k, int H, int I) {
 
 namespace {
 
-moe_status launch_decode_pair(const FwdArgs& a, const GuRoute* R, hipStream_t s) {
+moe_status launch_decode_pair(const FwdArgs& a, const GuRoute* R, hipStream_t s, bool one = false) {
     moe_status st;
     switch (a.H / 1024) {
-        case 1: st = launch_gateup_gpl<1>(a, R, s); break;
-        case 2: st = launch_gateup_gpl<2>(a, R, s); break;
-        case 3: st = launch_gateup_gpl<3>(a, R, s); break;
-        case 4: st = launch_gateup_gpl<4>(a, R, s); break;
-        case 5: st = launch_gateup_gpl<5>(a, R, s); break;
-        case 6: st = launch_gateup_gpl<6>(a, R, s); break;
-        case 7: st = launch_gateup_gpl<7>(a, R, s); break;
-        case 8: st = launch_gateup_gpl<8>(a, R, s); break;
+        case 1: st = launch_gateup_gpl<1>(a, R, s, one); break;
+        case 2: st = launch_gateup_gpl<2>(a, R, s, one); break;
+        case 3: st = launch_gateup_gpl<3>(a, R, s, one); break;
+        case 4: st = launch_gateup_gpl<4>(a, R, s, one); break;
+        case 5: st = launch_gateup_gpl<5>(a, R, s, one); break;
+        case 6: st = launch_gateup_gpl<6>(a, R, s, one); break;
+        case 7: st = launch_gateup_gpl<7>(a, R, s, one); break;
+        case 8: st = launch_gateup_gpl<8>(a, R, s, one); break;
         default: return MOE_ERR_UNSUPPORTED;
     }
     if (st != MOE_OK) return st;
     switch (a.I / 512) {
-        case 1: return launch_down_gpl<1>(a, s);
-        case 2: return launch_down_gpl<2>(a, s);
-        case 3: return launch_down_gpl<3>(a, s);
-        case 4: return launch_down_gpl<4>(a, s);
+        case 1: return launch_down_gpl<1>(a, s, one);
+        case 2: return launch_down_gpl<2>(a, s, one);
+        case 3: return launch_down_gpl<3>(a, s, one);
+        case 4: return launch_down_gpl<4>(a, s, one);
         default: return MOE_ERR_UNSUPPORTED;
     }
 }
@@ -612,6 +625,11 @@ moe_status launch_decode_pair(const FwdArgs& a, const GuRoute* R, hipStream_t s)
 }  // namespace
 
 moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s) { return launch_decode_pair(a, nullptr, s); }
+
+moe_status launch_forward_decode_one(const FwdArgs& a, hipStream_t s) {
+    if (a.E != 1 || a.k != 1) return MOE_ERR_UNSUPPORTED;
+    return launch_decode_pair(a, nullptr, s, true);
+}
 
 namespace {
 
