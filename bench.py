@@ -23,7 +23,7 @@ bounded sample of the same workload), "step_spread" (p10/p50/p90 of the step
 time over the graph replays, timed after the measured steps) and
 "achievable_peaks" (a 1 GiB device copy and an 8192^3 bf16 GEMM by the
 torch/ROCm libraries, for context beside the spec peaks), with the host CPU
-model in "cpu_baseline" and the GPU clocks rocm-smi reports right after the
+model in "cpu_baseline" and the GPU clocks the driver reports right after the
 timed region ("gpu_clocks_after_timing").
 """
 import argparse
@@ -535,17 +535,25 @@ def cpu_model():
 
 
 def gpu_clocks():
-    """Current shader and memory clocks as rocm-smi reports them right after the
-    timed region (context only; None when the tool is unavailable)."""
-    import subprocess
+    """Current shader and memory clocks of cuda:0 right after the timed region,
+    read from the amdgpu driver's DPM tables in sysfs (the entry marked '*'),
+    matched to the device by PCI address; context only, None when unreadable.
+    Reading files keeps the GPU process from starting any other program."""
+    import glob
+    import torch
     try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
-                             timeout=20).stdout
-        card = next(iter(json.loads(out).values()))
-        pick = lambda key: next((v for k, v in card.items() if key in k.lower()), None)
-        return {"sclk": pick("sclk"), "mclk": pick("mclk")}
+        p = torch.cuda.get_device_properties(0)
+        bdf = "%04x:%02x:%02x." % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+        for dev in glob.glob("/sys/class/drm/card*/device"):
+            if not os.path.basename(os.path.realpath(dev)).startswith(bdf):
+                continue
+            def cur(name):
+                with open(os.path.join(dev, name)) as f:
+                    return next((ln.split(":", 1)[1].replace("*", "").strip() for ln in f if "*" in ln), None)
+            return {"sclk": cur("pp_dpm_sclk"), "mclk": cur("pp_dpm_mclk")}
     except Exception:
-        return None
+        pass
+    return None
 
 
 if __name__ == "__main__":
