@@ -52,6 +52,9 @@ SHARED_CASES = [
     (1, 1024, 512, 21), (4, 1024, 512, 22), (8, 2048, 1024, 23),    # decode kernels
     (40, 1024, 512, 24), (300, 1024, 512, 25),                       # grouped / pipelined GEMMs
     (1, 5120, 1536, 26), (8, 5120, 1536, 27),                        # the model's shapes
+    # one-expert decode mode across its templates: H / 1024 = 3, 4, 8 and
+    # I / 512 = 2, 3, 4 with 2-, 4- and 8-token blocks
+    (2, 3072, 2048, 28), (3, 4096, 1024, 29), (5, 8192, 1536, 30),
 ]
 
 
@@ -65,10 +68,11 @@ def test_shared_expert_parity(T, H, I, seed):
     compare_out(bf16_bits_to_f64(out), ref, f"shared expert T={T} H={H} I={I}")
 
 
-def test_shared_expert_matches_one_expert_forward():
+@pytest.mark.parametrize("T,H,I", [(6, 1024, 512), (1, 5120, 1536), (8, 2048, 2048), (20, 1024, 512)])
+def test_shared_expert_matches_one_expert_forward(T, H, I):
     """The entry point is the routed forward with one expert, k = 1, weight 1:
-    the same kernels, the same bits."""
-    T, H, I = 6, 1024, 512
+    the same arithmetic, the same bits (1-8 tokens: the decode kernels in
+    their one-expert mode against the routed decode kernels)."""
     _, ms, xb, _, _ = wls.random_problem(41, T, H, I, 1, 1)
     gate, up, down = (pack_gpu(m) for m in ms)
     xd = to_dev(xb, torch.int16)
@@ -77,4 +81,4 @@ def test_shared_expert_matches_one_expert_forward():
     routed = B.moe_w4a16_forward(xd, gate, up, down, r)
     torch.cuda.synchronize()
     assert torch.equal(shared, routed)
-    log("shared expert: bit-identical to the one-expert routed forward")
+    log(f"shared expert T={T} H={H} I={I}: bit-identical to the one-expert routed forward")
