@@ -263,31 +263,18 @@ def main():
     w_d = packed_bytes(H, I)
     alg_bytes_step = U * (w_gu + w_d) + T * H * 2 * 2 + T * wl.E * 4
     flops_step = 6.0 * T * k * H * I
+    # (algorithmic bytes, flops) per launch; the grouped GEMMs read every
+    # touched expert's weights once and do 2 flops per weight per row
     kernel_work = {
-        "dec_fused": ("hbm", U * (w_gu + w_d) + T * H * 2 * 2 + T * wl.E * 4),
-        "dec_gateup": ("hbm", U * w_gu + T * H * 2),
-        "dec_gateup_route": ("hbm", U * w_gu + T * H * 2 + T * wl.E * 4),
-        "dec_down": ("hbm", U * w_d + T * H * 2),
-        "gemm_gateup": ("mfma", 4.0 * T * k * H * I),
-        "gemm_down": ("mfma", 2.0 * T * k * H * I),
+        "dec_fused": (U * (w_gu + w_d) + T * H * 2 * 2 + T * wl.E * 4, None),
+        "dec_gateup": (U * w_gu + T * H * 2, None),
+        "dec_gateup_route": (U * w_gu + T * H * 2 + T * wl.E * 4, None),
+        "dec_down": (U * w_d + T * H * 2, None),
+        "gemm_gateup": (U * w_gu + T * H * 2, 4.0 * T * k * H * I),
+        "gemm_down": (U * w_d + T * H * 2, 2.0 * T * k * H * I),
     }
-    if dominant in kernel_work:
-        bound, work = kernel_work[dominant]
-    else:
-        bound, work = "hbm", alg_bytes_step
-    if bound == "hbm":
-        achieved = work / (dom_us * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(dominant, wl.name),
-                    "kernel": dominant,
-                    "kernel_avg_us": round(dom_us, 3), "algorithmic_bytes_per_launch": int(work)}
-    else:
-        achieved = work / (dom_us * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                    "traffic": measured_traffic(dominant, wl.name),
-                    "kernel": dominant, "kernel_avg_us": round(dom_us, 3),
-                    "algorithmic_flops_per_launch": work}
+    work_bytes, work_flops = kernel_work.get(dominant, (alg_bytes_step, None))
+    roofline = make_roofline(dominant, dom_us, work_bytes, work_flops, measured_traffic(dominant, wl.name))
 
     tokens_per_s = T / (ms_per_step * 1e-3)
     step_gbps = alg_bytes_step / (ms_per_step * 1e-3) / 1e9
@@ -468,24 +455,15 @@ def bench_single(args, wl):
     dominant = max(prof, key=lambda k: prof[k][1])
     dom_us = prof[dominant][1] / prof[dominant][0] * 1e3
     if args.op == "linear":
-        work = {"dec_linear": ("hbm", w_bytes + T * H * 2 * 2), "gemm_down": ("mfma", 2.0 * T * H * H)}
+        work = {"dec_linear": (w_bytes + T * H * 2 * 2, None),
+                "gemm_down": (w_bytes + T * H * 2 * 2, 2.0 * T * H * H)}
         alg_bytes, flops = w_bytes + T * H * 2 * 2, 2.0 * T * H * H
     else:
-        work = {"dec_gateup": ("hbm", 2 * packed_bytes(I, H) + T * H * 2),
-                "dec_down": ("hbm", packed_bytes(H, I) + T * H * 2),
-                "gemm_gateup": ("mfma", 4.0 * T * H * I), "gemm_down": ("mfma", 2.0 * T * H * I)}
+        w_gu, w_d = 2 * packed_bytes(I, H), packed_bytes(H, I)
+        work = {"dec_gateup": (w_gu + T * H * 2, None), "dec_down": (w_d + T * H * 2, None),
+                "gemm_gateup": (w_gu + T * H * 2, 4.0 * T * H * I), "gemm_down": (w_d + T * H * 2, 2.0 * T * H * I)}
         alg_bytes, flops = w_bytes + T * H * 2 * 2, 6.0 * T * H * I
-    bound, wk = work.get(dominant, ("hbm", alg_bytes))
-    if bound == "hbm":
-        ach = wk / (dom_us * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dominant,
-                    "kernel_avg_us": round(dom_us, 3), "algorithmic_bytes_per_launch": int(wk)}
-    else:
-        ach = wk / (dom_us * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": dominant,
-                    "kernel_avg_us": round(dom_us, 3), "algorithmic_flops_per_launch": wk}
+    roofline = make_roofline(dominant, dom_us, *work.get(dominant, (alg_bytes, None)), traffic=None)
     cpu = None
     if not args.no_cpu:
         try:
@@ -532,6 +510,31 @@ def cpu_model():
     except OSError:
         pass
     return None
+
+
+def make_roofline(kernel, avg_us, work_bytes, work_flops, traffic):
+    """The dominant kernel against the roofline that binds it at this
+    workload: HBM when its algorithmic bytes take longer at 8 TB/s than its
+    flops at the bf16 MFMA peak (decode kernels have no flop figure), MFMA
+    otherwise; "other" gives the fraction of the other peak for context."""
+    t_hbm = work_bytes / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = work_flops / (BF16_PEAK_TFLOPS * 1e12) if work_flops else 0.0
+    gbps = work_bytes / (avg_us * 1e-6) / 1e9
+    tflops = work_flops / (avg_us * 1e-6) / 1e12 if work_flops else None
+    hbm = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+           "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    mfma = None if tflops is None else {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                                        "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+    main, other = (hbm, mfma) if t_hbm >= t_mfma else (mfma, hbm)
+    r = dict(main)
+    r.update({"traffic": traffic, "kernel": kernel, "kernel_avg_us": round(avg_us, 3),
+              "algorithmic_bytes_per_launch": int(work_bytes)})
+    if work_flops:
+        r["algorithmic_flops_per_launch"] = work_flops
+    if other is not None:
+        r["other"] = {"bound": other["bound"], "achieved": other["achieved"], "unit": other["unit"],
+                      "frac": other["frac"]}
+    return r
 
 
 def gpu_clocks():
