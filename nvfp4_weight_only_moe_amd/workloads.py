@@ -138,3 +138,14 @@ def random_problem(seed, T, H, I, E, k):
     xb = to_bf16_bits(g.standard_normal(size=(T, H), dtype=np.float32))
     lg = g.standard_normal(size=(T, E), dtype=np.float32)
     return wl, ms, xb, bf16_bits_to_f32(xb), lg
+
+
+def router_problem(seed, T, H, E):
+    """BF16 router inputs: (x bits [T, H], x fp32, router weight bits [E, H],
+    router weight fp32).  x ~ N(0, 1) and weights ~ N(0, 1/H) rounded to bf16,
+    so the logits are about N(0, 1) like the drawn logits of the workloads.
+    Keys start with 2 so they never collide with the generators above."""
+    g = rng((2, seed))
+    xb = to_bf16_bits(g.standard_normal(size=(T, H), dtype=np.float32))
+    wb = to_bf16_bits(np.float32(1.0 / np.sqrt(H)) * g.standard_normal(size=(E, H), dtype=np.float32))
+    return xb, bf16_bits_to_f32(xb), wb, bf16_bits_to_f32(wb)

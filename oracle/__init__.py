@@ -39,9 +39,10 @@ from .formats import (E2M1_MAGNITUDES, e2m1_decode, e2m1_encode, e4m3_decode,
 from .nvfp4 import quantize, dequantize, quantize_layer
 from .routing import route_topk, permutation
 from .moe import moe_forward, expert_ffn
+from .router import router_logits
 
 __all__ = [
     "E2M1_MAGNITUDES", "e2m1_decode", "e2m1_encode", "e4m3_decode",
     "e4m3_encode", "quantize", "dequantize", "quantize_layer", "route_topk",
-    "permutation", "moe_forward", "expert_ffn",
+    "permutation", "moe_forward", "expert_ffn", "router_logits",
 ]
