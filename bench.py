@@ -68,10 +68,11 @@ def parse():
                     help="step = moe_route_topk + moe_w4a16_forward (two calls) instead of route_forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM counter scaling)")
-    ap.add_argument("--op", choices=("moe", "linear", "shared"), default="moe",
+    ap.add_argument("--op", choices=("moe", "linear", "shared", "router"), default="moe",
                     help="moe: the routed layer (default); linear: a dense H x H NVFP4 projection "
-                         "(moe_w4a16_linear); shared: the shared expert (moe_w4a16_shared_expert), "
-                         "both at the workload's token count and shapes")
+                         "(moe_w4a16_linear); shared: the shared expert (moe_w4a16_shared_expert); "
+                         "router: the BF16 router logits (moe_router_logits); all at the workload's "
+                         "token count and shapes")
     return ap.parse_args()
 
 
@@ -387,21 +388,32 @@ def bench_single(args, wl):
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    T, H, I = wl.T, wl.H, wl.I
+    T, H, I, E = wl.T, wl.H, wl.I, wl.E
     decode = T <= 8
-    _, ms, xb, x, _ = wls.random_problem(7, T, H, H if args.op == "linear" else I, 1, 1)
-    if args.op == "linear":
-        ms = ms[:1]                                       # [1, H, H]
-        w_bytes = packed_bytes(H, H)
+    if args.op == "router":
+        # the BF16 router weight [E, H]; copies cycled past the Infinity Cache
+        xb, x, wb, wr = wls.router_problem(7, T, H, E)
+        w_bytes = E * H * 2
+        copies = args.copies or (max(1, -(-(1 << 29) // w_bytes)) if decode else 1)
+        base = torch.from_numpy(wb.view(np.int16)).to(dev)
+        sets = [base] + [base.clone() for _ in range(copies - 1)]
+        out = torch.empty((T, E), dtype=torch.float32, device=dev)
     else:
-        w_bytes = 2 * packed_bytes(I, H) + packed_bytes(H, I)
-    base = [B.moe_w4a16_quantize_pack(torch.from_numpy(m).to(dev)) for m in ms]
-    copies = args.copies or (max(1, -(-(1 << 30) // w_bytes)) if decode else 1)
-    sets = [base] + [[B.NVFP4Tensor(t.codes.clone(), t.scales.clone(), t.global_scale.clone()) for t in base]
-                     for _ in range(copies - 1)]
+        _, ms, xb, x, _ = wls.random_problem(7, T, H, H if args.op == "linear" else I, 1, 1)
+        if args.op == "linear":
+            ms = ms[:1]                                       # [1, H, H]
+            w_bytes = packed_bytes(H, H)
+        else:
+            w_bytes = 2 * packed_bytes(I, H) + packed_bytes(H, I)
+        base = [B.moe_w4a16_quantize_pack(torch.from_numpy(m).to(dev)) for m in ms]
+        copies = args.copies or (max(1, -(-(1 << 30) // w_bytes)) if decode else 1)
+        sets = [base] + [[B.NVFP4Tensor(t.codes.clone(), t.scales.clone(), t.global_scale.clone()) for t in base]
+                         for _ in range(copies - 1)]
+        out = torch.empty((T, H), dtype=torch.int16, device=dev)
     x_d = torch.from_numpy(xb.view(np.int16)).to(dev)
-    out = torch.empty((T, H), dtype=torch.int16, device=dev)
-    if args.op == "linear":
+    if args.op == "router":
+        step = lambda i: B.moe_router_logits(x_d, sets[i % copies], out=out)
+    elif args.op == "linear":
         ws = torch.empty((B.lib().moe_w4a16_linear_workspace_size(T, H, H),), dtype=torch.uint8, device=dev)
         step = lambda i: B.moe_w4a16_linear(x_d, sets[i % copies][0], out=out, ws=ws)
     else:
@@ -454,7 +466,11 @@ def bench_single(args, wl):
     per_kernel_us = {k: round(v[1] / v[0] * 1e3, 3) for k, v in prof.items()}
     dominant = max(prof, key=lambda k: prof[k][1])
     dom_us = prof[dominant][1] / prof[dominant][0] * 1e3
-    if args.op == "linear":
+    if args.op == "router":
+        rb = w_bytes + T * H * 2 + T * E * 4
+        work = {"router_gemv": (rb, None), "router_mfma": (rb, 2.0 * T * H * E)}
+        alg_bytes, flops = rb, 2.0 * T * H * E
+    elif args.op == "linear":
         work = {"dec_linear": (w_bytes + T * H * 2 * 2, None),
                 "gemm_down": (w_bytes + T * H * 2 * 2, 2.0 * T * H * H)}
         alg_bytes, flops = w_bytes + T * H * 2 * 2, 2.0 * T * H * H
@@ -471,25 +487,31 @@ def bench_single(args, wl):
             threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         except Exception:
             threads = 1
-        packed = [oracle.quantize_layer(m) for m in ms]
+        packed = [oracle.quantize_layer(m) for m in ms] if args.op != "router" else None
         n_tok = min(T, 64)
         t0 = time.perf_counter()
-        if args.op == "linear":
+        if args.op == "router":
+            for _ in range(200):
+                oracle.router_logits(x[:n_tok], wr)
+            n_tok *= 200
+        elif args.op == "linear":
             omoe.linear(x[:n_tok], packed[0][0][0], packed[0][1][0], packed[0][2][0])
         else:
             layer = {nm: p for nm, p in zip(("gate", "up", "down"), packed)}
             omoe.shared_expert_forward(x[:n_tok], layer)
         dt = time.perf_counter() - t0
         cpu = {"value": round(n_tok / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"{n_tok} token(s): dequantize + fp64 {'projection' if args.op == 'linear' else 'SwiGLU FFN'}"
-                         f", 1 run, {dt:.1f} s; quantization excluded",
+               "sample": (f"{n_tok} token-rows of fp64 logits (numpy matmul), {dt:.1f} s" if args.op == "router" else
+                          f"{n_tok} token(s): dequantize + fp64 {'projection' if args.op == 'linear' else 'SwiGLU FFN'}"
+                          f", 1 run, {dt:.1f} s; quantization excluded"),
                "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
     rec = {
         "metric": METRIC, "value": round(T / (ms_per_step * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{args.op}-t{T}-h{H}" + (f"-n{H}" if args.op == "linear" else f"-i{I}"),
-                   "T": T, "H": H, "I": H if args.op == "linear" else I, "copies": copies,
+        "config": {"workload": f"{args.op}-t{T}-h{H}" + (f"-e{E}" if args.op == "router" else
+                                                          f"-n{H}" if args.op == "linear" else f"-i{I}"),
+                   "T": T, "H": H, "I": H if args.op == "linear" else I, "E": E, "copies": copies,
                    "hip_graph": graph_ms is not None},
         "roofline": roofline, "cpu_baseline": cpu,
         "step_algorithmic_GBps": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),

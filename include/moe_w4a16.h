@@ -196,6 +196,25 @@ moe_status moe_w4a16_route_forward(const float *d_logits, const uint16_t *d_x,
                                    hipStream_t stream);
 
 /*
+ * Router logits, the step in front of moe_route_topk: the BF16 gate of the
+ * layer, logits[t][e] = sum_i x[t][i] * Wr[e][i], accumulated in fp32 (the
+ * routers stay BF16 and are never quantized: "GLM-5.3-Flash on Blackwell",
+ * "The quantization"; the pages print no router formula, the plain linear
+ * gate without bias is the reading taken).
+ *   d_x       bf16 [T][H] activations (caller-owned, read only)
+ *   d_wr      bf16 [E][H] router weight, row e = expert e (read only)
+ *   d_logits  fp32 [T][E] out, ready for moe_route_topk /
+ *             moe_w4a16_route_forward; must not overlap d_x or d_wr
+ *   H % 64 == 0, E >= 1, T >= 0 (T == 0 is a no-op); all pointers 16-byte
+ *   aligned.  1-8 tokens run a one-pass GEMV over Wr, more tokens bf16 MFMA
+ *   tiles; both sum in a fixed order (deterministic), no workspace, no
+ *   allocation, graph-capturable.
+ */
+moe_status moe_router_logits(const uint16_t *d_x, int32_t T, int32_t H,
+                             const uint16_t *d_wr, int32_t E, float *d_logits,
+                             hipStream_t stream);
+
+/*
  * Dense NVFP4 weight-only projection of T tokens: out = bf16(g * x . Wd^T),
  * Wd the dequantized [N][K] weight (E2M1 code * E4M3 group scale), g its
  * FP32 global scale, products accumulated in fp32 and rounded once (the dense

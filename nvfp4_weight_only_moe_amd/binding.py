@@ -56,6 +56,7 @@ _SIGS = {
     "moe_w4a16_workspace_init": (_I, [_P, _S, _P]),
     "moe_w4a16_linear_workspace_size": (_S, [_I, _I, _I]),
     "moe_w4a16_linear": (_I, [_P, _I, _I, _I, _TP, _P, _P, _S, _P]),
+    "moe_router_logits": (_I, [_P, _I, _I, _P, _I, _P, _P]),
     "moe_w4a16_shared_expert_workspace_size": (_S, [_I, _I, _I]),
     "moe_w4a16_shared_expert": (_I, [_P, _I, _I, _I, _TP, _TP, _TP, _P, _P, _S, _P]),
     "moe_debug_set_decode_wait_limit": (None, [_I]),
@@ -265,6 +266,18 @@ def moe_profile_end(max_names=64):
     n = lib().moe_profile_end(ctypes.cast(names, ctypes.c_void_p), ctypes.cast(counts, ctypes.c_void_p),
                               ctypes.cast(ms, ctypes.c_void_p), max_names)
     return {names[i].value.decode(): (int(counts[i]), float(ms[i])) for i in range(n)}
+
+
+def moe_router_logits(x_bits, wr_bits, out=None, stream=None):
+    """Router logits: bf16 bits x [T, H] and router weight [E, H] (int16
+    tensors) -> fp32 [T, E]."""
+    T, H = x_bits.shape
+    E, H2 = wr_bits.shape
+    assert H2 == H
+    out = torch.empty((T, E), dtype=torch.float32, device=x_bits.device) if out is None else out
+    _check(lib().moe_router_logits(_ptr(x_bits), T, H, _ptr(wr_bits), E, _ptr(out), _stream(stream)),
+           "moe_router_logits")
+    return out
 
 
 def moe_w4a16_linear(x_bits, w, out=None, ws=None, stream=None):

@@ -35,7 +35,7 @@ COMMON = [
 ]
 SOURCES = ["abi.cpp", "quantize.hip", "route.hip", "moe_decode.hip", "moe_decode_fused.hip",
            "moe_decode_t1_fused.hip", "moe_decode_t1_gateup.hip", "moe_decode_t1_down.hip",
-           "moe_decode_t8_fused.hip", "moe_decode_t8_gateup.hip", "moe_decode_t8_down.hip", "moe_prefill.hip", "moe_prefill_pipe.hip"]
+           "moe_decode_t8_fused.hip", "moe_decode_t8_gateup.hip", "moe_decode_t8_down.hip", "moe_prefill.hip", "moe_prefill_pipe.hip", "router.hip"]
 
 
 def _compile(src, verbose):

@@ -373,6 +373,21 @@ moe_status moe_w4a16_route_forward(const float* d_logits, const uint16_t* d_x, i
     return launch_decode_forward(a, L.sync, stream);
 }
 
+moe_status moe_router_logits(const uint16_t* d_x, int32_t T, int32_t H, const uint16_t* d_wr, int32_t E,
+                             float* d_logits, hipStream_t stream) {
+    if (T < 0 || H < 1 || E < 1 || !router_shape_supported(T, H, E)) return MOE_ERR_SHAPE;
+    if ((int64_t)T * H > (int64_t)INT32_MAX || (int64_t)E * H > (int64_t)INT32_MAX ||
+        (int64_t)T * E > (int64_t)INT32_MAX)
+        return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!d_x || !d_wr || !d_logits) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(d_x) || !aligned16(d_wr) || !aligned16(d_logits)) return MOE_ERR_ALIGN;
+    const size_t lb = (size_t)T * E * sizeof(float);
+    if (ranges_overlap(d_logits, lb, d_x, (size_t)T * H * 2) || ranges_overlap(d_logits, lb, d_wr, (size_t)E * H * 2))
+        return MOE_ERR_INVALID_ARG;
+    return launch_router_logits(d_x, T, H, d_wr, E, d_logits, stream);
+}
+
 size_t moe_w4a16_linear_workspace_size(int32_t T, int32_t K, int32_t N) {
     if (T <= 0 || K <= 0 || N <= 0) return 0;
     return linear_workspace_bytes(T, K, N);

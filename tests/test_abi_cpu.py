@@ -197,3 +197,22 @@ def test_shared_expert_argument_errors(L):
     assert shx(L, ws_bytes=1024) == -7
     need = L.moe_w4a16_shared_expert_workspace_size(4, 256, 128)
     assert need > L.moe_w4a16_workspace_size(4, 256, 128, 1, 1)  # identity routing in front
+
+
+def rtr(L, x=A, T=4, H=1024, wr=A + 0x100000, E=256, out=A + 0x800000):
+    return L.moe_router_logits(x, T, H, wr, E, out, None)
+
+
+def test_router_logits_argument_errors(L):
+    assert rtr(L, T=0) == b.MOE_OK                                 # no-op
+    assert rtr(L, T=-1) == -2                                      # SHAPE
+    assert rtr(L, H=100) == -2                                     # H % 64 != 0
+    assert rtr(L, H=0) == -2
+    assert rtr(L, E=0) == -2
+    assert rtr(L, x=0) == -1                                       # null pointers
+    assert rtr(L, wr=0) == -1
+    assert rtr(L, out=0) == -1
+    assert rtr(L, x=A + 2) == -3                                   # misaligned
+    assert rtr(L, out=A + 0x800004) == -3
+    assert rtr(L, out=A + 0x100) == -1                             # logits overlap x
+    assert rtr(L, out=A + 0x100000) == -1                          # logits overlap the router weight

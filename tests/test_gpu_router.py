@@ -1,0 +1,89 @@
+"""GPU parity of the router logits (moe_router_logits) against the oracle.
+
+Tolerance, derived from the arithmetic: the products of two bf16 values are
+exact in fp32, so the only error is the fp32 summation of H terms; in any
+order it is at most gamma_H * sum_i |x_i w_i| with gamma_n = n u / (1 - n u)
+(u = 2^-24; taken as 2^-23 to cover an accumulator that truncates).  The
+bound is per element, on the seeded inputs of the workload generators; the
+oracle sums in fp64."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from nvfp4_weight_only_moe_amd import binding as B
+from nvfp4_weight_only_moe_amd import workloads as wls
+from gpu_util import log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def bound(xa, wa):
+    H = xa.shape[1]
+    u = 2.0 ** -23
+    gamma = H * u / (1 - H * u)
+    return gamma * oracle.router_logits(np.abs(xa), np.abs(wa)) + 1e-30
+
+
+def run(T, H, E, seed):
+    xb, x, wb, w = wls.router_problem(seed, T, H, E)
+    got = B.moe_router_logits(to_dev(xb, torch.int16), to_dev(wb, torch.int16))
+    torch.cuda.synchronize()
+    return got.cpu().numpy().astype(np.float64), oracle.router_logits(x, w), bound(x, w)
+
+
+CASES = [
+    # 1-8 tokens: the GEMV
+    (1, 5120, 256, 1), (2, 1024, 64, 2), (5, 2048, 100, 3), (8, 5120, 256, 4), (3, 64, 1, 5), (7, 192, 33, 6),
+    # more tokens: MFMA tiles, ragged in tokens (32-row tiles) and experts (64-wide tiles)
+    (9, 1024, 256, 7), (33, 512, 70, 8), (100, 5120, 256, 9), (1000, 1024, 130, 10), (2048, 5120, 256, 11),
+    (40, 128, 1, 12),
+]
+
+
+@pytest.mark.parametrize("T,H,E,seed", CASES)
+def test_router_logits_parity(T, H, E, seed):
+    got, ref, tol = run(T, H, E, seed)
+    assert got.shape == (T, E)
+    err = np.abs(got - ref)
+    worst = float(np.max(err / tol))
+    assert np.all(err <= tol), f"T={T} H={H} E={E}: worst err/bound {worst:.3f}"
+    log(f"router T={T} H={H} E={E}: max|err| {err.max():.2e}, worst err/bound {worst:.3f}")
+
+
+def test_router_logits_deterministic_and_zero_tokens():
+    xb, _, wb, _ = wls.router_problem(21, 300, 1024, 256)
+    xd, wd = to_dev(xb, torch.int16), to_dev(wb, torch.int16)
+    a = B.moe_router_logits(xd, wd)
+    b = B.moe_router_logits(xd, wd)
+    x1 = B.moe_router_logits(xd[:4].contiguous(), wd)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    empty = B.moe_router_logits(torch.empty((0, 1024), dtype=torch.int16, device="cuda:0"), wd)
+    assert empty.shape == (0, 256)
+    with pytest.raises(B.MoeError) as err:
+        B.moe_router_logits(torch.zeros((2, 100), dtype=torch.int16, device="cuda:0"),
+                            torch.zeros((8, 100), dtype=torch.int16, device="cuda:0"))
+    assert B.STATUS[err.value.status] == "MOE_ERR_SHAPE"
+    # the GEMV rows and the MFMA rows agree within the bound of each
+    ref = oracle.router_logits(wls.bf16_bits_to_f32(xb[:4]), wls.bf16_bits_to_f32(wb))
+    tol = bound(wls.bf16_bits_to_f32(xb[:4]), wls.bf16_bits_to_f32(wb))
+    assert np.all(np.abs(a[:4].cpu().numpy() - ref) <= tol)
+    assert np.all(np.abs(x1.cpu().numpy() - ref) <= tol)
+    log("router: deterministic, T=0 no-op, bad H refused")
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_router_then_route_topk(T):
+    """The logits feed moe_route_topk; the top-k decision is taken by both
+    sides on the same fp32 logits (the device's), so ids are compared
+    bit-exactly against the oracle's routing of those logits."""
+    H, E, k = 5120, 256, 8
+    xb, _, wb, _ = wls.router_problem(30 + T, T, H, E)
+    lg = B.moe_router_logits(to_dev(xb, torch.int16), to_dev(wb, torch.int16))
+    r = B.moe_route_topk(lg, k)
+    torch.cuda.synchronize()
+    ids, w = oracle.route_topk(lg.cpu().numpy(), k)
+    assert np.array_equal(r.topk_ids.cpu().numpy(), ids)
+    assert float(np.max(np.abs(r.topk_w.cpu().numpy() - w))) <= 1e-6
+    log(f"router -> route_topk T={T}: ids bit-exact")
