@@ -8,13 +8,14 @@
 //    requests its 16-byte weight chunks and the tokens' matching x chunks
 //    (L2-resident) before using any, dots them in fp32 (v_dot2_f32_bf16),
 //    and the halves meet in LDS.  2.6 MB of weights at H 5120, E 256.
-//  * more tokens: v_mfma_f32_16x16x32_bf16 tiles.  A workgroup owns 32 token
-//    rows; each of its four waves computes 32 x 64 expert tiles, reading
-//    both operands straight from global memory (the whole W stays in L2):
+//  * more tokens: v_mfma_f32_16x16x32_bf16 tiles.  A workgroup owns a tile of
+//    64 tokens x 64 experts and its four waves split K in quarters, each
+//    reading its operand rows straight from global memory (W stays in L2):
 //    per 64-wide K stage a lane loads 32 contiguous bytes of each of its
 //    rows, one 16-byte piece per MFMA step; A and B see the same K order, so
-//    the dot products are unchanged.  Every workgroup reads all of W from
-//    L2, which bounds this shape (about 2 GB of L2 reads at 16K tokens).
+//    the dot products are unchanged.  The quarters meet in LDS and wave 0
+//    adds them in wave order.  Splitting K rather than the tile keeps many
+//    small waves in flight to cover the load latency of each stage.
 // Both are deterministic: fixed summation order, no atomics.
 #include "device_common.h"
 #include "internal.h"
@@ -25,8 +26,8 @@ namespace {
 constexpr int kRgThreads = 128;     // GEMV: two waves per expert row
 constexpr int kRgBatch = 5;         // 16-byte chunks per lane per batch (one batch at H 5120)
 constexpr int kRmThreads = 256;     // MFMA: four waves
-constexpr int kRmRows = 32;         // token rows per workgroup
-constexpr int kRmCols = 64;         // experts per wave tile
+constexpr int kRmRows = 64;         // token rows per workgroup tile
+constexpr int kRmCols = 64;         // experts per workgroup tile
 constexpr int kRmK = 64;            // K per stage (H % 64 == 0)
 
 // 8 bf16 pairs into an fp32 accumulator (v_dot2_f32_bf16: exact products)
@@ -90,65 +91,85 @@ __global__ void __launch_bounds__(kRgThreads) __attribute__((amdgpu_waves_per_eu
     if ((int)threadIdx.x < NT) logits[(int64_t)threadIdx.x * E + e] = s_part[0][threadIdx.x] + s_part[1][threadIdx.x];
 }
 
-__global__ void __launch_bounds__(kRmThreads)
+__global__ void __launch_bounds__(kRmThreads) __attribute__((amdgpu_waves_per_eu(2, 4)))
 k_router_mfma(const uint16_t* x, const uint16_t* w, int T, int H, int E, float* __restrict__ logits) {
+    constexpr int kMs = kRmRows / 16, kNs = kRmCols / 16;
+    constexpr int kWaves = kRmThreads / kWave;
+    constexpr int kSteps = kRmK / 32;                 // MFMA steps per stage
+    // partial tiles of waves 1..3, summed by wave 0: [wave - 1][ms][ns][lane] floatx4
+    __shared__ floatx4 part[kWaves - 1][kMs][kNs][kWave];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int lcol = lane & 15, kq = lane >> 4;
-    const int t0 = blockIdx.x * kRmRows;
-    const int ngroups = (E + kRmCols - 1) / kRmCols;
+    const int t0 = blockIdx.x * kRmRows, e0 = blockIdx.y * kRmCols;
+    // this wave's share of the K stages
+    const int nst = H / kRmK;
+    const int s0 = nst * wave / kWaves, s1 = nst * (wave + 1) / kWaves;
     // operand rows of this lane (clamped inside the tensors; stores are masked)
-    const uint16_t* arow[2];
+    const uint16_t* arow[kMs];
+    const uint16_t* brow[kNs];
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms)
+    for (int ms = 0; ms < kMs; ++ms)
         arow[ms] = x + (int64_t)min(t0 + ms * 16 + lcol, T - 1) * H + (kRmK / 4) * kq;
+#pragma unroll
+    for (int ns = 0; ns < kNs; ++ns)
+        brow[ns] = w + (int64_t)min(e0 + ns * 16 + lcol, E - 1) * H + (kRmK / 4) * kq;
 
-    for (int g = wave; g < ngroups; g += kRmThreads / kWave) {
-        const uint16_t* brow[4];
+    floatx4 acc[kMs][kNs];
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns)
-            brow[ns] = w + (int64_t)min(g * kRmCols + ns * 16 + lcol, E - 1) * H + (kRmK / 4) * kq;
-        floatx4 acc[2][4];
+    for (int ms = 0; ms < kMs; ++ms)
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms)
+        for (int ns = 0; ns < kNs; ++ns) acc[ms][ns] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // a lane's K slice of a stage: kRmK / 4 contiguous elements, one 16-byte
+    // piece per MFMA step
+    for (int st = s0; st < s1; ++st) {
+        const int k0 = st * kRmK;
+        uint4 a[kMs][kSteps], b[kNs][kSteps];
 #pragma unroll
-            for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = floatx4{0.f, 0.f, 0.f, 0.f};
-        // a lane's K slice of a stage: kRmK / 4 contiguous elements, one
-        // 16-byte piece per MFMA step
-        constexpr int kSteps = kRmK / 32;
-        for (int k0 = 0; k0 < H; k0 += kRmK) {
-            uint4 a[2][kSteps], b[4][kSteps];
+        for (int ms = 0; ms < kMs; ++ms)
 #pragma unroll
-            for (int ms = 0; ms < 2; ++ms)
+            for (int i = 0; i < kSteps; ++i) a[ms][i] = *reinterpret_cast<const uint4*>(arow[ms] + k0 + 8 * i);
 #pragma unroll
-                for (int i = 0; i < kSteps; ++i) a[ms][i] = *reinterpret_cast<const uint4*>(arow[ms] + k0 + 8 * i);
+        for (int ns = 0; ns < kNs; ++ns)
 #pragma unroll
-            for (int ns = 0; ns < 4; ++ns)
+            for (int i = 0; i < kSteps; ++i) b[ns][i] = *reinterpret_cast<const uint4*>(brow[ns] + k0 + 8 * i);
 #pragma unroll
-                for (int i = 0; i < kSteps; ++i) b[ns][i] = *reinterpret_cast<const uint4*>(brow[ns] + k0 + 8 * i);
+        for (int i = 0; i < kSteps; ++i)
 #pragma unroll
-            for (int i = 0; i < kSteps; ++i)
+            for (int ms = 0; ms < kMs; ++ms)
 #pragma unroll
-                for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-                    for (int ns = 0; ns < 4; ++ns)
-                        acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, a[ms][i]), __builtin_bit_cast(bf16x8, b[ns][i]),
-                            acc[ms][ns], 0, 0, 0);
-        }
-        // lane holds rows 4 kq + r of each 16-row subtile, column lcol
-#pragma unroll
-        for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = t0 + ms * 16 + 4 * kq + r;
-                if (t >= T) continue;
-#pragma unroll
-                for (int ns = 0; ns < 4; ++ns) {
-                    const int e = g * kRmCols + ns * 16 + lcol;
-                    if (e < E) logits[(int64_t)t * E + e] = acc[ms][ns][r];
-                }
-            }
+                for (int ns = 0; ns < kNs; ++ns)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, a[ms][i]), __builtin_bit_cast(bf16x8, b[ns][i]), acc[ms][ns], 0, 0,
+                        0);
     }
+    // the K quarters meet in LDS; wave 0 adds them in wave order
+    if (wave > 0) {
+#pragma unroll
+        for (int ms = 0; ms < kMs; ++ms)
+#pragma unroll
+            for (int ns = 0; ns < kNs; ++ns) part[wave - 1][ms][ns][lane] = acc[ms][ns];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int v = 0; v < kWaves - 1; ++v)
+#pragma unroll
+        for (int ms = 0; ms < kMs; ++ms)
+#pragma unroll
+            for (int ns = 0; ns < kNs; ++ns) acc[ms][ns] += part[v][ms][ns][lane];
+    // lane holds rows 4 kq + r of each 16-row subtile, column lcol
+#pragma unroll
+    for (int ms = 0; ms < kMs; ++ms)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + ms * 16 + 4 * kq + r;
+            if (t >= T) continue;
+#pragma unroll
+            for (int ns = 0; ns < kNs; ++ns) {
+                const int e = e0 + ns * 16 + lcol;
+                if (e < E) logits[(int64_t)t * E + e] = acc[ms][ns][r];
+            }
+        }
 }
 
 template <int NT>
@@ -176,8 +197,8 @@ moe_status launch_router_logits(const uint16_t* x, int T, int H, const uint16_t*
         case 8: return launch_gemv<8>(x, H, w, E, logits, s);
         default: break;
     }
-    const int grid = (T + kRmRows - 1) / kRmRows;
-    MOE_LAUNCH("router_mfma", k_router_mfma, dim3(grid), dim3(kRmThreads), 0, s, x, w, T, H, E, logits);
+    const dim3 grid((T + kRmRows - 1) / kRmRows, (E + kRmCols - 1) / kRmCols);
+    MOE_LAUNCH("router_mfma", k_router_mfma, grid, dim3(kRmThreads), 0, s, x, w, T, H, E, logits);
     return MOE_OK;
 }
 
