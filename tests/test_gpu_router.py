@@ -88,3 +88,45 @@ def test_router_then_route_topk(T):
     assert np.array_equal(r.topk_ids.cpu().numpy(), ids)
     assert float(np.max(np.abs(r.topk_w.cpu().numpy() - w))) <= 1e-6
     log(f"router -> route_topk T={T}: ids bit-exact")
+
+
+@pytest.mark.parametrize("T", [1, 100])
+def test_router_and_layer_in_one_graph(T):
+    """Router logits, then route + layer (moe_w4a16_route_forward), captured
+    in one HIP graph: every replay, with unrelated eager work between them,
+    gives the eager result bit for bit (the router needs no workspace and
+    allocates nothing)."""
+    H, I, E, k = 1024, 512, 32, 4
+    _, ms, _, _, _ = wls.random_problem(50 + T, T, H, I, E, k)
+    xb, _, wb, _ = wls.router_problem(60 + T, T, H, E)
+    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in ms)
+    xd, wd = to_dev(xb, torch.int16), to_dev(wb, torch.int16)
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda:0")
+    route = B.Routing.empty(T, E, k, "cuda:0")
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda:0")
+    ws = B.forward_workspace(T, H, I, E, k, "cuda:0")
+
+    def step():
+        B.moe_router_logits(xd, wd, out=lg)
+        B.moe_w4a16_route_forward(lg, xd, gate, up, down, k, routing=route, out=out, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_lg = out.clone(), lg.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        out.fill_(i + 1)
+        lg.fill_(float("nan"))
+        B.moe_router_logits(wd[:1].contiguous(), wd)             # unrelated eager work
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lg, ref_lg), f"replay {i}: logits"
+        assert torch.equal(out, ref_out), f"replay {i}: output"
+    log(f"router + route_forward graph T={T}: 3 replays bit-identical")
