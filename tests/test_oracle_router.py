@@ -60,3 +60,31 @@ def test_logit_scale_of_the_generator():
 def test_shape_mismatch_refused():
     with pytest.raises(ValueError):
         oracle.router_logits(np.zeros((2, 8)), np.zeros((3, 9)))
+
+
+# Planted mistakes in the router oracle must each trip one of the pins above.
+_MUTANTS = {
+    # the expert axis reversed (a wrong row index into W)
+    "experts reversed": lambda x, w: np.asarray(x, np.float64) @ np.asarray(w, np.float64)[::-1].T,
+    "dropped last column": lambda x, w: np.asarray(x, np.float64)[:, :-1] @ np.asarray(w, np.float64)[:, :-1].T,
+    "bias of one": lambda x, w: np.asarray(x, np.float64) @ np.asarray(w, np.float64).T + 1.0,
+    "sign flipped": lambda x, w: -(np.asarray(x, np.float64) @ np.asarray(w, np.float64).T),
+    "mean instead of sum": lambda x, w: (np.asarray(x, np.float64) @ np.asarray(w, np.float64).T) / np.asarray(x).shape[1],
+}
+
+
+def _router_pins():
+    test_one_hot_rows_pick_single_weights()
+    test_constant_rows_closed_form()
+    test_alternating_signs_cancel_and_negation_flips()
+    test_logit_scale_of_the_generator()
+
+
+@pytest.mark.parametrize("name", sorted(_MUTANTS))
+def test_planted_router_mistake_is_caught(name, monkeypatch):
+    import oracle.router as orouter
+    mutant = _MUTANTS[name]
+    monkeypatch.setattr(orouter, "router_logits", mutant)
+    monkeypatch.setattr(oracle, "router_logits", mutant)
+    with pytest.raises(AssertionError):
+        _router_pins()
