@@ -39,6 +39,8 @@ CASES = [
     (9, 1024, 256, 7), (33, 512, 70, 8), (100, 5120, 256, 9), (1000, 1024, 130, 10), (2048, 5120, 256, 11),
     (40, 128, 1, 12),
     (77, 320, 65, 13),        # 5 K stages: uneven split over the four waves
+    # wide routers and a long hidden size
+    (4, 8192, 300, 14), (8, 1024, 1024, 15), (130, 2048, 1000, 16), (65, 8192, 256, 17),
 ]
 
 
