@@ -9,7 +9,7 @@
 //    (L2-resident) before using any, dots them in fp32 (v_dot2_f32_bf16),
 //    and the halves meet in LDS.  2.6 MB of weights at H 5120, E 256.
 //  * more tokens: v_mfma_f32_16x16x32_bf16 tiles.  A workgroup owns a tile of
-//    64 tokens x 64 experts and its four waves split K in quarters, each
+//    32 or 64 tokens x 64 experts and its four waves split K in quarters, each
 //    reading its operand rows straight from global memory (W stays in L2):
 //    per 64-wide K stage a lane loads 32 contiguous bytes of each of its
 //    rows, one 16-byte piece per MFMA step; A and B see the same K order, so
@@ -26,7 +26,7 @@ namespace {
 constexpr int kRgThreads = 128;     // GEMV: two waves per expert row
 constexpr int kRgBatch = 5;         // 16-byte chunks per lane per batch (one batch at H 5120)
 constexpr int kRmThreads = 256;     // MFMA: four waves
-constexpr int kRmRows = 64;         // token rows per workgroup tile
+constexpr int kRmSmallT = 4096;     // up to here 32-token tiles, above 64
 constexpr int kRmCols = 64;         // experts per workgroup tile
 constexpr int kRmK = 64;            // K per stage (H % 64 == 0)
 
@@ -91,16 +91,17 @@ __global__ void __launch_bounds__(kRgThreads) __attribute__((amdgpu_waves_per_eu
     if ((int)threadIdx.x < NT) logits[(int64_t)threadIdx.x * E + e] = s_part[0][threadIdx.x] + s_part[1][threadIdx.x];
 }
 
+template <int ROWS>
 __global__ void __launch_bounds__(kRmThreads) __attribute__((amdgpu_waves_per_eu(2, 4)))
 k_router_mfma(const uint16_t* x, const uint16_t* w, int T, int H, int E, float* __restrict__ logits) {
-    constexpr int kMs = kRmRows / 16, kNs = kRmCols / 16;
+    constexpr int kMs = ROWS / 16, kNs = kRmCols / 16;
     constexpr int kWaves = kRmThreads / kWave;
     constexpr int kSteps = kRmK / 32;                 // MFMA steps per stage
     // partial tiles of waves 1..3, summed by wave 0: [wave - 1][ms][ns][lane] floatx4
     __shared__ floatx4 part[kWaves - 1][kMs][kNs][kWave];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int lcol = lane & 15, kq = lane >> 4;
-    const int t0 = blockIdx.x * kRmRows, e0 = blockIdx.y * kRmCols;
+    const int t0 = blockIdx.x * ROWS, e0 = blockIdx.y * kRmCols;
     // this wave's share of the K stages
     const int nst = H / kRmK;
     const int s0 = nst * wave / kWaves, s1 = nst * (wave + 1) / kWaves;
@@ -197,8 +198,15 @@ moe_status launch_router_logits(const uint16_t* x, int T, int H, const uint16_t*
         case 8: return launch_gemv<8>(x, H, w, E, logits, s);
         default: break;
     }
-    const dim3 grid((T + kRmRows - 1) / kRmRows, (E + kRmCols - 1) / kRmCols);
-    MOE_LAUNCH("router_mfma", k_router_mfma, grid, dim3(kRmThreads), 0, s, x, w, T, H, E, logits);
+    // 32-token tiles double the workgroups where tokens are few; 64-token
+    // tiles halve the W_r re-reads where there are many
+    if (T <= kRmSmallT) {
+        const dim3 grid((T + 31) / 32, (E + kRmCols - 1) / kRmCols);
+        MOE_LAUNCH("router_mfma", k_router_mfma<32>, grid, dim3(kRmThreads), 0, s, x, w, T, H, E, logits);
+    } else {
+        const dim3 grid((T + 63) / 64, (E + kRmCols - 1) / kRmCols);
+        MOE_LAUNCH("router_mfma", k_router_mfma<64>, grid, dim3(kRmThreads), 0, s, x, w, T, H, E, logits);
+    }
     return MOE_OK;
 }
 

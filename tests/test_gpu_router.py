@@ -35,12 +35,14 @@ def run(T, H, E, seed):
 CASES = [
     # 1-8 tokens: the GEMV
     (1, 5120, 256, 1), (2, 1024, 64, 2), (5, 2048, 100, 3), (8, 5120, 256, 4), (3, 64, 1, 5), (7, 192, 33, 6),
-    # more tokens: MFMA tiles, ragged in tokens (64-row tiles) and experts (64-wide tiles)
+    # more tokens: MFMA tiles (32 tokens up to 4096), ragged in tokens and experts (64-wide tiles)
     (9, 1024, 256, 7), (33, 512, 70, 8), (100, 5120, 256, 9), (1000, 1024, 130, 10), (2048, 5120, 256, 11),
     (40, 128, 1, 12),
     (77, 320, 65, 13),        # 5 K stages: uneven split over the four waves
     # wide routers and a long hidden size
     (4, 8192, 300, 14), (8, 1024, 1024, 15), (130, 2048, 1000, 16), (65, 8192, 256, 17),
+    # above 4096 tokens: 64-token tiles
+    (5000, 512, 70, 18), (4097, 1024, 256, 19),
 ]
 
 
