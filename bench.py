@@ -1,6 +1,6 @@
 """Benchmark of the NVFP4 W4A16 routed-expert MoE layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config C] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--config C] [--only] [--gpus 1]
 
 A step is one pass of the hot path over one batch of synthetic input:
 router top-k + permutation and the layer forward (gate/up grouped GEMM +
@@ -10,21 +10,26 @@ computed inside the gate/up kernel), or with --split as moe_route_topk
 followed by moe_w4a16_forward.  Quantization is load time and is not in a
 step.
 
-Default workload: decode, 1 token, hidden 5120, intermediate 1536, 256
-experts, top-8 (the "decode-t1" workload).  Inputs are resident in HBM before
-timing.  For decode workloads the step cycles through L distinct device
-copies of the packed layer so that the 256 MB Infinity Cache cannot serve the
-weights (a model has one such layer per MoE block); the steps are replayed
-from a HIP graph that holds L consecutive steps.
+Workloads (hidden 5120, intermediate 1536, 256 experts, top-8, one seeded
+layer): decode with 1 token (the headline, default --config 1), decode with
+8 tokens (MTP at 4 streams, shared router bias), a 1024-token prefill chunk
+and a 16384-token prefill with Zipf(1.1) expert popularity.  All four are
+measured in one run; the headline's fields are the top level of the JSON
+line and the others sit under "configs" with the same fields.  Inputs are
+resident in HBM before timing.  Decode workloads cycle through 16 distinct
+device copies of the packed layer so that the 256 MB Infinity Cache cannot
+serve the weights (a model has one such layer per MoE block); prefill
+workloads read all of a layer's touched experts (GBs) per step and use one.
+The timed region replays a HIP graph of `copies` consecutive steps at least
+10 times (more when --steps asks for more steps); "steps" is the number of
+steps actually timed and "step_spread" gives p10/p50/p90 over the replays.
 
-Prints one JSON line: the driver's fields plus "roofline" (dominant kernel,
-HIP-event timed on its own stream), "cpu_baseline" (the CPU oracle timed on a
-bounded sample of the same workload), "step_spread" (p10/p50/p90 of the step
-time over the graph replays, timed after the measured steps) and
+Each workload also carries "roofline" (the dominant kernel, timed by HIP
+events that its own launches stamp, against the roofline that binds it) and
+"cpu_baseline" (the oracle timed on the host cores on a bounded sample of
+the same workload, after all GPU work).  The top level adds
 "achievable_peaks" (a 1 GiB device copy and an 8192^3 bf16 GEMM by the
-torch/ROCm libraries, for context beside the spec peaks), with the host CPU
-model in "cpu_baseline" and the GPU clocks the driver reports right after the
-timed region ("gpu_clocks_after_timing").
+torch/ROCm libraries, for context beside the spec peaks).
 """
 import argparse
 import json
@@ -51,16 +56,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", type=int, default=1, help="workload index (1 = decode, 1 token)")
+    ap.add_argument("--config", type=int, default=1,
+                    help="headline workload index (1 = decode, 1 token); the others follow under \"configs\"")
+    ap.add_argument("--only", action="store_true", help="measure the headline workload alone")
     ap.add_argument("--copies", type=int, default=None, help="layer copies cycled through (decode)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak measurements")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--decode-variant", type=int, default=3,
-                    help="decode-shape kernels (moe_debug_set_decode_variant): 0 per-expert-block "
-                         "kernels, 1 one persistent launch, 2 its two halves, 3 the kernels of 0 "
-                         "with a single token's route inside the gate/up kernel (default)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget per workload")
     ap.add_argument("--prefill-variant", type=int, default=2,
                     help="grouped-GEMM kernels (moe_debug_set_prefill_variant): 0 register-staged, "
                          "1 LDS-pipelined, 2 chosen per product by rows per expert (default)")
@@ -83,7 +86,6 @@ def packed_bytes(N, K):
 # Sources that determine each kernel's memory traffic; the counters stored in
 # profiles/traffic.json are only reported while these files are unchanged.
 KERNEL_SOURCES = {
-    "dec_fused": ["decode_fused_kernel.h", "device_common.h", "route_common.h"],
     "dec_gateup": ["moe_decode.hip", "device_common.h", "route_common.h"],
     "dec_gateup_route": ["moe_decode.hip", "device_common.h", "route_common.h"],
     "dec_down": ["moe_decode.hip", "device_common.h", "route_common.h"],
@@ -126,21 +128,69 @@ def main():
     from nvfp4_weight_only_moe_amd import binding as B
     from nvfp4_weight_only_moe_amd import workloads as wls
 
-    wl = wls.WORKLOADS[args.config]
     if args.op != "moe":
-        return bench_single(args, wl)
-    B.moe_debug_set_decode_variant(args.decode_variant)
+        return bench_single(args, wls.WORKLOADS[args.config])
     B.moe_debug_set_prefill_variant(args.prefill_variant)
-    decode = wl.T <= 8
-    steps = args.steps or (400 if decode else (40 if wl.T <= 2048 else 10))
-    warmup = args.warmup if args.warmup is not None else (40 if decode else 3)
-    copies = args.copies or (16 if decode else 1)
-    dev = "cuda:0"
     torch.cuda.set_device(0)
-
-    # ---------------------------------------------------------------- layer
     t0 = time.time()
+    base, quant_ms = build_layer(wls.WORKLOADS[1])      # the one full-size layer of workloads 1-4
+    log(f"layer packed ({time.time() - t0:.1f} s)")
+
+    # the headline workload first, then the others in the same process
+    cfgs = [args.config] if args.only else [args.config] + [c for c in (1, 2, 3, 4) if c != args.config]
+    results = {}
+    copies_cache = {}
+    for cfg in cfgs:
+        results[cfg] = bench_moe_config(args, cfg, base, copies_cache)
+        torch.cuda.empty_cache()
+    copies_cache.clear()
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of 268435456 bytes (read 256 MiB, write 256 MiB each)")
+
+    # what plain library work reaches on this GPU, beside the spec peaks the
+    # roofline uses: a 1 GiB device copy (read + write) and a bf16 GEMM
+    achievable = None if args.no_peaks else achievable_peaks()
+
+    # the oracle on the host, per workload, after every GPU measurement
+    if not args.no_cpu:
+        for cfg in cfgs:
+            results[cfg]["cpu_baseline"] = cpu_baseline(wls.WORKLOADS[cfg], args.cpu_seconds)
+            log(f"cpu baseline {wls.WORKLOADS[cfg].name}: {results[cfg]['cpu_baseline']['value']} tokens/s")
+
+    head = results[cfgs[0]]
+    rec = {"metric": METRIC}
+    rec.update({k: head[k] for k in ("value", "unit")})
+    rec.update({"n_gpus": 1, "steps": head["steps"], "warmup": head["warmup"], "ms_per_step": head["ms_per_step"],
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                "data": "synthetic"})
+    rec["config"] = head["config"]
+    for key in ("roofline", "cpu_baseline", "steps_requested", "step_spread", "step_algorithmic_GBps",
+                "step_hbm_frac", "weight_GBps", "step_TFLOPs", "step_mfma_frac", "eager_ms_per_step",
+                "per_kernel_us"):
+        rec[key] = head.get(key)
+    rec["configs"] = {results[c]["config"]["workload"]: results[c] for c in cfgs[1:]}
+    rec["quantize_pack_ms_total"] = round(quant_ms, 2)
+    rec["achievable_peaks"] = achievable
+    rec["gpu_clocks_after_timing"] = head.get("gpu_clocks_after_timing")
+    print(json.dumps(rec), flush=True)
+
+
+def build_layer(wl):
+    """Generate the seeded fp32 masters of the full-size layer on the host and
+    quantize them on the GPU (load time, not part of a step).  Returns the
+    packed layer and the GPU quantize time in ms."""
+    import torch
     from concurrent.futures import ThreadPoolExecutor
+    from nvfp4_weight_only_moe_amd import binding as B
+    from nvfp4_weight_only_moe_amd import workloads as wls
+
+    dev = "cuda:0"
     threads = min(16, len(os.sched_getaffinity(0)))
     layer = {}
     quant_ms = 0.0
@@ -160,17 +210,40 @@ def main():
                 quant_ms += (time.perf_counter() - q0) * 1e3
                 del w
         layer[name] = t
-        log(f"packed {name} ({time.time() - t0:.1f} s)")
+    flag = torch.zeros((4,), dtype=torch.int32, device=dev)
     for name in ("gate", "up", "down"):
-        B.moe_w4a16_validate(layer[name])
-    layers = [layer]
-    for c in range(1, copies):
-        layers.append({n: B.NVFP4Tensor(t.codes.clone(), t.scales.clone(), t.global_scale.clone())
-                       for n, t in layer.items()})
-    torch.cuda.synchronize()
-    log(f"{copies} layer copies resident ({time.time() - t0:.1f} s)")
+        B.moe_w4a16_validate(layer[name], flag)
+    return layer, quant_ms
 
-    # ---------------------------------------------------------------- inputs
+
+def layer_copies(base, copies, cache):
+    """`copies` distinct device copies of the packed layer (the first is the
+    layer itself): a step cycles through them so the 256 MB Infinity Cache
+    cannot serve the weights, as with a model's many MoE layers."""
+    from nvfp4_weight_only_moe_amd import binding as B
+    lst = cache.setdefault("copies", [base])
+    while len(lst) < copies:
+        lst.append({n: B.NVFP4Tensor(t.codes.clone(), t.scales.clone(), t.global_scale.clone())
+                    for n, t in base.items()})
+    return lst[:copies]
+
+
+def bench_moe_config(args, cfg, base, cache):
+    """One workload: graph-replayed steps (route + layer), per-kernel times,
+    roofline of the dominant kernel."""
+    import torch
+    from nvfp4_weight_only_moe_amd import binding as B
+    from nvfp4_weight_only_moe_amd import workloads as wls
+
+    wl = wls.WORKLOADS[cfg]
+    dev = "cuda:0"
+    decode = wl.T <= 8
+    steps_req = args.steps or (400 if decode else 20)
+    warmup = args.warmup if args.warmup is not None else (40 if decode else 3)
+    copies = args.copies or (16 if decode else 1)
+    layers = layer_copies(base, copies, cache)
+    torch.cuda.synchronize()
+
     xb, _ = wls.activations(wl)
     lg = wls.logits(wl)
     x_d = torch.from_numpy(xb.view(np.int16)).to(dev)
@@ -194,7 +267,6 @@ def main():
     counts = route.counts.cpu().numpy()
     U = int((counts > 0).sum())
 
-    # ---------------------------------------------------------------- eager timing
     def timed(fn, n):
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -204,13 +276,14 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
-    eager_ms = timed(lambda n: [step(i) for i in range(n)], steps)
+    n_eager = max(steps_req, copies)
+    eager_ms = timed(lambda n: [step(i) for i in range(n)], n_eager)
     assert torch.equal(out, ref_out)
-    log(f"eager: {eager_ms * 1e3:.2f} us/step")
 
-    # ---------------------------------------------------------------- graph timing
-    graph_ms = None
-    step_spread = None
+    # timed region: R replays of a graph of `copies` consecutive steps, at
+    # least 10 so that the spread is over real samples; every replay is
+    # bracketed by its own events (stream-ordered, no synchronisation between)
+    graph_ms, spread, steps_timed = None, None, n_eager
     if not args.no_graph:
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -227,47 +300,47 @@ def main():
         g.replay()
         torch.cuda.synchronize()
         if not torch.equal(out, ref_out):
-            log("graph replay output differs from eager: graph timing discarded")
+            log(f"{wl.name}: graph replay output differs from eager: graph timing discarded")
         else:
-            reps = max(1, steps // copies)
+            reps = max(10, -(-steps_req // copies))
             for _ in range(3):
                 g.replay()
-            graph_ms = timed(lambda n: [g.replay() for _ in range(n)], reps) / copies
-            assert torch.equal(out, ref_out)
-            log(f"graph: {graph_ms * 1e3:.2f} us/step")
-            # spread: each replay (copies consecutive steps) timed on its own, after the timed region
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-            for a, b in evs:
-                a.record()
-                g.replay()
-                b.record()
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
             torch.cuda.synchronize()
-            per = sorted(a.elapsed_time(b) / copies * 1e3 for a, b in evs)
+            evs[0].record()
+            for r in range(reps):
+                g.replay()
+                evs[r + 1].record()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_out)
+            per = sorted(evs[r].elapsed_time(evs[r + 1]) / copies * 1e3 for r in range(reps))
+            graph_ms = evs[0].elapsed_time(evs[reps]) / (reps * copies)
+            steps_timed = reps * copies
             q = lambda f: round(per[int(round(f * (len(per) - 1)))], 3)
-            step_spread = {"p10_us": q(0.1), "p50_us": q(0.5), "p90_us": q(0.9), "samples": len(per),
-                           "steps_per_sample": copies}
+            spread = {"p10_us": q(0.1), "p50_us": q(0.5), "p90_us": q(0.9), "samples": reps,
+                      "steps_per_sample": copies}
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
+    log(f"{wl.name}: {ms_per_step * 1e3:.2f} us/step over {steps_timed} steps (eager {eager_ms * 1e3:.2f})")
 
-    # ---------------------------------------------------------------- per-kernel timing
-    B.moe_profile_begin(64 * max(steps, 1))
-    for i in range(steps):
+    # per-kernel times from events the launches stamp themselves
+    n_prof = max(steps_req, 10)
+    B.moe_profile_begin(64 * n_prof)
+    for i in range(n_prof):
         step(i)
     prof = B.moe_profile_end()
     per_kernel_us = {k: round(v[1] / v[0] * 1e3, 3) for k, v in prof.items()}
-    dominant = max(prof, key=lambda k: prof[k][1] / steps)
+    dominant = max(prof, key=lambda k: prof[k][1])
     dom_us = prof[dominant][1] / prof[dominant][0] * 1e3
-    log(f"per-kernel us: {per_kernel_us}")
+    log(f"{wl.name}: per-kernel us {per_kernel_us}")
+    clocks = gpu_clocks()
 
-    # ---------------------------------------------------------------- roofline
     H, I, T, k = wl.H, wl.I, wl.T, wl.k
-    w_gu = 2 * packed_bytes(I, H)
-    w_d = packed_bytes(H, I)
+    w_gu, w_d = 2 * packed_bytes(I, H), packed_bytes(H, I)
     alg_bytes_step = U * (w_gu + w_d) + T * H * 2 * 2 + T * wl.E * 4
     flops_step = 6.0 * T * k * H * I
     # (algorithmic bytes, flops) per launch; the grouped GEMMs read every
     # touched expert's weights once and do 2 flops per weight per row
     kernel_work = {
-        "dec_fused": (U * (w_gu + w_d) + T * H * 2 * 2 + T * wl.E * 4, None),
         "dec_gateup": (U * w_gu + T * H * 2, None),
         "dec_gateup_route": (U * w_gu + T * H * 2 + T * wl.E * 4, None),
         "dec_down": (U * w_d + T * H * 2, None),
@@ -276,104 +349,130 @@ def main():
     }
     work_bytes, work_flops = kernel_work.get(dominant, (alg_bytes_step, None))
     roofline = make_roofline(dominant, dom_us, work_bytes, work_flops, measured_traffic(dominant, wl.name))
-
-    tokens_per_s = T / (ms_per_step * 1e-3)
-    step_gbps = alg_bytes_step / (ms_per_step * 1e-3) / 1e9
-    step_tflops = flops_step / (ms_per_step * 1e-3) / 1e12
-
-    if args.copy_calibration:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("copy calibration: 3 copies of 268435456 bytes (read 256 MiB, write 256 MiB each)")
-
-    clocks = gpu_clocks()
-
-    # ---------------------------------------------------------------- achievable peaks
-    # what plain library work reaches on this GPU, beside the spec peaks the
-    # roofline uses: a 1 GiB device copy (read + write) and a bf16 GEMM
-    achievable = None
-    if not args.no_peaks:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        copy_ms = timed(lambda r: [dst.copy_(src) for _ in range(r)], 5)
-        del src, dst
-        m = 8192
-        ga = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
-        gb = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
-        gc = ga @ gb
-        mm_ms = timed(lambda r: [torch.matmul(ga, gb, out=gc) for _ in range(r)], 5)
-        del ga, gb, gc
-        achievable = {"hbm_copy_GBps": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
-                      "bf16_gemm_8192_TFLOPs": round(2.0 * m ** 3 / (mm_ms * 1e-3) / 1e12, 1)}
-        log(f"achievable: {achievable}")
-
-    # ---------------------------------------------------------------- CPU oracle baseline
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(wl, lg, args.cpu_seconds)
-
-    rec = {
-        "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": wl.E, "k": k,
-                   "layer_copies": copies, "hip_graph": graph_ms is not None, "touched_experts": U,
+    sec = ms_per_step * 1e-3
+    return {
+        "value": round(T / sec, 2), "unit": "tokens/s", "steps": steps_timed, "steps_requested": steps_req,
+        "warmup": warmup, "ms_per_step": round(ms_per_step, 6),
+        "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": wl.E, "k": k, "layer_copies": copies,
+                   "hip_graph": graph_ms is not None, "touched_experts": U,
+                   "max_rows_per_expert": int(counts.max()),
                    "step_calls": "route_topk+forward" if args.split else "route_forward",
-                   "decode_variant": args.decode_variant if decode else None,
                    "prefill_variant": None if decode else args.prefill_variant},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "step_algorithmic_GBps": round(step_gbps, 1), "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
-        "weight_GBps": round(U * (w_gu + w_d) / (ms_per_step * 1e-3) / 1e9, 1),
-        "step_TFLOPs": round(step_tflops, 3), "step_mfma_frac": round(step_tflops / BF16_PEAK_TFLOPS, 5),
-        "eager_ms_per_step": round(eager_ms, 6), "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 6),
-        "per_kernel_us": per_kernel_us, "quantize_pack_ms_total": round(quant_ms, 2),
-        "step_spread": step_spread, "achievable_peaks": achievable, "gpu_clocks_after_timing": clocks,
+        "roofline": roofline, "cpu_baseline": None, "step_spread": spread,
+        "step_algorithmic_GBps": round(alg_bytes_step / sec / 1e9, 1),
+        "step_hbm_frac": round(alg_bytes_step / sec / 1e9 / HBM_PEAK_GBPS, 4),
+        "weight_GBps": round(U * (w_gu + w_d) / sec / 1e9, 1),
+        "step_TFLOPs": round(flops_step / sec / 1e12, 3),
+        "step_mfma_frac": round(flops_step / sec / 1e12 / BF16_PEAK_TFLOPS, 5),
+        "eager_ms_per_step": round(eager_ms, 6), "per_kernel_us": per_kernel_us,
+        "gpu_clocks_after_timing": clocks,
     }
-    print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(wl, logits, budget_s):
-    """The oracle (fp64 numpy) on the host: route + FFN + combine for a
-    bounded sample of the workload's tokens, expert quantization excluded."""
+def achievable_peaks():
+    import torch
+    dev = "cuda:0"
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(n)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    copy_ms = timed(lambda r: [dst.copy_(src) for _ in range(r)], 5)
+    del src, dst
+    m = 8192
+    ga = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    gb = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    gc = ga @ gb
+    mm_ms = timed(lambda r: [torch.matmul(ga, gb, out=gc) for _ in range(r)], 5)
+    del ga, gb, gc
+    res = {"hbm_copy_GBps": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
+           "bf16_gemm_8192_TFLOPs": round(2.0 * m ** 3 / (mm_ms * 1e-3) / 1e12, 1)}
+    log(f"achievable: {res}")
+    return res
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle (fp64 numpy, BLAS on the host's cores) on a bounded sample
+    of the workload, expert quantization excluded.  Decode workloads: route +
+    FFN + combine of the first tokens (1, or 2 of the 8), repeated within the
+    budget.  Prefill workloads: the route of every token, then the experts
+    one at a time in ascending index, each adding its weighted FFN rows into
+    an fp64 [T, H] output, until the budget is spent; the rate counts the
+    rows processed (k rows make one token)."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
+    from oracle import moe as omoe
     from nvfp4_weight_only_moe_amd import workloads as wls
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
-    _, x = wls.activations(wl)
-    n_tok = 1 if wl.T <= 8 else 2
-    tokens = list(range(n_tok))
-    ids, _ = oracle.route_topk(logits[:n_tok], wl.k)
-    experts = sorted(set(int(e) for e in ids.ravel()))
     threads = min(16, len(os.sched_getaffinity(0)))
-    todo = [(p, n, e) for p, n in ((wls.GATE, "gate"), (wls.UP, "up"), (wls.DOWN, "down")) for e in experts]
-    with ThreadPoolExecutor(threads) as ex:
-        res = list(ex.map(lambda a: oracle.quantize(wls.master(wl, a[0], a[2])), todo))
-    layer = {n: ({}, {}, {}) for n in ("gate", "up", "down")}
-    for (p, n, e), (c, s, g) in zip(todo, res):
-        layer[n][0][e], layer[n][1][e], layer[n][2][e] = c, s, g
-    runs, t_total = 0, 0.0
-    while t_total < budget_s and runs < 50:
+    _, x = wls.activations(wl)
+    logits = wls.logits(wl)
+
+    def quantized(experts):
+        todo = [(p, n, e) for p, n in ((wls.GATE, "gate"), (wls.UP, "up"), (wls.DOWN, "down")) for e in experts]
+        with ThreadPoolExecutor(threads) as ex:
+            res = list(ex.map(lambda a: oracle.quantize(wls.master(wl, a[0], a[2])), todo))
+        layer = {n: ({}, {}, {}) for n in ("gate", "up", "down")}
+        for (p, n, e), (c, s, g) in zip(todo, res):
+            layer[n][0][e], layer[n][1][e], layer[n][2][e] = c, s, g
+        return layer
+
+    if wl.T <= 8:
+        n_tok = 1 if wl.T == 1 else 2
+        ids, _ = oracle.route_topk(logits[:n_tok], wl.k)
+        experts = sorted(set(int(e) for e in ids.ravel()))
+        layer = quantized(experts)
+        runs, t_total = 0, 0.0
+        while t_total < budget_s and runs < 50:
+            t0 = time.perf_counter()
+            ids_s, w_s = oracle.route_topk(logits[:n_tok], wl.k)
+            oracle.moe_forward(x[:n_tok], layer, ids_s, w_s, tokens=range(n_tok))
+            t_total += time.perf_counter() - t0
+            runs += 1
+        rate = n_tok * runs / t_total
+        sample = (f"{n_tok} of {wl.T} token(s): route + SwiGLU FFN of {len(experts)} experts (dequantize + fp64) "
+                  f"+ combine, {runs} runs, {t_total:.1f} s; expert quantization excluded")
+    else:
         t0 = time.perf_counter()
-        ids_s, w_s = oracle.route_topk(logits[:n_tok], wl.k)
-        oracle.moe_forward(x[:n_tok], layer, ids_s, w_s, tokens=tokens)
-        t_total += time.perf_counter() - t0
-        runs += 1
-    per_run = t_total / runs
-    return {"value": round(n_tok / per_run, 4), "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"{n_tok} token(s) of {wl.name}: route + SwiGLU FFN of {len(experts)} experts (dequantize "
-                      f"+ fp64) + combine, {runs} runs, {t_total:.1f} s; expert quantization excluded",
-            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+        ids, w = oracle.route_topk(logits, wl.k)
+        t_route = time.perf_counter() - t0
+        present = sorted(set(int(e) for e in ids.ravel()))
+        out = np.zeros((wl.T, wl.H))
+        xf = x.astype(np.float64)
+        t_total, rows, done, i = t_route, 0, [], 0
+        while i < len(present) and t_total < budget_s:
+            batch = present[i:i + 4]
+            layer = quantized(batch)                     # excluded from the time
+            for e in batch:
+                t0 = time.perf_counter()
+                r, sl = np.nonzero(ids == e)
+                wg, wu, wd = omoe.dequantize_expert(layer, e)
+                out[r] += w[r, sl][:, None] * omoe.expert_ffn(xf[r], wg, wu, wd)
+                t_total += time.perf_counter() - t0
+                rows += r.size
+                done.append(e)
+            i += len(batch)
+        rate = rows / wl.k / t_total
+        sample = (f"route of all {wl.T} tokens ({t_route:.1f} s), then {len(done)} of {len(present)} touched experts "
+                  f"one at a time (ascending index), {rows} of {wl.T * wl.k} (token, expert) rows, dequantize + "
+                  f"fp64 SwiGLU FFN accumulated into an fp64 [T, H] output, {t_total:.1f} s; rate = rows / k / time; "
+                  f"expert quantization excluded")
+    return {"value": round(rate, 4), "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": sample, "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
 
 
 def bench_single(args, wl):
@@ -452,8 +551,9 @@ def bench_single(args, wl):
         g.replay()
         torch.cuda.synchronize()
         if torch.equal(out, ref_out):
-            reps = max(1, steps // copies)
+            reps = max(10, -(-steps // copies))
             graph_ms = timed(lambda n: [g.replay() for _ in range(n)], reps) / copies
+            steps = reps * copies
             assert torch.equal(out, ref_out)
         else:
             log("graph replay output differs from eager: graph timing discarded")

@@ -33,7 +33,13 @@
  *     anything is enqueued; the call then has no effect.  Launch failures
  *     return MOE_ERR_HIP.  A device fault surfaces at the caller's next
  *     synchronisation, as usual for HIP.
- *   - The library keeps no state between calls and is thread-safe.
+ *   - The entry points keep no state between calls and may be called from
+ *     several threads at once (on different streams, or ordered on one).
+ *     The only process-wide state is the benchmarking switches at the end
+ *     of this header (the grouped-GEMM kernel choice and per-kernel
+ *     profiling): a call reads them atomically when it starts, so changing
+ *     them while other threads run forwards is safe and affects only calls
+ *     made afterwards.
  *
  * Limits: 1 <= E <= 1024, 1 <= k <= min(E, 32); quantize_pack needs
  * K % 32 == 0; the forward needs H % 256 == 0 and I % 128 == 0.
@@ -116,16 +122,27 @@ moe_status moe_w4a16_dequantize(const moe_nvfp4_tensor *t, float *d_w_out, hipSt
  * Check a tensor stack before use.  SYNCHRONISES `stream`.  Returns
  * MOE_ERR_NONFINITE if a global scale is NaN/Inf, MOE_ERR_BAD_SCALE if one is
  * <= 0 (the unset-scale fault: "GLM-5.3-Flash on Blackwell", "The model
- * loaded, served an API, and produced garbage") or if a group scale byte is
- * an E4M3 NaN (0x7F / 0xFF).  Allocates and frees a 4-byte device flag.
+ * loaded, served an API, and produced garbage"; the static check for a
+ * missing weight_scale_2 before load: "GLM-5.3-Flash-NVFP4-h", "Config
+ * expectations") or if a group scale byte is an E4M3 NaN (0x7F / 0xFF).
+ *   d_flag  a caller-owned device word (4 bytes, 16-byte aligned) that the
+ *           call clears and the check kernel sets; its value afterwards is
+ *           unspecified.  Must not overlap the tensor.  NULL gives
+ *           MOE_ERR_WORKSPACE.  The call allocates nothing.
  */
-moe_status moe_w4a16_validate(const moe_nvfp4_tensor *t, hipStream_t stream);
+moe_status moe_w4a16_validate(const moe_nvfp4_tensor *t, void *d_flag, hipStream_t stream);
 
 /* Workspace bytes moe_route_topk needs for T tokens (0 is a valid answer). */
 size_t moe_route_workspace_size(int32_t T, int32_t E, int32_t k);
 
 /*
- * Router top-k + softmax, and the expert-sorted permutation.
+ * Router top-k + softmax, and the expert-sorted permutation.  The pages keep
+ * every router in BF16 and never quantize it ("GLM-5.3-Flash on Blackwell",
+ * "The quantization"; "GLM-5.3-Flash-NVFP4-h", "Config expectations", the
+ * ignore list) but print no scoring rule.  Reading taken: the k largest
+ * logits, ties to the lower expert index, then a softmax over the k selected
+ * logits (equal to a softmax over all E renormalised over the k); no bias
+ * correction, grouped top-k or routed scaling factor.
  *   d_logits       fp32 [T][E] router logits (finite)
  *   d_topk_ids     int32 [T][k] out: per token, experts by descending logit,
  *                  ties to the lower index
@@ -145,9 +162,8 @@ moe_status moe_route_topk(const float *d_logits, int32_t T, int32_t E, int32_t k
                           void *d_ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Workspace bytes moe_w4a16_forward and moe_w4a16_route_forward need.  Its
- * first 256 bytes must be zero before the first call on it
- * (moe_w4a16_workspace_init); the calls keep them zero afterwards.
+ * Workspace bytes moe_w4a16_forward and moe_w4a16_route_forward need (no
+ * initialisation: every call writes what it reads).
  */
 size_t moe_w4a16_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
 
@@ -176,8 +192,9 @@ moe_status moe_w4a16_forward(const uint16_t *d_x, int32_t T, int32_t H, int32_t 
                              hipStream_t stream);
 
 /*
- * Route and layer in one call: moe_route_topk on d_logits (fp32 [T][E]),
- * storing every routing output exactly as moe_route_topk does, followed by
+ * Route and layer in one call (the pages treat routing and the expert FFN as
+ * one MoE layer): moe_route_topk on d_logits (fp32 [T][E]), storing every
+ * routing output exactly as moe_route_topk does, followed by
  * moe_w4a16_forward on that routing.  Decode shapes (1 <= T <= 8, T*k <= 64,
  * H % 1024 == 0, H <= 8192, I % 512 == 0, I <= 2048): with one token the
  * gate/up kernel routes itself (two launches in all), with more tokens a
@@ -256,41 +273,6 @@ moe_status moe_w4a16_shared_expert(const uint16_t *d_x, int32_t T, int32_t H, in
                                    void *d_ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Prepare a forward workspace for first use: zeroes its first 256 bytes, the
- * words through which the workgroups of the single-launch decode path hand
- * the SwiGLU output over to the down projection.  A workspace must start
- * with these bytes zero (this call, or memory allocated zero-filled); every
- * forward leaves them zero again, so a workspace is prepared once, not per
- * call.  Calls that share a workspace must be ordered on one stream.
- */
-moe_status moe_w4a16_workspace_init(void *d_ws, size_t ws_bytes, hipStream_t stream);
-
-/*
- * Test hook: how many times a workgroup of the single-launch decode path
- * polls for the other workgroups' SwiGLU outputs before it computes all of
- * them itself (default 1048576).  0 forces that local computation in every
- * workgroup, which exercises the path taken when not every workgroup of the
- * grid can be resident at once.  Process-wide; not for use while forwards
- * run on other threads.
- */
-void moe_debug_set_decode_wait_limit(int32_t polls);
-
-/*
- * Benchmarking and test hook: which kernels run decode shapes (1-8 tokens).
- * 0: a gate/up kernel and a down kernel, one workgroup per (expert, block
- * of rows); 1: the whole layer in one persistent launch (with the route,
- * for moe_w4a16_route_forward); 2: the gate/up and down halves of that
- * persistent kernel as two launches; 3 (default): the kernels of 0, and for
- * moe_w4a16_route_forward with one token the routing is computed inside the
- * gate/up kernel from the logits (no separate route launch; other calls run
- * 0).  All give results within the
- * forward's tolerance of each other; each is deterministic.  Shapes a
- * variant does not cover use variant 0.  Process-wide.  Returns
- * MOE_ERR_INVALID_ARG for other values.
- */
-moe_status moe_debug_set_decode_variant(int32_t variant);
-
-/*
  * Benchmarking and test hook: which grouped-GEMM kernels run the shapes the
  * decode kernels do not take.  0: operands staged through registers, one
  * K stage in flight, for both products; 1: operands streamed to LDS by DMA
@@ -299,8 +281,9 @@ moe_status moe_debug_set_decode_variant(int32_t variant);
  * expert (T * k / min(E, T * k)) is at least 256, the register-staged
  * kernels otherwise.  All give results within the forward's
  * tolerance of each other; each is deterministic.  Shapes the LDS-streamed
- * kernel does not cover (H % 512 or I % 256 nonzero) use 0.  Process-wide.
- * Returns MOE_ERR_INVALID_ARG for other values.
+ * kernel does not cover (H % 512 or I % 256 nonzero) use 0.  Process-wide,
+ * stored atomically; a call made afterwards on any thread uses the new
+ * value.  Returns MOE_ERR_INVALID_ARG for other values.
  */
 moe_status moe_debug_set_prefill_variant(int32_t variant);
 
@@ -311,7 +294,9 @@ moe_status moe_debug_set_prefill_variant(int32_t variant);
  * (hipExtLaunchKernel), for up to n kernels; do not profile while a stream is
  * being captured.  moe_profile_end() synchronises on the events and writes, for each
  * distinct kernel name (up to `max`), its launch count and total milliseconds.
- * Returns the number of names written.  Not thread-safe; for benchmarks only.
+ * Returns the number of names written.  The switch is process-wide: launches
+ * on every thread are timed while it is on.  Call begin and end from one
+ * thread; for benchmarks only.
  */
 moe_status moe_profile_begin(int32_t max_launches);
 int32_t moe_profile_end(char (*names)[64], int32_t *counts, double *total_ms, int32_t max);

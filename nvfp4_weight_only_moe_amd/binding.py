@@ -46,21 +46,18 @@ _SIGS = {
     "moe_w4a16_version": (_I, []),
     "moe_w4a16_quantize_pack": (_I, [_P, _I, _I, _I, _TP, _P]),
     "moe_w4a16_dequantize": (_I, [_TP, _P, _P]),
-    "moe_w4a16_validate": (_I, [_TP, _P]),
+    "moe_w4a16_validate": (_I, [_TP, _P, _P]),
     "moe_route_workspace_size": (_S, [_I, _I, _I]),
     "moe_route_topk": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
     "moe_w4a16_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "moe_w4a16_forward": (_I, [_P, _I, _I, _I, _I, _I, _TP, _TP, _TP, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
     "moe_w4a16_route_forward": (_I, [_P, _P, _I, _I, _I, _I, _I, _TP, _TP, _TP, _P, _P, _P, _P, _P, _P, _P, _P,
                                      _S, _P]),
-    "moe_w4a16_workspace_init": (_I, [_P, _S, _P]),
     "moe_w4a16_linear_workspace_size": (_S, [_I, _I, _I]),
     "moe_w4a16_linear": (_I, [_P, _I, _I, _I, _TP, _P, _P, _S, _P]),
     "moe_router_logits": (_I, [_P, _I, _I, _P, _I, _P, _P]),
     "moe_w4a16_shared_expert_workspace_size": (_S, [_I, _I, _I]),
     "moe_w4a16_shared_expert": (_I, [_P, _I, _I, _I, _TP, _TP, _TP, _P, _P, _S, _P]),
-    "moe_debug_set_decode_wait_limit": (None, [_I]),
-    "moe_debug_set_decode_variant": (_I, [_I]),
     "moe_debug_set_prefill_variant": (_I, [_I]),
     "moe_profile_begin": (_I, [_I]),
     "moe_profile_end": (_I, [_P, _P, _P, _I]),
@@ -108,6 +105,31 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+_BITS16 = (torch.int16, torch.uint16, torch.bfloat16) if hasattr(torch, "uint16") else (torch.int16, torch.bfloat16)
+
+
+def _dev_tensor(t, name, dtype=None, shape=None, min_bytes=None):
+    """The C ABI takes bare pointers and (for outputs) no sizes, so the
+    binding checks every tensor before the call: a device tensor,
+    contiguous, of the expected dtype(s) and exact shape (or at least
+    `min_bytes`).  Raises ValueError instead of calling into the library."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: expected a device (cuda) tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None:
+        ok = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in ok:
+            raise ValueError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in ok)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, at least {min_bytes} needed")
+    return t
+
+
 @dataclass
 class NVFP4Tensor:
     """E experts of an [N, K] NVFP4 projection in canonical layout (device)."""
@@ -120,7 +142,15 @@ class NVFP4Tensor:
         E, N, half = self.codes.shape
         return E, N, half * 2
 
+    def check(self, name="tensor"):
+        E, N, K = self.shape
+        _dev_tensor(self.codes, f"{name}.codes", torch.uint8, (E, N, K // 2))
+        _dev_tensor(self.scales, f"{name}.scales", torch.uint8, (E, N, K // 16))
+        _dev_tensor(self.global_scale, f"{name}.global_scale", torch.float32, (E,))
+        return self
+
     def cstruct(self):
+        self.check()
         E, N, K = self.shape
         return NVFP4TensorC(E, N, K, self.codes.data_ptr(), self.scales.data_ptr(),
                             self.global_scale.data_ptr())
@@ -138,8 +168,11 @@ def moe_w4a16_version():
 
 def moe_w4a16_quantize_pack(w, out=None, stream=None):
     """fp32 masters [E, N, K] (device) -> NVFP4Tensor."""
+    _dev_tensor(w, "w", torch.float32)
     E, N, K = w.shape
     out = NVFP4Tensor.empty(E, N, K, w.device) if out is None else out
+    if out.shape != (E, N, K):
+        raise ValueError(f"out: shape {out.shape}, expected {(E, N, K)}")
     st = out.cstruct()
     _check(lib().moe_w4a16_quantize_pack(_ptr(w), E, N, K, ctypes.byref(st), _stream(stream)),
            "moe_w4a16_quantize_pack")
@@ -149,14 +182,19 @@ def moe_w4a16_quantize_pack(w, out=None, stream=None):
 def moe_w4a16_dequantize(t, out=None, stream=None):
     E, N, K = t.shape
     out = torch.empty((E, N, K), dtype=torch.float32, device=t.codes.device) if out is None else out
+    _dev_tensor(out, "out", torch.float32, (E, N, K))
     st = t.cstruct()
     _check(lib().moe_w4a16_dequantize(ctypes.byref(st), _ptr(out), _stream(stream)), "moe_w4a16_dequantize")
     return out
 
 
-def moe_w4a16_validate(t, stream=None):
+def moe_w4a16_validate(t, flag=None, stream=None):
+    """Synchronises; raises MoeError on a bad scale.  `flag`: an optional
+    caller-owned device tensor of at least 4 bytes (allocated here if None)."""
+    flag = torch.empty((4,), dtype=torch.int32, device=t.codes.device) if flag is None else flag
+    _dev_tensor(flag, "flag", min_bytes=4)
     st = t.cstruct()
-    _check(lib().moe_w4a16_validate(ctypes.byref(st), _stream(stream)), "moe_w4a16_validate")
+    _check(lib().moe_w4a16_validate(ctypes.byref(st), _ptr(flag), _stream(stream)), "moe_w4a16_validate")
 
 
 def moe_route_workspace_size(T, E, k):
@@ -186,11 +224,24 @@ class Routing:
                        torch.empty((max(moe_route_workspace_size(T, E, k), 16),), dtype=torch.uint8,
                                    device=device))
 
+    def check(self, T, E, k):
+        i32 = torch.int32
+        _dev_tensor(self.topk_ids, "routing.topk_ids", i32, (T, k))
+        _dev_tensor(self.topk_w, "routing.topk_w", torch.float32, (T, k))
+        _dev_tensor(self.counts, "routing.counts", i32, (E,))
+        _dev_tensor(self.offsets, "routing.offsets", i32, (E + 1,))
+        _dev_tensor(self.sorted_slots, "routing.sorted_slots", i32, (T * k,))
+        _dev_tensor(self.slot_pos, "routing.slot_pos", i32, (T * k,))
+        _dev_tensor(self.ws, "routing.ws", torch.uint8, min_bytes=moe_route_workspace_size(T, E, k))
+        return self
+
 
 def moe_route_topk(logits, k, out=None, stream=None):
     """fp32 logits [T, E] (device) -> Routing."""
+    _dev_tensor(logits, "logits", torch.float32)
     T, E = logits.shape
     r = Routing.empty(T, E, k, logits.device) if out is None else out
+    r.check(T, E, k)
     _check(lib().moe_route_topk(_ptr(logits), T, E, k, _ptr(r.topk_ids), _ptr(r.topk_w), _ptr(r.counts),
                                 _ptr(r.offsets), _ptr(r.sorted_slots), _ptr(r.slot_pos), _ptr(r.ws),
                                 r.ws.numel(), _stream(stream)), "moe_route_topk")
@@ -198,21 +249,8 @@ def moe_route_topk(logits, k, out=None, stream=None):
 
 
 def forward_workspace(T, H, I, E, k, device="cuda"):
-    """A forward workspace, allocated zero-filled (so it is ready for use
-    without moe_w4a16_workspace_init)."""
-    return torch.zeros((max(moe_w4a16_workspace_size(T, H, I, E, k), 256),), dtype=torch.uint8, device=device)
-
-
-def moe_w4a16_workspace_init(ws, stream=None):
-    _check(lib().moe_w4a16_workspace_init(_ptr(ws), ws.numel(), _stream(stream)), "moe_w4a16_workspace_init")
-
-
-def moe_debug_set_decode_wait_limit(polls):
-    lib().moe_debug_set_decode_wait_limit(int(polls))
-
-
-def moe_debug_set_decode_variant(variant):
-    _check(lib().moe_debug_set_decode_variant(int(variant)), "moe_debug_set_decode_variant")
+    """A forward workspace (needs no initialisation)."""
+    return torch.empty((max(moe_w4a16_workspace_size(T, H, I, E, k), 256),), dtype=torch.uint8, device=device)
 
 
 def moe_debug_set_prefill_variant(variant):
@@ -222,11 +260,15 @@ def moe_debug_set_prefill_variant(variant):
 def moe_w4a16_forward(x_bits, gate, up, down, routing, out=None, ws=None, stream=None):
     """bf16 activations (int16/uint16 bit patterns or torch.bfloat16) [T, H] ->
     bf16 bits [T, H] (int16 tensor; view as torch.bfloat16 for values)."""
+    _dev_tensor(x_bits, "x", _BITS16)
     T, H = x_bits.shape
     E, I, _ = gate.shape
     k = routing.topk_ids.shape[1]
+    routing.check(T, E, k)
     out = torch.empty((T, H), dtype=torch.int16, device=x_bits.device) if out is None else out
+    _dev_tensor(out, "out", _BITS16, (T, H))
     ws = forward_workspace(T, H, I, E, k, x_bits.device) if ws is None else ws
+    _dev_tensor(ws, "ws", min_bytes=moe_w4a16_workspace_size(T, H, I, E, k))
     g, u, d = gate.cstruct(), up.cstruct(), down.cstruct()
     _check(lib().moe_w4a16_forward(_ptr(x_bits), T, H, I, E, k, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
                                    _ptr(routing.topk_ids), _ptr(routing.topk_w), _ptr(routing.counts),
@@ -239,12 +281,16 @@ def moe_w4a16_route_forward(logits, x_bits, gate, up, down, k, routing=None, out
     """Route (as moe_route_topk, outputs stored in `routing`) and run the
     layer (with one token the gate/up kernel routes itself).  Returns
     (out, routing)."""
+    _dev_tensor(x_bits, "x", _BITS16)
     T, H = x_bits.shape
     E, I, _ = gate.shape
-    assert logits.shape == (T, E)
+    _dev_tensor(logits, "logits", torch.float32, (T, E))
     routing = Routing.empty(T, E, k, x_bits.device) if routing is None else routing
+    routing.check(T, E, k)
     out = torch.empty((T, H), dtype=torch.int16, device=x_bits.device) if out is None else out
+    _dev_tensor(out, "out", _BITS16, (T, H))
     ws = forward_workspace(T, H, I, E, k, x_bits.device) if ws is None else ws
+    _dev_tensor(ws, "ws", min_bytes=moe_w4a16_workspace_size(T, H, I, E, k))
     g, u, d = gate.cstruct(), up.cstruct(), down.cstruct()
     _check(lib().moe_w4a16_route_forward(_ptr(logits), _ptr(x_bits), T, H, I, E, k, ctypes.byref(g), ctypes.byref(u),
                                          ctypes.byref(d), _ptr(routing.topk_ids), _ptr(routing.topk_w),
@@ -271,10 +317,14 @@ def moe_profile_end(max_names=64):
 def moe_router_logits(x_bits, wr_bits, out=None, stream=None):
     """Router logits: bf16 bits x [T, H] and router weight [E, H] (int16
     tensors) -> fp32 [T, E]."""
+    _dev_tensor(x_bits, "x", _BITS16)
+    _dev_tensor(wr_bits, "wr", _BITS16)
     T, H = x_bits.shape
     E, H2 = wr_bits.shape
-    assert H2 == H
+    if H2 != H:
+        raise ValueError(f"wr: {H2} columns, x has {H}")
     out = torch.empty((T, E), dtype=torch.float32, device=x_bits.device) if out is None else out
+    _dev_tensor(out, "out", torch.float32, (T, E))
     _check(lib().moe_router_logits(_ptr(x_bits), T, H, _ptr(wr_bits), E, _ptr(out), _stream(stream)),
            "moe_router_logits")
     return out
@@ -283,13 +333,17 @@ def moe_router_logits(x_bits, wr_bits, out=None, stream=None):
 def moe_w4a16_linear(x_bits, w, out=None, ws=None, stream=None):
     """Dense projection: bf16 bits [T, K] and an NVFP4 tensor with E = 1,
     shape [1, N, K] -> bf16 bits [T, N] (int16 tensor)."""
+    _dev_tensor(x_bits, "x", _BITS16)
     T, K = x_bits.shape
     E, N, K2 = w.shape
-    assert E == 1 and K2 == K
+    if E != 1 or K2 != K:
+        raise ValueError(f"w: shape {(E, N, K2)}, expected (1, N, {K})")
     out = torch.empty((T, N), dtype=torch.int16, device=x_bits.device) if out is None else out
+    _dev_tensor(out, "out", _BITS16, (T, N))
     if ws is None:
         ws = torch.empty((max(lib().moe_w4a16_linear_workspace_size(max(T, 1), K, N), 256),), dtype=torch.uint8,
                          device=x_bits.device)
+    _dev_tensor(ws, "ws", min_bytes=lib().moe_w4a16_linear_workspace_size(T, K, N))
     c = w.cstruct()
     _check(lib().moe_w4a16_linear(_ptr(x_bits), T, K, N, ctypes.byref(c), _ptr(out), _ptr(ws), ws.numel(),
                                   _stream(stream)), "moe_w4a16_linear")
@@ -299,13 +353,17 @@ def moe_w4a16_linear(x_bits, w, out=None, ws=None, stream=None):
 def moe_w4a16_shared_expert(x_bits, gate, up, down, out=None, ws=None, stream=None):
     """The shared expert (one SwiGLU FFN for every token): bf16 bits [T, H]
     and NVFP4 tensors with E = 1 -> bf16 bits [T, H] (int16 tensor)."""
+    _dev_tensor(x_bits, "x", _BITS16)
     T, H = x_bits.shape
     E, I, _ = gate.shape
-    assert E == 1
+    if E != 1:
+        raise ValueError(f"gate: {E} experts, the shared expert has 1")
     out = torch.empty((T, H), dtype=torch.int16, device=x_bits.device) if out is None else out
+    _dev_tensor(out, "out", _BITS16, (T, H))
     if ws is None:
         ws = torch.empty((max(lib().moe_w4a16_shared_expert_workspace_size(max(T, 1), H, I), 256),),
                          dtype=torch.uint8, device=x_bits.device)
+    _dev_tensor(ws, "ws", min_bytes=lib().moe_w4a16_shared_expert_workspace_size(T, H, I))
     g, u, d = gate.cstruct(), up.cstruct(), down.cstruct()
     _check(lib().moe_w4a16_shared_expert(_ptr(x_bits), T, H, I, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
                                          _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),

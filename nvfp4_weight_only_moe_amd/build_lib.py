@@ -33,9 +33,8 @@ COMMON = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["abi.cpp", "quantize.hip", "route.hip", "moe_decode.hip", "moe_decode_fused.hip",
-           "moe_decode_t1_fused.hip", "moe_decode_t1_gateup.hip", "moe_decode_t1_down.hip",
-           "moe_decode_t8_fused.hip", "moe_decode_t8_gateup.hip", "moe_decode_t8_down.hip", "moe_prefill.hip", "moe_prefill_pipe.hip", "router.hip"]
+SOURCES = ["abi.cpp", "quantize.hip", "route.hip", "moe_decode.hip", "moe_prefill.hip", "moe_prefill_pipe.hip",
+           "router.hip"]
 
 
 def _compile(src, verbose):

@@ -4,6 +4,7 @@
 // contract of each entry point.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -46,14 +47,14 @@ struct ProfRec {
     hipEvent_t start, stop;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};   // read without the mutex by every launch
 int g_prof_max = 0;
 std::vector<ProfRec> g_prof;
 
 }  // namespace
 
 bool prof_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
-    if (!g_prof_on) return false;
+    if (!g_prof_on.load(std::memory_order_relaxed)) return false;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if ((int)g_prof.size() >= g_prof_max) return false;
     ProfRec r{name, nullptr, nullptr};
@@ -81,19 +82,14 @@ moe_status allow_dynamic_lds(const void* kernel, size_t bytes) {
     return MOE_OK;
 }
 
-// Forward workspace: [sync words | h (bf16 [T*k][I]) | y (fp32 [T*k][H]) |
-// route scratch].  The sync words are at a fixed offset so that one
-// workspace serves calls of any shape.
-constexpr size_t kSyncBytes = 256;
-
+// Forward workspace: [h (bf16 [T*k][I]) | y (fp32 [T*k][H]) | route scratch].
 size_t forward_workspace_bytes(int T, int H, int I, int E, int k) {
     const size_t slots = (size_t)T * k;
-    return kSyncBytes + round_up(slots * I * sizeof(uint16_t), kAlign) + round_up(slots * H * sizeof(float), kAlign) +
+    return round_up(slots * I * sizeof(uint16_t), kAlign) + round_up(slots * H * sizeof(float), kAlign) +
            round_up(route_workspace_bytes(T, E, k), kAlign);
 }
 
 struct WsLayout {
-    uint32_t* sync;
     uint16_t* h;
     float* y;
     void* route;
@@ -104,20 +100,8 @@ WsLayout ws_layout(void* d_ws, int T, int H, int I, int k) {
     const size_t slots = (size_t)T * k;
     const size_t hb = round_up(slots * I * sizeof(uint16_t), kAlign);
     const size_t yb = round_up(slots * H * sizeof(float), kAlign);
-    return WsLayout{reinterpret_cast<uint32_t*>(ws), reinterpret_cast<uint16_t*>(ws + kSyncBytes),
-                    reinterpret_cast<float*>(ws + kSyncBytes + hb), ws + kSyncBytes + hb + yb};
+    return WsLayout{reinterpret_cast<uint16_t*>(ws), reinterpret_cast<float*>(ws + hb), ws + hb + yb};
 }
-
-// Decode-shape kernels: 0 = gate/up and down kernels of moe_decode.hip,
-// 1 = one launch for the whole layer (route included when routing here),
-// 2 = the gate/up and down halves of the single-launch kernel as two
-// launches, 3 = the kernels of 0, with the routing of a single token computed
-// by the gate/up kernel (moe_w4a16_route_forward with T == 1; everything else
-// runs 0).  Chosen by moe_debug_set_decode_variant (a benchmarking and test
-// hook); 3 is the default: on MI355X at one token (H 5120, I 1536, 256
-// experts, top-8) it saves the route launch, 32.0 us per layer against 34.6.  Shapes a
-// variant does not cover fall back to 0, then to the grouped-GEMM path.
-int g_decode_variant = 3;
 
 // Grouped-GEMM kernels for larger T: 0 = register-staged (k_grouped_gemm)
 // for both products, 1 = LDS-pipelined (k_gemm_pipe) for both, 2 = chosen
@@ -125,16 +109,17 @@ int g_decode_variant = 3;
 // kernel's 128-row tiles pay off once experts hold a few hundred rows (16K
 // tokens, top-8 of 256 on MI355X: gate/up 4.6 ms against 7.3, down 2.5 ms
 // against 4.1); with few rows per expert (1K tokens: about 32) its padding
-// costs more than it saves.  Chosen by moe_debug_set_prefill_variant.
-int g_prefill_variant = 2;
+// costs more than it saves.  Chosen by moe_debug_set_prefill_variant; a
+// forward reads it once, atomically, when it is called.
+std::atomic<int> g_prefill_variant{2};
 constexpr int64_t kPipeMinRowsPerExpert = 256;
 
 moe_status launch_prefill(const FwdArgs& a, hipStream_t stream) {
     const bool pipe_ok = prefill_pipe_supported(a.T, a.k, a.H, a.I);
     const int64_t slots = (int64_t)a.T * a.k;
     const int64_t per_expert = slots / std::max<int64_t>(1, std::min<int64_t>(a.E, slots));
-    const bool pipe =
-        pipe_ok && (g_prefill_variant == 1 || (g_prefill_variant == 2 && per_expert >= kPipeMinRowsPerExpert));
+    const int variant = g_prefill_variant.load(std::memory_order_relaxed);
+    const bool pipe = pipe_ok && (variant == 1 || (variant == 2 && per_expert >= kPipeMinRowsPerExpert));
     moe_status st = pipe ? launch_gateup_pipe(a, stream) : launch_gateup_grouped(a, stream);
     if (st != MOE_OK) return st;
     st = pipe ? launch_down_pipe(a, stream) : launch_down_grouped(a, stream);
@@ -142,10 +127,7 @@ moe_status launch_prefill(const FwdArgs& a, hipStream_t stream) {
     return launch_combine(a, stream);
 }
 
-moe_status launch_decode_forward(const FwdArgs& a, uint32_t* sync, hipStream_t stream) {
-    if (g_decode_variant == 1 && fused_decode_supported(a.T, a.k, a.H, a.I))
-        return launch_decode_fused(a, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, sync, stream);
-    if (g_decode_variant == 2 && fused_decode_supported(a.T, a.k, a.H, a.I)) return launch_decode_two(a, stream);
+moe_status launch_decode_forward(const FwdArgs& a, hipStream_t stream) {
     if (decode_path_supported(a.T, a.k, a.H, a.I)) return launch_forward_decode(a, stream);
     return launch_prefill(a, stream);
 }
@@ -285,19 +267,22 @@ moe_status moe_w4a16_dequantize(const moe_nvfp4_tensor* t, float* d_w_out, hipSt
     return launch_dequantize(t, d_w_out, stream);
 }
 
-moe_status moe_w4a16_validate(const moe_nvfp4_tensor* t, hipStream_t stream) {
+moe_status moe_w4a16_validate(const moe_nvfp4_tensor* t, void* d_flag, hipStream_t stream) {
     moe_status st = check_tensor_self(t);
     if (st != MOE_OK) return st;
-    uint32_t* d_flag = nullptr;
-    if (hipMalloc(&d_flag, sizeof(uint32_t)) != hipSuccess) return MOE_ERR_HIP;
+    if (!d_flag) return MOE_ERR_WORKSPACE;
+    if (!aligned16(d_flag)) return MOE_ERR_ALIGN;
+    uint32_t* flag_d = static_cast<uint32_t*>(d_flag);
+    if (ranges_overlap(d_flag, sizeof(uint32_t), t->codes, (size_t)t->E * t->N * t->K / 2) ||
+        ranges_overlap(d_flag, sizeof(uint32_t), t->scales, (size_t)t->E * t->N * t->K / 16) ||
+        ranges_overlap(d_flag, sizeof(uint32_t), t->global_scale, (size_t)t->E * sizeof(float)))
+        return MOE_ERR_INVALID_ARG;
+    st = launch_zero_words(flag_d, 1, stream);
+    if (st == MOE_OK) st = launch_validate(t, flag_d, stream);
     uint32_t flag = 0;
-    st = MOE_OK;
-    if (hipMemcpyAsync(d_flag, &flag, sizeof(flag), hipMemcpyHostToDevice, stream) != hipSuccess) st = MOE_ERR_HIP;
-    if (st == MOE_OK) st = launch_validate(t, d_flag, stream);
-    if (st == MOE_OK && hipMemcpyAsync(&flag, d_flag, sizeof(flag), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    if (st == MOE_OK && hipMemcpyAsync(&flag, flag_d, sizeof(flag), hipMemcpyDeviceToHost, stream) != hipSuccess)
         st = MOE_ERR_HIP;
     if (st == MOE_OK && hipStreamSynchronize(stream) != hipSuccess) st = MOE_ERR_HIP;
-    (void)hipFree(d_flag);
     if (st != MOE_OK) return st;
     if (flag & 1u) return MOE_ERR_NONFINITE;
     if (flag & 6u) return MOE_ERR_BAD_SCALE;
@@ -346,7 +331,7 @@ moe_status moe_w4a16_forward(const uint16_t* d_x, int32_t T, int32_t H, int32_t 
     const WsLayout L = ws_layout(d_ws, T, H, I, k);
     const FwdArgs a = make_args(d_x, T, H, I, E, k, gate, up, down, d_topk_ids, d_topk_w, d_counts, d_offsets,
                                 d_sorted_slots, d_slot_pos, d_out, L);
-    return launch_decode_forward(a, L.sync, stream);
+    return launch_decode_forward(a, stream);
 }
 
 moe_status moe_w4a16_route_forward(const float* d_logits, const uint16_t* d_x, int32_t T, int32_t H, int32_t I,
@@ -361,16 +346,13 @@ moe_status moe_w4a16_route_forward(const float* d_logits, const uint16_t* d_x, i
     const WsLayout L = ws_layout(d_ws, T, H, I, k);
     const FwdArgs a = make_args(d_x, T, H, I, E, k, gate, up, down, d_topk_ids, d_topk_w, d_counts, d_offsets,
                                 d_sorted_slots, d_slot_pos, d_out, L);
-    if (g_decode_variant == 1 && fused_decode_supported(T, k, H, I))
-        return launch_decode_fused(a, d_logits, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots,
-                                   d_slot_pos, L.sync, stream);
-    if (g_decode_variant == 3 && T == 1 && decode_path_supported(T, k, H, I))
+    if (T == 1 && decode_path_supported(T, k, H, I))
         return launch_forward_decode_routed(a, d_logits, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots,
                                             d_slot_pos, stream);
     st = launch_route(d_logits, T, E, k, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots, d_slot_pos,
                       L.route, stream);
     if (st != MOE_OK) return st;
-    return launch_decode_forward(a, L.sync, stream);
+    return launch_decode_forward(a, stream);
 }
 
 moe_status moe_router_logits(const uint16_t* d_x, int32_t T, int32_t H, const uint16_t* d_wr, int32_t E,
@@ -468,24 +450,9 @@ moe_status moe_w4a16_shared_expert(const uint16_t* d_x, int32_t T, int32_t H, in
     return launch_prefill(a, stream);
 }
 
-moe_status moe_w4a16_workspace_init(void* d_ws, size_t ws_bytes, hipStream_t stream) {
-    if (!d_ws) return MOE_ERR_WORKSPACE;
-    if (!aligned16(d_ws)) return MOE_ERR_ALIGN;
-    if (ws_bytes < kSyncBytes) return MOE_ERR_WORKSPACE;
-    return launch_zero_words(static_cast<uint32_t*>(d_ws), (int)(kSyncBytes / sizeof(uint32_t)), stream);
-}
-
-void moe_debug_set_decode_wait_limit(int32_t polls) { set_decode_wait_limit(polls); }
-
 moe_status moe_debug_set_prefill_variant(int32_t variant) {
     if (variant < 0 || variant > 2) return MOE_ERR_INVALID_ARG;
-    g_prefill_variant = variant;
-    return MOE_OK;
-}
-
-moe_status moe_debug_set_decode_variant(int32_t variant) {
-    if (variant < 0 || variant > 3) return MOE_ERR_INVALID_ARG;
-    g_decode_variant = variant;
+    g_prefill_variant.store(variant, std::memory_order_relaxed);
     return MOE_OK;
 }
 
@@ -498,13 +465,13 @@ moe_status moe_profile_begin(int32_t max_launches) {
     g_prof.clear();
     g_prof.reserve(max_launches > 0 ? max_launches : 0);
     g_prof_max = max_launches > 0 ? max_launches : 0;
-    g_prof_on = g_prof_max > 0;
+    g_prof_on.store(g_prof_max > 0, std::memory_order_relaxed);
     return MOE_OK;
 }
 
 int32_t moe_profile_end(char (*names)[64], int32_t* counts, double* total_ms, int32_t max) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    g_prof_on = false;
+    g_prof_on.store(false, std::memory_order_relaxed);
     std::vector<std::string> keys;
     std::vector<int32_t> cnt;
     std::vector<double> ms;

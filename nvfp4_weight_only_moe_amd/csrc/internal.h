@@ -38,6 +38,8 @@ moe_status launch_quantize_pack(const float* w, int E, int N, int K, const moe_n
                                 hipStream_t s);
 moe_status launch_dequantize(const moe_nvfp4_tensor* t, float* w_out, hipStream_t s);
 moe_status launch_validate(const moe_nvfp4_tensor* t, uint32_t* d_flag, hipStream_t s);
+// n words set to zero by a fill kernel (graph-safe: no memset node)
+moe_status launch_zero_words(uint32_t* p, int n, hipStream_t s);
 
 // ---- route.hip
 size_t route_workspace_bytes(int T, int E, int k);
@@ -70,15 +72,6 @@ struct FwdArgs {
 
 size_t forward_workspace_bytes(int T, int H, int I, int E, int k);
 bool decode_path_supported(int T, int k, int H, int I);
-// moe_decode_fused.hip: single-launch decode path (route optional: logits
-// non-null routes in the kernel and stores the routing outputs)
-bool fused_decode_supported(int T, int k, int H, int I);
-void set_decode_wait_limit(int polls);
-moe_status launch_decode_fused(const FwdArgs& a, const float* logits, int32_t* ids_out, float* w_out,
-                               int32_t* counts_out, int32_t* offsets_out, int32_t* sorted_out, int32_t* pos_out,
-                               uint32_t* sync, hipStream_t s);
-moe_status launch_decode_two(const FwdArgs& a, hipStream_t s);
-moe_status launch_zero_words(uint32_t* p, int n, hipStream_t s);
 moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s);
 // the same kernels for one always-on expert (E = 1, k = 1, weight 1, tokens
 // in order): no routing arrays are read

@@ -70,8 +70,8 @@ template <bool LINEAR> constexpr int x_stage_tokens() { return LINEAR ? kXTokens
 // go straight to LDS, and the codes of all stages are requested before any
 // is used: stages are computed in order as they land (vector loads complete
 // in issue order).
-// Routing computed by the gate/up kernel itself, for one token (decode
-// variant 3): every workgroup recomputes the token's top-k from its E logits
+// Routing computed by the gate/up kernel itself, for one token
+// (moe_w4a16_route_forward with T == 1): every workgroup recomputes the token's top-k from its E logits
 // and the expert order of the k slots, which replaces the lookup of the
 // routing outputs (one dependent load either way) and saves the route
 // launch; the workgroups of expert column 0 store the routing outputs for the

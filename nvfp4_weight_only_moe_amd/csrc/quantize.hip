@@ -183,6 +183,13 @@ __global__ void __launch_bounds__(kQBlock) k_validate(const uint8_t* __restrict_
     if (f) atomicOr(flag, f);
 }
 
+// Clears n words with vector stores (a fill kernel, not a memset node, so
+// that it is safe inside a captured graph).
+__global__ void k_zero_words(uint32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
 inline int blocks_for(int64_t n, int per) { return (int)((n + per - 1) / per); }
 
 }  // namespace
@@ -205,6 +212,12 @@ moe_status launch_dequantize(const moe_nvfp4_tensor* t, float* w_out, hipStream_
     const int64_t groups = (int64_t)t->N * t->K / 16;
     MOE_LAUNCH("dequantize", k_dequant, dim3(blocks_for(groups, kQBlock), t->E), dim3(kQBlock), 0, s,
                (const uint8_t*)t->codes, (const uint8_t*)t->scales, (const float*)t->global_scale, groups, w_out);
+    return MOE_OK;
+}
+
+moe_status launch_zero_words(uint32_t* p, int n, hipStream_t s) {
+    if (n <= 0) return MOE_OK;
+    MOE_LAUNCH("zero_words", k_zero_words, dim3(blocks_for(n, kQBlock)), dim3(kQBlock), 0, s, p, n);
     return MOE_OK;
 }
 

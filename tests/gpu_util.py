@@ -17,8 +17,6 @@ from oracle import moe as omoe
 from nvfp4_weight_only_moe_amd import binding as B
 from nvfp4_weight_only_moe_amd import workloads as wls
 
-# decode-shape kernel set the library selects by default (moe_debug_set_decode_variant)
-DEFAULT_DECODE_VARIANT = 3
 DEV = "cuda:0"
 PROJ = ((wls.GATE, "gate"), (wls.UP, "up"), (wls.DOWN, "down"))
 THREADS = min(16, os.cpu_count() or 4)
@@ -61,6 +59,72 @@ def compare_out(got, ref, where=""):
     return rel_fro, rel_max, cos, ratio
 
 
+# ------------------------------------------------------------------ guard bands
+GUARD_BYTES = 4096
+GUARD_BYTE = 0xA5
+
+
+class Guarded:
+    """A device buffer between two guard bands of GUARD_BYTES filled with a
+    byte pattern; ``t`` is the caller-visible tensor (contiguous, 256-byte
+    aligned).  ``check`` asserts both bands, and the padding up to the next
+    256-byte boundary, still hold the pattern after the library wrote ``t``:
+    every kernel writes through computed indices, so a stray write shows up
+    here even when it lands where no parity check looks."""
+
+    def __init__(self, shape, dtype, device=DEV):
+        shape = tuple(int(d) for d in shape)
+        nbytes = int(np.prod(shape, dtype=np.int64)) * torch.empty((), dtype=dtype).element_size()
+        self.nbytes = nbytes
+        padded = (nbytes + 255) // 256 * 256
+        self.raw = torch.full((GUARD_BYTES + padded + GUARD_BYTES,), GUARD_BYTE, dtype=torch.uint8, device=device)
+        self.t = self.raw[GUARD_BYTES:GUARD_BYTES + nbytes].view(dtype).view(shape)
+
+    def check(self, where):
+        head = self.raw[:GUARD_BYTES]
+        tail = self.raw[GUARD_BYTES + self.nbytes:]
+        bad_head = int((head != GUARD_BYTE).sum())
+        bad_tail = int((tail != GUARD_BYTE).sum())
+        assert bad_head == 0 and bad_tail == 0, f"{where}: {bad_head} guard bytes before and {bad_tail} after changed"
+
+
+def guarded_routing(T, E, k):
+    """A Routing whose every array (and route scratch) sits between guard bands."""
+    parts = {
+        "topk_ids": Guarded((T, k), torch.int32), "topk_w": Guarded((T, k), torch.float32),
+        "counts": Guarded((E,), torch.int32), "offsets": Guarded((E + 1,), torch.int32),
+        "sorted_slots": Guarded((T * k,), torch.int32), "slot_pos": Guarded((T * k,), torch.int32),
+        "ws": Guarded((max(B.moe_route_workspace_size(T, E, k), 16),), torch.uint8),
+    }
+    r = B.Routing(**{n: g.t for n, g in parts.items()})
+    return r, parts
+
+
+def check_guards(parts, where):
+    for name, g in parts.items():
+        g.check(f"{where}: {name}")
+
+
+def guarded_forward(x_bits, gate, up, down, logits, k, fused):
+    """Route + forward (two calls, or moe_w4a16_route_forward when `fused`)
+    into guarded output, routing and workspace buffers sized exactly as the
+    header states; asserts the guards and returns (out, routing)."""
+    T, H = x_bits.shape
+    E, I, _ = gate.shape
+    r, parts = guarded_routing(T, E, k)
+    parts["out"] = Guarded((T, H), torch.int16)
+    parts["forward_ws"] = Guarded((max(B.moe_w4a16_workspace_size(T, H, I, E, k), 16),), torch.uint8)
+    out, ws = parts["out"].t, parts["forward_ws"].t
+    if fused:
+        B.moe_w4a16_route_forward(logits, x_bits, gate, up, down, k, routing=r, out=out, ws=ws)
+    else:
+        B.moe_route_topk(logits, k, out=r)
+        B.moe_w4a16_forward(x_bits, gate, up, down, r, out=out, ws=ws)
+    torch.cuda.synchronize()
+    check_guards(parts, f"T{T} H{H} I{I} E{E} k{k} {'route_forward' if fused else 'route+forward'}")
+    return out, r
+
+
 # ------------------------------------------------------------------ packing
 def pack_gpu(masters):
     """numpy fp32 [E, N, K] -> NVFP4Tensor packed by the HIP library."""
@@ -93,11 +157,10 @@ class Problem:
     def reference(self, **kw):
         return omoe.moe_forward(self.x, self.layer, self.ids, self.w, **kw)
 
-    def run_gpu(self):
+    def run_gpu(self, fused=False):
+        """Pack on the GPU, then route + forward into guarded buffers."""
         gate, up, down = (pack_gpu(m) for m in self.ms)
-        r = B.moe_route_topk(to_dev(self.logits), self.k)
-        out = B.moe_w4a16_forward(to_dev(self.xb, torch.int16), gate, up, down, r)
-        torch.cuda.synchronize()
+        out, r = guarded_forward(to_dev(self.xb, torch.int16), gate, up, down, to_dev(self.logits), self.k, fused)
         return out, r, (gate, up, down)
 
 
@@ -130,6 +193,31 @@ def full_layer_gpu():
         log(f"full layer: {name} packed ({time.time() - t0:.1f} s)")
     _FULL["gpu"] = packed
     return packed
+
+
+def oracle_forward_parallel(x, layer, ids, w, tokens):
+    """oracle.moe_forward restricted to `tokens`, with the experts' work
+    (dequantize + fp64 FFN) spread over threads and the contributions then
+    added in ascending expert order, as moe_forward adds them: the same
+    oracle arithmetic, faster on a many-core host."""
+    x = np.asarray(x, np.float64)
+    ids = np.asarray(ids)
+    w = np.asarray(w, np.float64)
+    tokens = np.asarray(sorted(set(int(t) for t in tokens)))
+    experts = [int(e) for e in np.unique(ids[tokens].reshape(-1))]
+
+    def one(e):
+        rows, slots = np.nonzero(ids[tokens] == e)
+        toks = tokens[rows]
+        wg, wu, wd = omoe.dequantize_expert(layer, e)
+        return toks, w[toks, slots][:, None] * omoe.expert_ffn(x[toks], wg, wu, wd)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        parts = list(ex.map(one, experts))
+    out = np.zeros_like(x)
+    for toks, contrib in parts:
+        out[toks] += contrib
+    return out
 
 
 _ORACLE_EXPERTS = {}

@@ -94,8 +94,12 @@ def test_quantize_dequantize_validate_argument_errors(L):
     assert L.moe_w4a16_quantize_pack(A + 0x4000000, 2000, 64, 256, ctypes.byref(T_(2000, 64, 256)), None) == -4
     assert L.moe_w4a16_dequantize(ctypes.byref(t), None, None) == -1
     assert L.moe_w4a16_dequantize(ctypes.byref(T_(2, 64, 40)), A, None) == -2
-    assert L.moe_w4a16_validate(None, None) == -1
-    assert L.moe_w4a16_validate(ctypes.byref(T_(0, 64, 256)), None) == -2
+    assert L.moe_w4a16_validate(None, A + 0x4000000, None) == -1
+    assert L.moe_w4a16_validate(ctypes.byref(T_(0, 64, 256)), A + 0x4000000, None) == -2
+    # the flag word is the caller's: required, aligned, and apart from the tensor
+    assert L.moe_w4a16_validate(ctypes.byref(t), None, None) == -7
+    assert L.moe_w4a16_validate(ctypes.byref(t), A + 0x4000004, None) == -3
+    assert L.moe_w4a16_validate(ctypes.byref(t), A + 0x100000, None) == -1    # the first scale byte
 
 
 def test_workspace_sizes(L):
@@ -126,24 +130,19 @@ def test_route_forward_argument_errors(L):
     assert rfwd(L, ws_bytes=16) == -7
 
 
-def test_workspace_init_and_size(L):
-    assert L.moe_w4a16_workspace_init(0, 1 << 20, None) == -7
-    assert L.moe_w4a16_workspace_init(A + 4, 1 << 20, None) == -3
-    assert L.moe_w4a16_workspace_init(A, 128, None) == -7           # smaller than the sync words
-    # the workspace always begins with the 256 sync bytes, then h and y
+def test_forward_workspace_layout_size(L):
+    # h (bf16 [T*k][I]) then y (fp32 [T*k][H]); nothing before them
     T, H, I, E, k = 3, 1024, 512, 16, 4
-    assert L.moe_w4a16_workspace_size(T, H, I, E, k) >= 256 + T * k * I * 2 + T * k * H * 4
+    assert L.moe_w4a16_workspace_size(T, H, I, E, k) == T * k * I * 2 + T * k * H * 4
     # large T also carries the route scratch
     assert L.moe_w4a16_workspace_size(1000, H, I, E, k) >= (
-        256 + 1000 * k * (I * 2 + H * 4) + L.moe_route_workspace_size(1000, E, k))
+        1000 * k * (I * 2 + H * 4) + L.moe_route_workspace_size(1000, E, k))
 
 
-def test_decode_variant_hook(L):
-    assert L.moe_debug_set_decode_variant(4) == -1
-    assert L.moe_debug_set_decode_variant(-1) == -1
-    for v in (0, 1, 2, 3):
-        assert L.moe_debug_set_decode_variant(v) == 0
-    assert L.moe_debug_set_decode_variant(3) == 0    # the default
+def test_removed_entry_points_are_gone(L):
+    # the single-launch decode variant and its hooks were retired
+    for name in ("moe_w4a16_workspace_init", "moe_debug_set_decode_variant", "moe_debug_set_decode_wait_limit"):
+        assert not hasattr(L, name), name
 
 
 def test_prefill_variant_hook(L):

@@ -1,20 +1,23 @@
 """GPU parity: the layer forward against the oracle on small seeded problems
 (decode path: T <= 8 with H % 1024 == 0 and I % 512 == 0; grouped-GEMM path
-otherwise), ragged and skewed routing, edge cases, determinism."""
+otherwise), ragged and skewed routing, experts long enough to span several
+scheduling groups of row tiles, edge cases, determinism.  Every output,
+routing array and workspace is allocated between guard bands that must stay
+untouched (gpu_util.Guarded)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_util import DEFAULT_DECODE_VARIANT, DEV, Problem, bf16_bits_to_f64, compare_out, log, to_dev
+from gpu_util import DEV, Problem, bf16_bits_to_f64, compare_out, guarded_forward, log, to_dev
 from nvfp4_weight_only_moe_amd import binding as B
 from nvfp4_weight_only_moe_amd import workloads as wls
 
 pytestmark = pytest.mark.gpu
 
 
-def run_and_compare(p, where):
-    out, r, _ = p.run_gpu()
+def run_and_compare(p, where, fused=False):
+    out, r, _ = p.run_gpu(fused)
     assert np.array_equal(r.topk_ids.cpu().numpy(), p.ids)
     got = bf16_bits_to_f64(out)
     ref = p.reference()
@@ -52,8 +55,9 @@ def test_tiny_workload():
     (257, 256, 256, 4, 2, 8),      # 128-row tiles, several row tiles per expert
     (40, 768, 256, 1, 1, 9),       # E = 1, k = 1
 ])
-def test_random_shapes(T, H, I, E, k, seed):
-    run_and_compare(Problem(T, H, I, E, k, seed), f"T{T}-H{H}-I{I}-E{E}-k{k}")
+@pytest.mark.parametrize("fused", [False, True])
+def test_random_shapes(T, H, I, E, k, seed, fused):
+    run_and_compare(Problem(T, H, I, E, k, seed), f"T{T}-H{H}-I{I}-E{E}-k{k}", fused)
 
 
 @pytest.mark.parametrize("T,H,I", [(6, 1024, 512), (300, 256, 128)])
@@ -136,7 +140,7 @@ def test_hip_graph_replay_matches_eager(T, H, I):
     other = B.moe_route_topk(to_dev(p.logits[::-1].copy()), k)
     for i in range(4):
         out.fill_(i + 1)
-        ws[256:].fill_(0xAB)    # everything but the sync words, which calls keep at zero
+        ws.fill_(0xAB)          # the workspace needs no initialisation
         B.moe_w4a16_forward(xb, gate, up, down, other)      # unrelated eager work
         g.replay()
         torch.cuda.synchronize()
@@ -144,15 +148,6 @@ def test_hip_graph_replay_matches_eager(T, H, I):
 
 
 # ------------------------------------------------------------------ route + forward in one call
-@pytest.fixture
-def decode_variant(request):
-    """Select the decode-shape kernels (moe_debug_set_decode_variant) for one
-    test; the default is restored afterwards."""
-    B.moe_debug_set_decode_variant(request.param)
-    yield request.param
-    B.moe_debug_set_decode_variant(DEFAULT_DECODE_VARIANT)
-
-
 DECODE_CASES = [
     (1, 1024, 512, 8, 2, 70),
     (1, 2048, 1536, 8, 6, 71),
@@ -162,21 +157,17 @@ DECODE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("decode_variant", [0, 1, 2, 3], indirect=True)
 @pytest.mark.parametrize("T,H,I,E,k,seed", DECODE_CASES + [(40, 512, 256, 16, 4, 75)])
-def test_route_forward_matches_route_then_forward(T, H, I, E, k, seed, decode_variant):
+def test_route_forward_matches_route_then_forward(T, H, I, E, k, seed):
     """moe_w4a16_route_forward stores exactly moe_route_topk's outputs and
-    exactly moe_w4a16_forward's result (with variants 1 and 3 the route runs
-    inside the layer's kernels), for every decode variant, and matches the
-    oracle."""
+    exactly moe_w4a16_forward's result (with one token the route runs inside
+    the gate/up kernel), and matches the oracle."""
     p = Problem(T, H, I, E, k, seed)
     gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
     lg, xb = to_dev(p.logits), to_dev(p.xb, torch.int16)
-    log(f"route_forward T{T} H{H} I{I} E{E} k{k} decode variant {decode_variant}")
-    r_ref = B.moe_route_topk(lg, k)
-    out_ref = B.moe_w4a16_forward(xb, gate, up, down, r_ref)
-    out, r = B.moe_w4a16_route_forward(lg, xb, gate, up, down, k)
-    torch.cuda.synchronize()
+    log(f"route_forward T{T} H{H} I{I} E{E} k{k}")
+    out_ref, r_ref = guarded_forward(xb, gate, up, down, lg, k, fused=False)
+    out, r = guarded_forward(xb, gate, up, down, lg, k, fused=True)
     for name in ("topk_ids", "topk_w", "counts", "offsets", "sorted_slots", "slot_pos"):
         assert torch.equal(getattr(r, name), getattr(r_ref, name)), name
     assert np.array_equal(r.topk_ids.cpu().numpy(), p.ids)
@@ -184,11 +175,10 @@ def test_route_forward_matches_route_then_forward(T, H, I, E, k, seed, decode_va
     compare_out(bf16_bits_to_f64(out), p.reference(), f"route_forward-T{T}")
 
 
-@pytest.mark.parametrize("decode_variant", [0, 1, 3], indirect=True)
 @pytest.mark.parametrize("E", [64, 256])
-def test_route_forward_ties(E, decode_variant):
+def test_route_forward_ties(E):
     """One token whose logits hold many exact ties (integers): the routing
-    computed inside the layer's kernels picks the same experts, in the same
+    computed inside the gate/up kernel picks the same experts, in the same
     order, as moe_route_topk and the oracle."""
     T, H, I, k = 1, 1024, 512, 8
     lg_np = np.random.default_rng(E).integers(-2, 3, size=(T, E)).astype(np.float32)
@@ -196,48 +186,18 @@ def test_route_forward_ties(E, decode_variant):
     p = Problem(T, H, I, E, k, 300 + E, logits=lg_np)
     gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
     lg, xb = to_dev(p.logits), to_dev(p.xb, torch.int16)
-    r_ref = B.moe_route_topk(lg, k)
-    out_ref = B.moe_w4a16_forward(xb, gate, up, down, r_ref)
-    out, r = B.moe_w4a16_route_forward(lg, xb, gate, up, down, k)
-    torch.cuda.synchronize()
+    out_ref, r_ref = guarded_forward(xb, gate, up, down, lg, k, fused=False)
+    out, r = guarded_forward(xb, gate, up, down, lg, k, fused=True)
     for name in ("topk_ids", "topk_w", "counts", "offsets", "sorted_slots", "slot_pos"):
         assert torch.equal(getattr(r, name), getattr(r_ref, name)), name
     assert np.array_equal(r.topk_ids.cpu().numpy(), p.ids)
     assert torch.equal(out, out_ref)
 
 
-@pytest.mark.parametrize("decode_variant", [1], indirect=True)
-@pytest.mark.parametrize("T,H,I,E,k,seed", DECODE_CASES[:3])
-def test_decode_local_h_path_is_bit_identical(T, H, I, E, k, seed, decode_variant):
-    """With the hand-off wait limit at 0 every workgroup computes all of h
-    itself (the path taken when the grid is not fully resident); the result
-    is bit-identical to the normal hand-off."""
-    p = Problem(T, H, I, E, k, seed)
-    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
-    lg, xb = to_dev(p.logits), to_dev(p.xb, torch.int16)
-    out_ref, _ = B.moe_w4a16_route_forward(lg, xb, gate, up, down, k)
-    torch.cuda.synchronize()
-    ws = B.forward_workspace(T, H, I, E, k, DEV)
-    try:
-        B.moe_debug_set_decode_wait_limit(0)
-        outs = [B.moe_w4a16_route_forward(lg, xb, gate, up, down, k, ws=ws)[0] for _ in range(2)]
-        torch.cuda.synchronize()
-    finally:
-        B.moe_debug_set_decode_wait_limit(1 << 20)
-    for o in outs:
-        assert torch.equal(o, out_ref)
-    # the workspace is still good for the normal path afterwards
-    again, _ = B.moe_w4a16_route_forward(lg, xb, gate, up, down, k, ws=ws)
-    torch.cuda.synchronize()
-    assert torch.equal(again, out_ref)
-
-
-@pytest.mark.parametrize("decode_variant", [1, 2, 3], indirect=True)
-def test_workspace_reused_across_problems(decode_variant):
+def test_workspace_reused_across_problems():
     """One workspace serves consecutive calls with different inputs, routings
-    and shapes: no call reads another call's intermediate values, and
-    moe_w4a16_workspace_init restores a workspace whose sync words were
-    overwritten."""
+    and shapes, and garbage left in it between calls changes nothing: no
+    call reads a value it did not write in the same call."""
     cases = [(1, 1024, 512, 16, 4, 80), (8, 1024, 512, 16, 4, 81), (3, 2048, 512, 16, 4, 82),
              (1, 1024, 512, 16, 4, 83), (50, 1024, 512, 16, 4, 84), (2, 1024, 512, 16, 4, 85)]
     ws = B.forward_workspace(50, 2048, 512, 16, 4, DEV)
@@ -248,36 +208,12 @@ def test_workspace_reused_across_problems(decode_variant):
         fresh, _ = B.moe_w4a16_route_forward(to_dev(p.logits), to_dev(p.xb, torch.int16), *packed, k)
         probs.append((p, packed, fresh))
     torch.cuda.synchronize()
-    for rnd in range(2):
+    for rnd, fill in enumerate((0x00, 0x5A, 0xFF)):
+        ws.fill_(fill)
         for p, packed, fresh in probs:
             out, _ = B.moe_w4a16_route_forward(to_dev(p.logits), to_dev(p.xb, torch.int16), *packed, p.k, ws=ws)
             torch.cuda.synchronize()
             assert torch.equal(out, fresh), f"round {rnd} T{p.T} H{p.H}"
-        ws.fill_(0x5A)
-        B.moe_w4a16_workspace_init(ws)
-
-
-@pytest.mark.parametrize("T,H,I,E,k,seed", DECODE_CASES)
-def test_decode_variants_agree(T, H, I, E, k, seed):
-    """The decode-shape kernel sets each match the oracle, and agree with
-    one another to the forward's tolerance."""
-    p = Problem(T, H, I, E, k, seed)
-    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
-    lg, xb = to_dev(p.logits), to_dev(p.xb, torch.int16)
-    ref = p.reference()
-    outs = []
-    try:
-        for v in (0, 1, 2, 3):
-            B.moe_debug_set_decode_variant(v)
-            out, _ = B.moe_w4a16_route_forward(lg, xb, gate, up, down, k)
-            torch.cuda.synchronize()
-            got = bf16_bits_to_f64(out)
-            compare_out(got, ref, f"variant {v} T{T}")
-            outs.append(got)
-    finally:
-        B.moe_debug_set_decode_variant(DEFAULT_DECODE_VARIANT)
-    for v in (1, 2, 3):
-        compare_out(outs[v], outs[0], f"variant {v} vs 0")
 
 
 PREFILL_CASES = [
@@ -305,8 +241,7 @@ def test_prefill_variants_agree(T, H, I, E, k, seed):
         for v in (0, 1, 2):
             B.moe_debug_set_prefill_variant(v)
             log(f"prefill variant {v} T{T} H{H} I{I} E{E} k{k}")
-            out, _ = B.moe_w4a16_route_forward(lg, xb, gate, up, down, k)
-            torch.cuda.synchronize()
+            out, _ = guarded_forward(xb, gate, up, down, lg, k, fused=True)
             got = bf16_bits_to_f64(out)
             compare_out(got, ref, f"prefill variant {v} T{T}")
             outs.append(got)
@@ -314,3 +249,48 @@ def test_prefill_variants_agree(T, H, I, E, k, seed):
         B.moe_debug_set_prefill_variant(2)
     for v in (1, 2):
         compare_out(outs[v], outs[0], f"prefill variant {v} vs 0")
+
+
+# Experts long enough that the grouped GEMMs' tile numbering (an expert's row
+# tiles in scheduling groups of 8 x all column tiles, then a tail group) runs
+# through whole groups, every offset inside a group and the tail: one expert
+# is made hot (+40 on its logit), so it holds every token.  Gate/up and down
+# both have two column tiles.  Per case: (T, H, I, E, k, seed, register-staged
+# row tile that variant 0 picks by the mean rows per touched expert).
+LONG_EXPERT_CASES = [
+    (2200, 1024, 512, 4, 2, 110, 128),     # 17+ tiles of 128: 2 groups + tail (both kernels)
+    (2100, 512, 512, 72, 2, 111, 64),      # 33 tiles of 64: 4 groups + tail; 16+ of 128
+    (1500, 512, 512, 200, 2, 112, 32),     # 47 tiles of 32: 5 groups + tail; 11+ of 128
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,seed,bm", LONG_EXPERT_CASES)
+def test_prefill_long_expert_every_tile(T, H, I, E, k, seed, bm):
+    """Every token compared against the oracle, for every grouped-GEMM kernel
+    choice, on experts that span several groups of 8 row tiles."""
+    r = np.random.default_rng(seed)
+    lg_np = r.standard_normal((T, E)).astype(np.float32)
+    hot = 1
+    lg_np[:, hot] += 40.0
+    p = Problem(T, H, I, E, k, seed, logits=lg_np)
+    slots = T * k
+    avg = slots // min(E, slots)
+    assert (avg <= 16) == (bm == 32) and (16 < avg <= 64) == (bm == 64), "variant 0 row tile"
+    counts = np.bincount(p.ids.ravel(), minlength=E)
+    assert counts[hot] == T and counts[hot] >= 2 * 8 * bm + 1, counts[hot]
+    assert counts[hot] >= 8 * 128 + 1                          # the pipelined kernel's 128-row tiles too
+    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
+    lg, xb = to_dev(p.logits), to_dev(p.xb, torch.int16)
+    ref = p.reference()
+    try:
+        for v in (0, 1, 2):
+            B.moe_debug_set_prefill_variant(v)
+            out, _ = guarded_forward(xb, gate, up, down, lg, k, fused=True)
+            got = bf16_bits_to_f64(out)
+            compare_out(got, ref, f"long expert T{T} E{E} variant {v}")
+            # rows of the hot expert, row tile by row tile: each tile's worst row
+            err = np.abs(got - ref).max(axis=1) / np.abs(ref).max()
+            tiles = [err[i:i + bm].max() for i in range(0, T, bm)]
+            assert max(tiles) <= 1e-2, (v, int(np.argmax(tiles)))
+    finally:
+        B.moe_debug_set_prefill_variant(2)
