@@ -356,3 +356,201 @@ def pin_shared_expert_textbook(seed=0, H=64, I=32, T=5):
     assert torch.allclose(torch.from_numpy(out), ref, rtol=1e-12, atol=1e-14)
     routed = omoe.moe_forward(x, layer, np.zeros((T, 1), np.int32), np.ones((T, 1)))
     assert np.array_equal(out, routed)
+
+
+# ---------------------------------------------------------------- W4A4 (activations in NVFP4 too)
+from oracle import w4a4 as ow4  # noqa: E402
+
+
+def _e4m3_bits_torch(x):
+    """E4M3 bytes of non-negative fp32 values by torch's conversion, with the
+    saturation at 448 applied first (torch maps >= 464 to NaN)."""
+    x = np.minimum(np.asarray(x, np.float32), np.float32(448.0))
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _e4m3_value_torch(b):
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(b, np.uint8))).view(
+        torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
+def _bruteforce_act_quant(row, input_scale):
+    """One activation row -> its dequantized fp32 values, element by element:
+    scale by torch's E4M3 conversion, code by a nearest search over the eight
+    magnitudes (ties to the even code), sign copied from the quotient."""
+    s_in = np.float32(input_scale)
+    out = []
+    for j in range(0, len(row), 16):
+        grp = [np.float32(v) for v in row[j:j + 16]]
+        amax = max(abs(v) for v in grp)
+        s_f = np.float32(np.float32(amax / np.float32(6.0)) / s_in)
+        s_q = _e4m3_value_torch(_e4m3_bits_torch([s_f]))[0]
+        d = np.float32(s_q * s_in)
+        for v in grp:
+            if d == 0:
+                out.append(0.0)
+                continue
+            q = np.float32(v / d)
+            dist = [abs(abs(float(q)) - m) for m in E2M1_TABLE]
+            best = [i for i, dd in enumerate(dist) if dd == min(dist)]
+            c = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+            mag = E2M1_TABLE[c]
+            val = np.float32(np.float32(mag * s_q) * s_in)
+            out.append(-float(val) if np.signbit(q) else float(val))
+    return out
+
+
+def pin_act_exact_roundtrip(seed=0):
+    """Activations built as code * E4M3 scale * input_scale (a +-6 code in
+    every group, one group at scale 448) quantize back to exactly those codes
+    and scales under that input scale, and dequantize to the same bits."""
+    a, codes, sb, g = representable_tensor(seed)       # g = 2^-12 plays the input scale
+    packed, scales = ow4.quantize_activations(a, g)
+    assert np.array_equal(scales, sb)
+    assert np.array_equal(onv.unpack_codes(packed), codes)
+    back = ow4.dequantize_activations(packed, scales, g)
+    assert np.array_equal(back.view(np.uint32), a.view(np.uint32))
+    # the same tensor under twice the input scale: every scale byte halves
+    # its value (one binade down), codes unchanged -- the scale is used, once
+    p2, s2 = ow4.quantize_activations(a, np.float32(2 * g))
+    normal = np.repeat(sb >= 0x10, 16, axis=1)        # groups whose halved scale stays normal
+    assert np.array_equal(onv.unpack_codes(p2)[normal], codes[normal])
+    assert np.array_equal(_e4m3_value_torch(s2[sb >= 0x10]) * 2, _e4m3_value_torch(sb[sb >= 0x10]))
+
+
+def pin_act_scale_rule(seed=0, input_scale=np.float32(6.0 / 2688.0)):
+    """Group scales of random activations against torch's E4M3 conversion of
+    (amax / 6) / input_scale, and every dequantized value against the
+    element-by-element brute force."""
+    r = np.random.default_rng(seed)
+    a = r.standard_normal((6, 96)).astype(np.float32)
+    a[1, :16] = 0.0
+    a[2, 16:32] = np.float32(1e-4) * a[2, 16:32]             # small-amax group
+    a[3, 40] = np.float32(50.0)                                # beyond 6 * 448 * s: saturates
+    packed, scales = ow4.quantize_activations(a, input_scale)
+    amax_g = np.abs(a).reshape(6, 6, 16).max(axis=2)
+    s_f = (amax_g / np.float32(6)) / np.float32(input_scale)
+    assert np.array_equal(scales, _e4m3_bits_torch(s_f))
+    got = ow4.dequantize_activations(packed, scales, input_scale)
+    for i in range(a.shape[0]):
+        assert got[i].tolist() == _bruteforce_act_quant(a[i], input_scale), i
+
+
+def pin_input_scale_refusal():
+    """Missing, zero, negative and non-finite input scales are refused, by the
+    quantizer and by the layer (the unset-scale fault)."""
+    x = np.ones((2, 32), np.float32)
+    layer = _pack_layer([np.full((1, 32, 32), 0.01, np.float32)] * 3)
+    ids, w = np.zeros((2, 1), np.int32), np.ones((2, 1))
+    for bad in (None, 0.0, -0.0, -1.0, float("nan"), float("inf"), float("-inf")):
+        for call in (lambda: ow4.quantize_activations(x, bad),
+                     lambda: ow4.moe_forward_w4a4(x, layer, ids, w, bad, 1.0),
+                     lambda: ow4.moe_forward_w4a4(x, layer, ids, w, 1.0, bad)):
+            try:
+                call()
+            except ValueError:
+                continue
+            raise AssertionError(f"input scale {bad!r} accepted")
+
+
+def pin_placeholder_underflow():
+    """The placeholder input scale 1.0 the pages report: a group whose
+    amax / 6 falls below half the smallest E4M3 step (2^-10) gets scale 0 and
+    all-zero activations, so a token of small activations yields an exactly
+    zero layer output; a calibrated scale (amax / 2688) keeps it, close to
+    the W4A16 output."""
+    r = np.random.default_rng(3)
+    H, I = 64, 32
+    ms = [(0.05 * r.standard_normal((1,) + s)).astype(np.float32) for s in ((I, H), (I, H), (H, I))]
+    layer = _pack_layer(ms)
+    x = (np.float32(5e-4) * r.standard_normal((1, H))).astype(np.float32)   # amax / 6 < 2^-10
+    ids, w = np.zeros((1, 1), np.int32), np.ones((1, 1))
+    packed, scales = ow4.quantize_activations(x, 1.0)
+    assert not scales.any() and not (onv.unpack_codes(packed) & 7).any()
+    assert not ow4.moe_forward_w4a4(x, layer, ids, w, 1.0, 1.0).any()
+    cal = np.float32(np.max(np.abs(x)) / np.float32(2688.0))
+    y = ow4.moe_forward_w4a4(x, layer, ids, w, cal, 1.0e-6)
+    ref = omoe.moe_forward(x, layer, ids, w)
+    assert np.linalg.norm(y) > 0
+    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 0.35
+
+
+def pin_w4a4_representable_x(seed=0):
+    """Activations exactly representable under their input scale pass the
+    quantizer unchanged, so the W4A4 gate/up pre-activations and h equal the
+    W4A16 layer's on the same x."""
+    r = np.random.default_rng(seed)
+    H, I = 96, 32
+    xa, _, _, g = representable_tensor(seed, n=3, k=H)
+    ms = [(0.05 * r.standard_normal((1,) + s)).astype(np.float32) for s in ((I, H), (I, H), (H, I))]
+    layer = _pack_layer(ms)
+    wg, wu, wd = omoe.dequantize_expert(layer, 0)
+    xq = ow4.fake_quantize(xa, g)
+    assert np.array_equal(xq.view(np.uint32), xa.view(np.uint32))
+    _, h = ow4.expert_ffn_w4a4(xq, wg, wu, wd, np.float32(1.0), return_h=True)
+    x64 = xa.astype(np.float64)
+    a, b = x64 @ wg.astype(np.float64).T, x64 @ wu.astype(np.float64).T
+    assert np.array_equal(h, a / (1.0 + np.exp(-a)) * b)
+
+
+def pin_w4a4_bruteforce(seed=0, H=64, I=64, E=4, k=2, T=16, tol=1e-12):
+    """Per-token pure-Python loops (their own activation quantizer, math.fsum
+    products) against the vectorised W4A4 oracle on a tiny layer."""
+    r = np.random.default_rng(seed)
+    ms = [(0.05 * r.standard_normal((E,) + s)).astype(np.float32) for s in ((I, H), (I, H), (H, I))]
+    layer = _pack_layer(ms)
+    x = r.standard_normal((T, H)).astype(np.float32)
+    lg = r.standard_normal((T, E)).astype(np.float32)
+    ids, w = ort.route_topk(lg, k)
+    sx, sh = np.float32(5.0 / 2688.0), np.float32(3.0 / 2688.0)
+    out = ow4.moe_forward_w4a4(x, layer, ids, w, sx, sh)
+    deq = {}
+    for t in range(T):
+        xq = _bruteforce_act_quant(x[t], sx)
+        ref = [0.0] * H
+        for j in range(k):
+            e = int(ids[t, j])
+            if e not in deq:
+                deq[e] = [a.astype(np.float64).tolist() for a in omoe.dequantize_expert(layer, e)]
+            wg, wu, wd = deq[e]
+            hvec = []
+            for i in range(I):
+                a = math.fsum(xq[q] * wg[i][q] for q in range(H))
+                b = math.fsum(xq[q] * wu[i][q] for q in range(H))
+                hvec.append(np.float32(a / (1.0 + math.exp(-a)) * b))
+            hq = _bruteforce_act_quant(hvec, sh)
+            for n in range(H):
+                ref[n] += float(w[t, j]) * math.fsum(hq[i] * wd[n][i] for i in range(I))
+        err = max(abs(a - b) for a, b in zip(out[t], ref))
+        assert err <= tol * max(max(abs(v) for v in ref), 1e-300), (t, err)
+
+
+def pin_w4a4_magnitude(seed=0, H=128, I=64, E=4, k=2, T=16):
+    """The W4A4 output keeps the unquantized layer's magnitude (norm ratio in
+    [0.8, 1.25]) and differs from the W4A16 output by the activation
+    quantization error -- clearly nonzero, well below the signal."""
+    r = np.random.default_rng(seed)
+    ms = [(0.02 * r.standard_normal((E,) + s)).astype(np.float32) for s in ((I, H), (I, H), (H, I))]
+    layer = _pack_layer(ms)
+    x = r.standard_normal((T, H)).astype(np.float32)
+    ids, w = ort.route_topk(r.standard_normal((T, E)).astype(np.float32), k)
+    sx = np.float32(np.max(np.abs(x)) / np.float32(2688.0))
+    h_amax = 0.0
+    for e in range(E):
+        wg, wu, _ = omoe.dequantize_expert(layer, e)
+        a, b = x.astype(np.float64) @ wg.T.astype(np.float64), x.astype(np.float64) @ wu.T.astype(np.float64)
+        h_amax = max(h_amax, float(np.max(np.abs(a / (1 + np.exp(-a)) * b))))
+    sh = np.float32(np.float32(h_amax) / np.float32(2688.0))
+    y4 = ow4.moe_forward_w4a4(x, layer, ids, w, sx, sh)
+    y16 = omoe.moe_forward(x, layer, ids, w)
+    x64 = x.astype(np.float64)
+    ref = np.zeros_like(x64)
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            ref[t] += w[t, j] * omoe.expert_ffn(x64[t:t + 1], ms[0][e], ms[1][e], ms[2][e])[0]
+    ratio = float(np.linalg.norm(y4) / np.linalg.norm(ref))
+    assert 0.8 <= ratio <= 1.25, ratio
+    d = float(np.linalg.norm(y4 - y16) / np.linalg.norm(y16))
+    assert 0.01 <= d <= 0.3, d
+    return ratio, d

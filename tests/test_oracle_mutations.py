@@ -179,3 +179,107 @@ def test_planted_mistake_is_caught(name, monkeypatch):
         monkeypatch.setattr(mod, attr, fn)
     with pytest.raises((AssertionError, ValueError)):
         _all_pins()
+
+
+# ---------------------------------------------------------------- the W4A4 variant
+from oracle import w4a4 as ow4  # noqa: E402
+
+
+def _all_w4a4_pins():
+    pins.pin_act_exact_roundtrip(0)
+    pins.pin_act_scale_rule(0)
+    pins.pin_input_scale_refusal()
+    pins.pin_placeholder_underflow()
+    pins.pin_w4a4_representable_x()
+    pins.pin_w4a4_bruteforce()
+    pins.pin_w4a4_magnitude()
+
+
+_orig_qact = ow4.quantize_activations
+_orig_dqact = ow4.dequantize_activations
+_orig_fq = ow4.fake_quantize
+_orig_ffn4 = ow4.expert_ffn_w4a4
+
+
+def _qact_scale_ignored(a, input_scale):
+    ow4.check_input_scale(input_scale)
+    return _orig_qact(a, 1.0)
+
+
+def _dqact_scale_ignored(packed, scales, input_scale):
+    return _orig_dqact(packed, scales, 1.0)
+
+
+def _dqact_scale_twice(packed, scales, input_scale):
+    return (_orig_dqact(packed, scales, input_scale) * np.float32(input_scale)).astype(np.float32)
+
+
+def _fq_identity(a, input_scale):
+    ow4.check_input_scale(input_scale)
+    return np.asarray(a, np.float32)
+
+
+def _ffn4_h_unquantized(xq, wg, wu, wd, input_scale_h, return_h=False):
+    x = np.asarray(xq, np.float64)
+    a = x @ np.asarray(wg, np.float64).T
+    b = x @ np.asarray(wu, np.float64).T
+    h = a / (1 + np.exp(-a)) * b
+    y = h @ np.asarray(wd, np.float64).T
+    return (y, h) if return_h else y
+
+
+def _ffn4_h_via_bf16(xq, wg, wu, wd, input_scale_h, return_h=False):
+    x = np.asarray(xq, np.float64)
+    a = x @ np.asarray(wg, np.float64).T
+    b = x @ np.asarray(wu, np.float64).T
+    h = a / (1 + np.exp(-a)) * b
+    hb = omoe._bf16_round(h).astype(np.float32)
+    y = _orig_fq(hb, input_scale_h).astype(np.float64) @ np.asarray(wd, np.float64).T
+    return (y, h) if return_h else y
+
+
+def _forward4_h_with_x_scale(x, layer, ids, weights, input_scale_x, input_scale_h, tokens=None):
+    return _orig_fwd4(x, layer, ids, weights, input_scale_x, input_scale_x, tokens)
+
+
+_orig_fwd4 = ow4.moe_forward_w4a4
+
+
+def _qact_strided_groups(a, input_scale):
+    # a reshape-order slip: group j takes k = j, j + K/16, j + 2K/16, ...
+    a = np.asarray(a, np.float32)
+    k = a.shape[1]
+    idx = np.arange(k).reshape(16, k // 16).T.ravel()
+    p, s = _orig_qact(np.ascontiguousarray(a[:, idx]), input_scale)
+    codes = np.empty((a.shape[0], k), np.uint8)
+    codes[:, idx] = onv.unpack_codes(p)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8), s
+
+
+def _check_scale_accepts_anything(s, name="input_scale"):
+    return np.float32(1.0 if s is None else s)
+
+
+W4A4_MUTATIONS = {
+    "act-input-scale-ignored": [(ow4, "quantize_activations", _qact_scale_ignored),
+                                (ow4, "dequantize_activations", _dqact_scale_ignored)],
+    "act-dequant-scale-applied-twice": [(ow4, "dequantize_activations", _dqact_scale_twice)],
+    "activations-not-quantized": [(ow4, "fake_quantize", _fq_identity)],
+    "h-not-quantized": [(ow4, "expert_ffn_w4a4", _ffn4_h_unquantized)],
+    "h-rounded-to-bf16-before-quantization": [(ow4, "expert_ffn_w4a4", _ffn4_h_via_bf16)],
+    "h-quantized-with-the-x-scale": [(ow4, "moe_forward_w4a4", _forward4_h_with_x_scale)],
+    "act-groups-strided": [(ow4, "quantize_activations", _qact_strided_groups)],
+    "zero-input-scale-accepted": [(ow4, "check_input_scale", _check_scale_accepts_anything)],
+}
+
+
+def test_unmutated_w4a4_oracle_passes_all_pins():
+    _all_w4a4_pins()
+
+
+@pytest.mark.parametrize("name", sorted(W4A4_MUTATIONS))
+def test_planted_w4a4_mistake_is_caught(name, monkeypatch):
+    for mod, attr, fn in W4A4_MUTATIONS[name]:
+        monkeypatch.setattr(mod, attr, fn)
+    with pytest.raises((AssertionError, ValueError)):
+        _all_w4a4_pins()
