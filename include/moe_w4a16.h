@@ -213,6 +213,45 @@ moe_status moe_w4a16_route_forward(const float *d_logits, const uint16_t *d_x,
                                    hipStream_t stream);
 
 /*
+ * The W4A4 NVFP4 variant: the stock routed experts of the NVIDIA release keep
+ * W4A4 NVFP4 -- activations quantized to NVFP4 as well -- with a per-tensor
+ * activation scale (input_scale) in the checkpoint ("GLM-5.3-Flash-NVFP4-h --
+ * W4A16 dense-side quantization", its opening; "GLM-5.3-Flash · 512k + MTP +
+ * vision ...", "Input-scales provenance").  The pages print no formula; the
+ * reading taken: an activation row is quantized exactly like a weight row --
+ * per 16-group s = E4M3((amax / 6) / input_scale), code =
+ * E2M1(v / (E4M3(s) * input_scale)), correctly rounded fp32 steps -- with a
+ * static FP32 input scale for the gate/up input x and one for the down input
+ * h (h quantized from its fp32 value).  A missing scale read as 0 zeroes every
+ * expert output ("GLM-5.3-Flash on Blackwell", "The model loaded, served an
+ * API, and produced garbage"), so every call below refuses an input scale
+ * that is not finite (MOE_ERR_NONFINITE) or not > 0 (MOE_ERR_BAD_SCALE)
+ * before anything else, even with T == 0.
+ *
+ * moe_nvfp4_quantize_activations: bf16 activations [T][K] (K % 32 == 0) ->
+ *   d_codes u8 [T][K/2] (byte i = code(2i) | code(2i+1) << 4) and d_scales u8
+ *   [T][K/16] (E4M3 bytes), bit-identical to the definition above.  The
+ *   three buffers must not overlap.  Asynchronous; allocates nothing.
+ *
+ * moe_w4a4_forward: as moe_w4a16_forward (same routing arrays, same output,
+ *   same shape rules) with x and h passed through that quantization: the
+ *   matrix units see the exact values E2M1 * E4M3 of both operands (exact in
+ *   bf16) and the input scale multiplies the weight's global scale in each
+ *   epilogue; products accumulate in fp32.  d_ws of moe_w4a4_workspace_size
+ *   bytes (no initialisation).  Deterministic; graph-capturable.
+ */
+moe_status moe_nvfp4_quantize_activations(const uint16_t *d_x, int32_t T, int32_t K, float input_scale,
+                                          uint8_t *d_codes, uint8_t *d_scales, hipStream_t stream);
+size_t moe_w4a4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
+moe_status moe_w4a4_forward(const uint16_t *d_x, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                            const moe_nvfp4_tensor *gate, const moe_nvfp4_tensor *up,
+                            const moe_nvfp4_tensor *down, float input_scale_x, float input_scale_h,
+                            const int32_t *d_topk_ids, const float *d_topk_w,
+                            const int32_t *d_counts, const int32_t *d_offsets,
+                            const int32_t *d_sorted_slots, const int32_t *d_slot_pos,
+                            uint16_t *d_out, void *d_ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Router logits, the step in front of moe_route_topk: the BF16 gate of the
  * layer, logits[t][e] = sum_i x[t][i] * Wr[e][i], accumulated in fp32 (the
  * routers stay BF16 and are never quantized: "GLM-5.3-Flash on Blackwell",

@@ -59,6 +59,10 @@ _SIGS = {
     "moe_w4a16_shared_expert_workspace_size": (_S, [_I, _I, _I]),
     "moe_w4a16_shared_expert": (_I, [_P, _I, _I, _I, _TP, _TP, _TP, _P, _P, _S, _P]),
     "moe_debug_set_prefill_variant": (_I, [_I]),
+    "moe_nvfp4_quantize_activations": (_I, [_P, _I, _I, ctypes.c_float, _P, _P, _P]),
+    "moe_w4a4_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "moe_w4a4_forward": (_I, [_P, _I, _I, _I, _I, _I, _TP, _TP, _TP, ctypes.c_float, ctypes.c_float,
+                              _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
     "moe_profile_begin": (_I, [_I]),
     "moe_profile_end": (_I, [_P, _P, _P, _I]),
 }
@@ -368,4 +372,53 @@ def moe_w4a16_shared_expert(x_bits, gate, up, down, out=None, ws=None, stream=No
     _check(lib().moe_w4a16_shared_expert(_ptr(x_bits), T, H, I, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
                                          _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
            "moe_w4a16_shared_expert")
+    return out
+
+
+def _input_scale(s, name):
+    """A W4A4 input scale as a Python float; None (a missing scale) is
+    refused here, everything else is checked by the library."""
+    if s is None:
+        raise ValueError(f"{name} is missing: a W4A4 layer needs its static input scale")
+    return float(s)
+
+
+def moe_nvfp4_quantize_activations(x_bits, input_scale, codes=None, scales=None, stream=None):
+    """bf16 bits [T, K] -> (codes uint8 [T, K/2], scales uint8 [T, K/16])."""
+    s = _input_scale(input_scale, "input_scale")
+    _dev_tensor(x_bits, "x", _BITS16)
+    T, K = x_bits.shape
+    codes = torch.empty((T, K // 2), dtype=torch.uint8, device=x_bits.device) if codes is None else codes
+    scales = torch.empty((T, K // 16), dtype=torch.uint8, device=x_bits.device) if scales is None else scales
+    _dev_tensor(codes, "codes", torch.uint8, (T, K // 2))
+    _dev_tensor(scales, "scales", torch.uint8, (T, K // 16))
+    _check(lib().moe_nvfp4_quantize_activations(_ptr(x_bits), T, K, s, _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_nvfp4_quantize_activations")
+    return codes, scales
+
+
+def moe_w4a4_workspace_size(T, H, I, E, k):
+    return int(lib().moe_w4a4_workspace_size(T, H, I, E, k))
+
+
+def moe_w4a4_forward(x_bits, gate, up, down, routing, input_scale_x, input_scale_h, out=None, ws=None,
+                     stream=None):
+    """The W4A4 layer: bf16 bits [T, H] -> bf16 bits [T, H] (int16 tensor)."""
+    sx = _input_scale(input_scale_x, "input_scale_x")
+    sh = _input_scale(input_scale_h, "input_scale_h")
+    _dev_tensor(x_bits, "x", _BITS16)
+    T, H = x_bits.shape
+    E, I, _ = gate.shape
+    k = routing.topk_ids.shape[1]
+    routing.check(T, E, k)
+    out = torch.empty((T, H), dtype=torch.int16, device=x_bits.device) if out is None else out
+    _dev_tensor(out, "out", _BITS16, (T, H))
+    need = moe_w4a4_workspace_size(T, H, I, E, k)
+    ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=x_bits.device) if ws is None else ws
+    _dev_tensor(ws, "ws", min_bytes=need)
+    g, u, d = gate.cstruct(), up.cstruct(), down.cstruct()
+    _check(lib().moe_w4a4_forward(_ptr(x_bits), T, H, I, E, k, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                                  sx, sh, _ptr(routing.topk_ids), _ptr(routing.topk_w), _ptr(routing.counts),
+                                  _ptr(routing.offsets), _ptr(routing.sorted_slots), _ptr(routing.slot_pos),
+                                  _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "moe_w4a4_forward")
     return out

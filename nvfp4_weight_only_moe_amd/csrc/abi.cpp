@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -114,12 +115,10 @@ WsLayout ws_layout(void* d_ws, int T, int H, int I, int k) {
 std::atomic<int> g_prefill_variant{2};
 constexpr int64_t kPipeMinRowsPerExpert = 256;
 
+bool use_pipe(const FwdArgs& a);
+
 moe_status launch_prefill(const FwdArgs& a, hipStream_t stream) {
-    const bool pipe_ok = prefill_pipe_supported(a.T, a.k, a.H, a.I);
-    const int64_t slots = (int64_t)a.T * a.k;
-    const int64_t per_expert = slots / std::max<int64_t>(1, std::min<int64_t>(a.E, slots));
-    const int variant = g_prefill_variant.load(std::memory_order_relaxed);
-    const bool pipe = pipe_ok && (variant == 1 || (variant == 2 && per_expert >= kPipeMinRowsPerExpert));
+    const bool pipe = use_pipe(a);
     moe_status st = pipe ? launch_gateup_pipe(a, stream) : launch_gateup_grouped(a, stream);
     if (st != MOE_OK) return st;
     st = pipe ? launch_down_pipe(a, stream) : launch_down_grouped(a, stream);
@@ -135,7 +134,8 @@ moe_status launch_decode_forward(const FwdArgs& a, hipStream_t stream) {
 // Checks shared by moe_w4a16_forward and moe_w4a16_route_forward.
 moe_status check_forward(const uint16_t* d_x, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                          const moe_nvfp4_tensor* gate, const moe_nvfp4_tensor* up, const moe_nvfp4_tensor* down,
-                         const void* const* ptrs, int nptrs, const uint16_t* d_out, void* d_ws, size_t ws_bytes) {
+                         const void* const* ptrs, int nptrs, const uint16_t* d_out, void* d_ws, size_t ws_bytes,
+                         size_t need_override = 0) {
     if (T < 0 || E < 1 || k < 1 || H < 1 || I < 1) return MOE_ERR_SHAPE;
     if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || k > E) return MOE_ERR_UNSUPPORTED;
     if (H % 256 || I % 128) return MOE_ERR_SHAPE;
@@ -156,7 +156,7 @@ moe_status check_forward(const uint16_t* d_x, int32_t T, int32_t H, int32_t I, i
     if (!aligned16(d_ws)) return MOE_ERR_ALIGN;
     const size_t xbytes = (size_t)T * H * sizeof(uint16_t);
     if (ranges_overlap(d_x, xbytes, d_out, xbytes)) return MOE_ERR_INVALID_ARG;
-    const size_t need = forward_workspace_bytes(T, H, I, E, k);
+    const size_t need = need_override ? need_override : forward_workspace_bytes(T, H, I, E, k);
     if (ws_bytes < need) return MOE_ERR_WORKSPACE;
     if (ranges_overlap(d_ws, need, d_out, xbytes) || ranges_overlap(d_ws, need, d_x, xbytes))
         return MOE_ERR_INVALID_ARG;
@@ -219,6 +219,31 @@ size_t linear_workspace_bytes(int T, int K, int N) {
 }
 
 size_t shared_workspace_bytes(int T, int H, int I) { return id_route_bytes(T) + forward_workspace_bytes(T, H, I, 1, 1); }
+
+// W4A4 forward workspace: [x as NVFP4 values (bf16 [T][H]) | SwiGLU output
+// (fp32 [T*k][I]) | the W4A16 forward workspace (h as NVFP4 values, y, ...)].
+size_t w4a4_workspace_bytes(int T, int H, int I, int E, int k) {
+    const size_t slots = (size_t)T * k;
+    return round_up((size_t)T * H * sizeof(uint16_t), kAlign) + round_up(slots * I * sizeof(float), kAlign) +
+           forward_workspace_bytes(T, H, I, E, k);
+}
+
+// A static input scale must be a finite number > 0: a missing scale read as
+// 0.0 multiplies every expert output by zero ("GLM-5.3-Flash on Blackwell",
+// "The model loaded, served an API, and produced garbage").
+moe_status check_input_scale(float s) {
+    if (!std::isfinite(s)) return MOE_ERR_NONFINITE;
+    if (!(s > 0.0f)) return MOE_ERR_BAD_SCALE;
+    return MOE_OK;
+}
+
+bool use_pipe(const FwdArgs& a) {
+    const int64_t slots = (int64_t)a.T * a.k;
+    const int64_t per_expert = slots / std::max<int64_t>(1, std::min<int64_t>(a.E, slots));
+    const int variant = g_prefill_variant.load(std::memory_order_relaxed);
+    return prefill_pipe_supported(a.T, a.k, a.H, a.I) &&
+           (variant == 1 || (variant == 2 && per_expert >= kPipeMinRowsPerExpert));
+}
 
 }  // namespace moe
 
@@ -353,6 +378,66 @@ moe_status moe_w4a16_route_forward(const float* d_logits, const uint16_t* d_x, i
                       L.route, stream);
     if (st != MOE_OK) return st;
     return launch_decode_forward(a, stream);
+}
+
+size_t moe_w4a4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k) {
+    if (T <= 0 || H <= 0 || I <= 0 || k <= 0) return 0;
+    return w4a4_workspace_bytes(T, H, I, E, k);
+}
+
+moe_status moe_nvfp4_quantize_activations(const uint16_t* d_x, int32_t T, int32_t K, float input_scale,
+                                          uint8_t* d_codes, uint8_t* d_scales, hipStream_t stream) {
+    moe_status st = check_input_scale(input_scale);
+    if (st != MOE_OK) return st;
+    if (T < 0 || K < 32 || K % 32) return MOE_ERR_SHAPE;
+    if ((int64_t)T * K > (int64_t)INT32_MAX * 16) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!d_x || !d_codes || !d_scales) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(d_x) || !aligned16(d_codes) || !aligned16(d_scales)) return MOE_ERR_ALIGN;
+    const size_t xb = (size_t)T * K * 2, cb = (size_t)T * K / 2, sb = (size_t)T * K / 16;
+    if (ranges_overlap(d_x, xb, d_codes, cb) || ranges_overlap(d_x, xb, d_scales, sb) ||
+        ranges_overlap(d_codes, cb, d_scales, sb))
+        return MOE_ERR_INVALID_ARG;
+    return launch_quant_act(d_x, false, T, K, input_scale, d_codes, d_scales, nullptr, stream);
+}
+
+moe_status moe_w4a4_forward(const uint16_t* d_x, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                            const moe_nvfp4_tensor* gate, const moe_nvfp4_tensor* up, const moe_nvfp4_tensor* down,
+                            float input_scale_x, float input_scale_h, const int32_t* d_topk_ids,
+                            const float* d_topk_w, const int32_t* d_counts, const int32_t* d_offsets,
+                            const int32_t* d_sorted_slots, const int32_t* d_slot_pos, uint16_t* d_out, void* d_ws,
+                            size_t ws_bytes, hipStream_t stream) {
+    moe_status st = check_input_scale(input_scale_x);
+    if (st != MOE_OK) return st;
+    if ((st = check_input_scale(input_scale_h)) != MOE_OK) return st;
+    const void* ptrs[] = {d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots, d_slot_pos};
+    const size_t need = T > 0 && k > 0 && H > 0 && I > 0 ? w4a4_workspace_bytes(T, H, I, E, k) : 0;
+    st = check_forward(d_x, T, H, I, E, k, gate, up, down, ptrs, 6, d_out, d_ws, ws_bytes, need);
+    if (st != MOE_OK || T == 0) return st;
+    uint8_t* ws = static_cast<uint8_t*>(d_ws);
+    const size_t slots = (size_t)T * k;
+    uint16_t* xq = reinterpret_cast<uint16_t*>(ws);
+    float* hf = reinterpret_cast<float*>(ws + round_up((size_t)T * H * sizeof(uint16_t), kAlign));
+    void* fws = ws + round_up((size_t)T * H * sizeof(uint16_t), kAlign) + round_up(slots * I * sizeof(float), kAlign);
+    const WsLayout L = ws_layout(fws, T, H, I, k);
+    FwdArgs a = make_args(xq, T, H, I, E, k, gate, up, down, d_topk_ids, d_topk_w, d_counts, d_offsets,
+                          d_sorted_slots, d_slot_pos, d_out, L);
+    a.xs = input_scale_x;
+    a.hs = input_scale_h;
+    a.hf = hf;
+    // x -> NVFP4 values; gate/up + SwiGLU in fp32; h -> NVFP4 values; down
+    if ((st = launch_quant_act(d_x, false, T, H, input_scale_x, nullptr, nullptr, xq, stream)) != MOE_OK) return st;
+    const bool decode = decode_path_supported(T, k, H, I);
+    const bool pipe = !decode && use_pipe(a);
+    st = decode ? launch_forward_decode_gateup(a, stream)
+                : (pipe ? launch_gateup_pipe(a, stream) : launch_gateup_grouped(a, stream));
+    if (st != MOE_OK) return st;
+    if ((st = launch_quant_act(hf, true, (int64_t)slots, I, input_scale_h, nullptr, nullptr, L.h, stream)) != MOE_OK)
+        return st;
+    if (decode) return launch_forward_decode_down(a, stream);
+    st = pipe ? launch_down_pipe(a, stream) : launch_down_grouped(a, stream);
+    if (st != MOE_OK) return st;
+    return launch_combine(a, stream);
 }
 
 moe_status moe_router_logits(const uint16_t* d_x, int32_t T, int32_t H, const uint16_t* d_wr, int32_t E,

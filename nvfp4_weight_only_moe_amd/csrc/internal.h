@@ -38,6 +38,11 @@ moe_status launch_quantize_pack(const float* w, int E, int N, int K, const moe_n
                                 hipStream_t s);
 moe_status launch_dequantize(const moe_nvfp4_tensor* t, float* w_out, hipStream_t s);
 moe_status launch_validate(const moe_nvfp4_tensor* t, uint32_t* d_flag, hipStream_t s);
+// W4A4 activations: rows x K (bf16, or fp32 when in_f32) quantized to NVFP4
+// with a static input scale; either packed (codes/scales non-null) or the
+// unscaled values E2M1 * E4M3 as bf16 into deq
+moe_status launch_quant_act(const void* in, bool in_f32, int64_t rows, int K, float input_scale, uint8_t* codes,
+                            uint8_t* scales, uint16_t* deq, hipStream_t s);
 // n words set to zero by a fill kernel (graph-safe: no memset node)
 moe_status launch_zero_words(uint32_t* p, int n, hipStream_t s);
 
@@ -66,13 +71,23 @@ struct FwdArgs {
     const int32_t* sorted_slots;
     const int32_t* slot_pos;
     uint16_t* out;
-    uint16_t* h;  // workspace: [T*k][I] bf16, expert-sorted rows
+    uint16_t* h;  // workspace: [T*k][I] bf16, expert-sorted rows (the down GEMM's input)
     float* y;     // workspace: [T*k][H] fp32, expert-sorted rows (prefill only)
+    // W4A4: the activations' static input scales multiply the weights' global
+    // scales in the epilogues (x: gate/up, h: down; 1 for W4A16), and the
+    // gate/up output goes as fp32 to hf (when set) for the NVFP4 quantization
+    // of h instead of as bf16 to h
+    float xs = 1.0f;
+    float hs = 1.0f;
+    float* hf = nullptr;
 };
 
 size_t forward_workspace_bytes(int T, int H, int I, int E, int k);
 bool decode_path_supported(int T, int k, int H, int I);
 moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s);
+// its two halves (gate/up + SwiGLU, down + combine) as separate calls
+moe_status launch_forward_decode_gateup(const FwdArgs& a, hipStream_t s);
+moe_status launch_forward_decode_down(const FwdArgs& a, hipStream_t s);
 // the same kernels for one always-on expert (E = 1, k = 1, weight 1, tokens
 // in order): no routing arrays are read
 moe_status launch_forward_decode_one(const FwdArgs& a, hipStream_t s);

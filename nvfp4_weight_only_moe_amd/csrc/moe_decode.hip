@@ -97,7 +97,7 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
              const uint8_t* gc, const uint8_t* gs, const float* __restrict__ gg,
              const uint8_t* uc, const uint8_t* us, const float* __restrict__ ug,
              const int32_t* __restrict__ counts, const int32_t* __restrict__ sorted_slots,
-             uint16_t* __restrict__ h, const GuRoute R) {
+             uint16_t* __restrict__ h, const GuRoute R, float x_scale, float* __restrict__ hf) {
     constexpr int kXT = x_stage_tokens<LINEAR>();
     extern __shared__ uint4 xs[];   // [kXT][H / 8]
     __shared__ int s_ids[kDecodeMaxSlots], s_pos[kDecodeMaxSlots], s_sorted[kDecodeMaxSlots];
@@ -168,7 +168,7 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
     stage_x(0);
 
     const int nb = (blockIdx.x * kGuWaves + wave) * (2 * RW);   // first feature of this wave
-    const float g_gate = gg[e], g_up = LINEAR ? 0.0f : ug[e];
+    const float g_gate = gg[e] * x_scale, g_up = LINEAR ? 0.0f : ug[e] * x_scale;
     constexpr int kLoadsPerChunk = LINEAR ? 2 : 4;
     // the codes of all RW stages are requested at once and stay in registers
     // for every token of the expert
@@ -242,8 +242,10 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
                 }
                 if (lane < 2 && n + lane < I) {
                     const float av = lane ? a1 : a0, bv = lane ? b1 : b0;
-                    h[(int64_t)(p0 + qt) * I + n + lane] =
-                        LINEAR ? f32_to_bf16_rne(g_gate * av) : f32_to_bf16_rne(silu(g_gate * av) * (g_up * bv));
+                    const float v = LINEAR ? g_gate * av : silu(g_gate * av) * (g_up * bv);
+                    const int64_t idx = (int64_t)(p0 + qt) * I + n + lane;
+                    if (hf) hf[idx] = v;
+                    else h[idx] = f32_to_bf16_rne(v);
                 }
             }
         }
@@ -285,7 +287,7 @@ __global__ void __launch_bounds__(kDownMaxWaves * kWave)
 k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
            const uint8_t* dc, const uint8_t* ds, const float* __restrict__ dg,
            const int32_t* __restrict__ ids, const float* __restrict__ topk_w,
-           uint16_t* __restrict__ out, int slot_cap) {
+           uint16_t* __restrict__ out, int slot_cap, float h_scale) {
     constexpr int kDownChunkExperts = down_chunk_experts<MAXT>();
     extern __shared__ uint4 hs[];     // [slot_cap][I / 8]
     __shared__ int s_list[kDecodeMaxSlots], s_ucnt[kDecodeMaxSlots], s_uoff[kDecodeMaxSlots];
@@ -382,7 +384,7 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
     const int64_t code_stride = (int64_t)H * (I / 2), scale_stride = (int64_t)H * ngroups;
 
     // every touched expert's global scale in one vector load (lane u: expert u)
-    const float gvv = dg[s_list[min(lane, s_U - 1)]];
+    const float gvv = dg[s_list[min(lane, s_U - 1)]] * h_scale;
 
     float acc[MAXT][R];
 #pragma unroll
@@ -525,7 +527,7 @@ moe_status launch_gateup_epl(const FwdArgs& a, const GuRoute& R, hipStream_t s) 
     MOE_LAUNCH(ROUTE ? "dec_gateup_route" : "dec_gateup", kern, grid, dim3(kGuThreads), shmem, s, a.x, a.H, a.I,
                a.E, a.k, a.T * a.k, (const uint8_t*)a.gate->codes, (const uint8_t*)a.gate->scales,
                (const float*)a.gate->global_scale, (const uint8_t*)a.up->codes, (const uint8_t*)a.up->scales,
-               (const float*)a.up->global_scale, a.counts, a.sorted_slots, a.h, R);
+               (const float*)a.up->global_scale, a.counts, a.sorted_slots, a.h, R, a.xs, a.hf);
     return MOE_OK;
 }
 
@@ -573,7 +575,7 @@ moe_status launch_down_t(const FwdArgs& a, hipStream_t s) {
     MOE_LAUNCH("dec_down", (k_dec_down<GPL2, MAXT, ONE>), dim3((a.H + rows_per_block - 1) / rows_per_block),
                dim3(waves * kWave), shmem, s, (const uint16_t*)a.h, a.T, a.H, a.I, a.E, a.k,
                (const uint8_t*)a.down->codes, (const uint8_t*)a.down->scales, (const float*)a.down->global_scale,
-               a.ids, a.topk_w, a.out, slot_cap);
+               a.ids, a.topk_w, a.out, slot_cap, a.hs);
     return MOE_OK;
 }
 
@@ -599,20 +601,21 @@ bool decode_path_supported(int T, int k, int H, int I) {
 
 namespace {
 
-moe_status launch_decode_pair(const FwdArgs& a, const GuRoute* R, hipStream_t s, bool one = false) {
-    moe_status st;
+moe_status launch_decode_gateup_part(const FwdArgs& a, const GuRoute* R, hipStream_t s, bool one) {
     switch (a.H / 1024) {
-        case 1: st = launch_gateup_gpl<1>(a, R, s, one); break;
-        case 2: st = launch_gateup_gpl<2>(a, R, s, one); break;
-        case 3: st = launch_gateup_gpl<3>(a, R, s, one); break;
-        case 4: st = launch_gateup_gpl<4>(a, R, s, one); break;
-        case 5: st = launch_gateup_gpl<5>(a, R, s, one); break;
-        case 6: st = launch_gateup_gpl<6>(a, R, s, one); break;
-        case 7: st = launch_gateup_gpl<7>(a, R, s, one); break;
-        case 8: st = launch_gateup_gpl<8>(a, R, s, one); break;
+        case 1: return launch_gateup_gpl<1>(a, R, s, one);
+        case 2: return launch_gateup_gpl<2>(a, R, s, one);
+        case 3: return launch_gateup_gpl<3>(a, R, s, one);
+        case 4: return launch_gateup_gpl<4>(a, R, s, one);
+        case 5: return launch_gateup_gpl<5>(a, R, s, one);
+        case 6: return launch_gateup_gpl<6>(a, R, s, one);
+        case 7: return launch_gateup_gpl<7>(a, R, s, one);
+        case 8: return launch_gateup_gpl<8>(a, R, s, one);
         default: return MOE_ERR_UNSUPPORTED;
     }
-    if (st != MOE_OK) return st;
+}
+
+moe_status launch_decode_down_part(const FwdArgs& a, hipStream_t s, bool one) {
     switch (a.I / 512) {
         case 1: return launch_down_gpl<1>(a, s, one);
         case 2: return launch_down_gpl<2>(a, s, one);
@@ -622,7 +625,18 @@ moe_status launch_decode_pair(const FwdArgs& a, const GuRoute* R, hipStream_t s,
     }
 }
 
+moe_status launch_decode_pair(const FwdArgs& a, const GuRoute* R, hipStream_t s, bool one = false) {
+    const moe_status st = launch_decode_gateup_part(a, R, s, one);
+    if (st != MOE_OK) return st;
+    return launch_decode_down_part(a, s, one);
+}
+
 }  // namespace
+
+moe_status launch_forward_decode_gateup(const FwdArgs& a, hipStream_t s) {
+    return launch_decode_gateup_part(a, nullptr, s, false);
+}
+moe_status launch_forward_decode_down(const FwdArgs& a, hipStream_t s) { return launch_decode_down_part(a, s, false); }
 
 moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s) { return launch_decode_pair(a, nullptr, s); }
 
@@ -644,7 +658,7 @@ moe_status launch_linear_rw(const FwdArgs& a, hipStream_t s) {
     MOE_LAUNCH("dec_linear", kern, grid, dim3(kGuThreads), shmem, s, a.x, a.H, a.I, 1, 1, a.T,
                (const uint8_t*)a.gate->codes, (const uint8_t*)a.gate->scales, (const float*)a.gate->global_scale,
                (const uint8_t*)a.gate->codes, (const uint8_t*)a.gate->scales, (const float*)a.gate->global_scale,
-               a.counts, a.sorted_slots, a.h, none);
+               a.counts, a.sorted_slots, a.h, none, 1.0f, (float*)nullptr);
     return MOE_OK;
 }
 

@@ -53,6 +53,8 @@ struct GemmParams {
     const int32_t* offsets;
     void* out;                  // GATEUP: h bf16 [T*k][N]; DOWN: y fp32 [T*k][N]
     int ntn;                    // column tiles per expert
+    float gmul;                 // multiplies the global scales (W4A4 input scale; 1 for W4A16)
+    float* hf;                  // gate/up: fp32 h instead of bf16 into out, when set (W4A4)
 };
 
 __device__ __forceinline__ bf16x8 decode8(uint32_t word, float s) {
@@ -213,7 +215,7 @@ __global__ void __launch_bounds__(kGThreads, gemm_wg_per_cu<BM>()) k_grouped_gem
 
         // epilogue: lane holds rows 4*kq + i (i < 4) of each 16-row subtile, column lcol
         if (GATEUP) {
-            const float gg = P.g0[e], gu = P.g1[e];
+            const float gg = P.g0[e] * P.gmul, gu = P.g1[e] * P.gmul;
             uint16_t* h = reinterpret_cast<uint16_t*>(P.out);
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms)
@@ -226,12 +228,15 @@ __global__ void __launch_bounds__(kGThreads, gemm_wg_per_cu<BM>()) k_grouped_gem
                             const float a = gg * acc[ms][ns][i];
                             const float b = gu * acc[ms][ns + 2][i];
                             const int col = nt * BN + wave * 32 + ns * 16 + lcol;
-                            h[(int64_t)(p0 + r) * P.N + col] = f32_to_bf16_rne(silu(a) * b);
+                            const int64_t idx = (int64_t)(p0 + r) * P.N + col;
+                            const float v = silu(a) * b;
+                            if (P.hf) P.hf[idx] = v;
+                            else h[idx] = f32_to_bf16_rne(v);
                         }
                     }
                 }
         } else {
-            const float gd = P.g0[e];
+            const float gd = P.g0[e] * P.gmul;
             float* y = reinterpret_cast<float*>(P.out);
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms)
@@ -335,6 +340,8 @@ moe_status launch_gateup_grouped(const FwdArgs& a, hipStream_t s) {
     g.offsets = a.offsets;
     g.out = a.h;
     g.ntn = a.I / 128;
+    g.gmul = a.xs;
+    g.hf = a.hf;
     return launch_gemm_bm<true>(g, slots, a.E, s);
 }
 
@@ -352,6 +359,8 @@ moe_status launch_down_grouped(const FwdArgs& a, hipStream_t s) {
     d.offsets = a.offsets;
     d.out = a.y;
     d.ntn = a.H / 256;
+    d.gmul = a.hs;
+    d.hf = nullptr;
     return launch_gemm_bm<false>(d, slots, a.E, s);
 }
 

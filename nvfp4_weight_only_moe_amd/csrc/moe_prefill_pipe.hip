@@ -83,6 +83,8 @@ struct PipeParams {
     const int32_t* offsets;
     void* out;                  // gate/up: h bf16 [T*k][N]; down: y fp32 [T*k][N]
     int ntn;                    // column tiles per expert
+    float gmul;                 // multiplies the global scales (W4A4 input scale; 1 for W4A16)
+    float* hf;                  // gate/up: fp32 h instead of bf16 into out, when set (W4A4)
 };
 
 struct Tile {
@@ -389,8 +391,8 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
         // as pending across the stage loop makes the compiler wait for all
         // of them inside it
         const int e_cur = __builtin_amdgcn_readfirstlane(cur.e);
-        const float g_a = ((const __attribute__((address_space(4))) float*)P.g0)[e_cur];
-        const float g_b = GATEUP ? ((const __attribute__((address_space(4))) float*)P.g1)[e_cur] : 0.0f;
+        const float g_a = ((const __attribute__((address_space(4))) float*)P.g0)[e_cur] * P.gmul;
+        const float g_b = GATEUP ? ((const __attribute__((address_space(4))) float*)P.g1)[e_cur] * P.gmul : 0.0f;
         floatx4 acc[8][kNS];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -432,7 +434,10 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
                             const float av = gg * acc[ms][ns][i];
                             const float bv = gu * acc[ms][ns + kNS / 2][i];
                             const int col = cur.nt * (kBN / 2) + 32 * wave + 16 * ns + lcol;
-                            h[(int64_t)(cur.p0 + r) * P.N + col] = f32_to_bf16_rne(silu(av) * bv);
+                            const int64_t idx = (int64_t)(cur.p0 + r) * P.N + col;
+                            const float v = silu(av) * bv;
+                            if (P.hf) P.hf[idx] = v;
+                            else h[idx] = f32_to_bf16_rne(v);
                         }
                     }
                 }
@@ -504,6 +509,8 @@ moe_status launch_gateup_pipe(const FwdArgs& a, hipStream_t s) {
     g.offsets = a.offsets;
     g.out = a.h;
     g.ntn = a.I / (kBN / 2);
+    g.gmul = a.xs;
+    g.hf = a.hf;
     return launch_pipe<true>(g, (int64_t)a.T * a.k, s);
 }
 
@@ -520,6 +527,8 @@ moe_status launch_down_pipe(const FwdArgs& a, hipStream_t s) {
     d.offsets = a.offsets;
     d.out = a.y;
     d.ntn = a.H / kBN;
+    d.gmul = a.hs;
+    d.hf = nullptr;
     return launch_pipe<false>(d, (int64_t)a.T * a.k, s);
 }
 

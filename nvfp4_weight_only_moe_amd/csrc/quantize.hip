@@ -190,9 +190,104 @@ __global__ void k_zero_words(uint32_t* p, int n) {
     if (i < n) p[i] = 0u;
 }
 
+// ---- W4A4: activations quantized like the weights, with a static input
+// scale in the place of the global scale ("GLM-5.3-Flash-NVFP4-h", opening:
+// the routed experts' stock W4A4 quantization; "GLM-5.3-Flash · 512k + MTP +
+// vision ...", "Input-scales provenance": the per-tensor input_scale).  One
+// thread per 16-group of a row:
+//   s = E4M3((amax / 6) / input_scale),  code = E2M1(v / (E4M3(s) * input_scale)),
+// the same correctly rounded fp32 steps as the weights.  Output either the
+// packed codes and scale bytes (the canonical activation layout), or the
+// group's values E2M1(code) * E4M3(s) as bf16 -- exact (at most 6
+// significant bits) and without the input scale, which the GEMM epilogue
+// applies with the weight's global scale.
+template <bool IN_F32, bool PACKED>
+__global__ void __launch_bounds__(kQBlock) k_quant_act(const void* __restrict__ in, int64_t groups, float input_scale,
+                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                       uint16_t* __restrict__ deq) {
+    const int64_t gi = (int64_t)blockIdx.x * kQBlock + threadIdx.x;
+    if (gi >= groups) return;
+    float v[16];
+    if constexpr (IN_F32) {
+        const float4* src = reinterpret_cast<const float4*>(in) + gi * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 q = src[i];
+            v[4 * i + 0] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+        }
+    } else {
+        const uint4* src = reinterpret_cast<const uint4*>(in) + gi * 2;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint4 q = src[i];
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * i + 2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+                v[8 * i + 2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+            }
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const float s_f = (amax / 6.0f) / input_scale;
+    const uint32_t sb = e4m3_encode_rne_sat(s_f);
+    const float s_q = e4m3_to_f32(sb);
+    const float d = s_q * input_scale;
+    uint32_t c[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        c[i] = (d == 0.0f) ? ((__float_as_uint(v[i]) >> 31) << 3) : e2m1_encode_rne_sat(v[i] / d);
+    if constexpr (PACKED) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            lo |= c[i] << (4 * i);
+            hi |= c[8 + i] << (4 * i);
+        }
+        reinterpret_cast<uint2*>(codes)[gi] = make_uint2(lo, hi);
+        scales[gi] = (uint8_t)sb;
+    } else {
+        // E2M1 magnitude * scale, exact in fp32 and in bf16 (truncation exact)
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t pair = c[2 * i] | (c[2 * i + 1] << 4);
+            const floatx2 f = e2m1x2_to_f32<0>(pair);
+            o[i] = pack_bf16x2_exact(f[0] * s_q, f[1] * s_q);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(deq) + gi * 2;
+        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+}
+
 inline int blocks_for(int64_t n, int per) { return (int)((n + per - 1) / per); }
 
 }  // namespace
+
+moe_status launch_quant_act(const void* in, bool in_f32, int64_t rows, int K, float input_scale, uint8_t* codes,
+                            uint8_t* scales, uint16_t* deq, hipStream_t s) {
+    const int64_t groups = rows * (K / 16);
+    if (groups == 0) return MOE_OK;
+    const dim3 grid(blocks_for(groups, kQBlock));
+    if (codes) {
+        if (in_f32)
+            MOE_LAUNCH("quant_act", (k_quant_act<true, true>), grid, dim3(kQBlock), 0, s, in, groups, input_scale,
+                       codes, scales, deq);
+        else
+            MOE_LAUNCH("quant_act", (k_quant_act<false, true>), grid, dim3(kQBlock), 0, s, in, groups, input_scale,
+                       codes, scales, deq);
+    } else if (in_f32) {
+        MOE_LAUNCH("quant_act", (k_quant_act<true, false>), grid, dim3(kQBlock), 0, s, in, groups, input_scale,
+                   codes, scales, deq);
+    } else {
+        MOE_LAUNCH("quant_act", (k_quant_act<false, false>), grid, dim3(kQBlock), 0, s, in, groups, input_scale,
+                   codes, scales, deq);
+    }
+    return MOE_OK;
+}
 
 moe_status launch_quantize_pack(const float* w, int E, int N, int K, const moe_nvfp4_tensor* out,
                                 hipStream_t s) {

@@ -26,6 +26,11 @@ key):
 
 The shapes are those of a GLM-5.3-Flash-class routed-expert layer: hidden
 5120, 256 experts, top-8, intermediate 1536.
+
+W4A4 input scales: a W4A4 checkpoint carries static, calibrated activation
+scales; the synthetic stand-ins are fixed constants, one for the gate/up
+input (covering |x| <= 6 of the N(0, 1) activations at the largest code and
+scale) and one for the down input (covering |h| <= 32).
 """
 
 from dataclasses import dataclass
@@ -55,6 +60,10 @@ WORKLOADS = {
     3: Workload(3, "prefill-t1024-h5120-i1536-e256-k8", 1024, 5120, 1536, 256, 8, 1, "none"),
     4: Workload(4, "prefill-t16384-h5120-i1536-e256-k8-zipf1.1", 16384, 5120, 1536, 256, 8, 1, "zipf"),
 }
+
+
+# (gate/up input, down input) static input scales of the W4A4 workloads
+W4A4_INPUT_SCALES = (2.2321428e-03, 1.1904762e-02)
 
 
 def rng(key):

@@ -215,3 +215,43 @@ def test_router_logits_argument_errors(L):
     assert rtr(L, out=A + 0x800004) == -3
     assert rtr(L, out=A + 0x100) == -1                             # logits overlap x
     assert rtr(L, out=A + 0x100000) == -1                          # logits overlap the router weight
+
+
+def w4(L, x=A, T=4, H=256, I=128, E=8, k=2, sx=0.01, sh=0.02, ptr=A, out=A + 0x800000, ws=A + 0x900000,
+       ws_bytes=1 << 30):
+    gate, up, down = T_(E, I, H), T_(E, I, H, A + 0x1000000), T_(E, H, I, A + 0x2000000)
+    p = [ptr] * 6
+    return L.moe_w4a4_forward(x, T, H, I, E, k, ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down),
+                              ctypes.c_float(sx), ctypes.c_float(sh), *p, out, ws, ws_bytes, None)
+
+
+def test_w4a4_argument_errors(L):
+    L.moe_w4a4_forward.argtypes = b._SIGS["moe_w4a4_forward"][1]
+    assert w4(L, T=0) == b.MOE_OK
+    for bad in (0.0, -0.0, -1.0):
+        assert w4(L, sx=bad) == -6                                   # BAD_SCALE
+        assert w4(L, sh=bad) == -6
+        assert w4(L, T=0, sx=bad) == -6                              # refused even as a no-op
+    for bad in (float("nan"), float("inf"), float("-inf")):
+        assert w4(L, sx=bad) == -5                                   # NONFINITE
+        assert w4(L, sh=bad) == -5
+    assert w4(L, H=200) == -2
+    assert w4(L, x=0) == -1
+    assert w4(L, out=A) == -1
+    assert w4(L, ws=0) == -7
+    need = L.moe_w4a4_workspace_size(4, 256, 128, 8, 2)
+    assert need > L.moe_w4a16_workspace_size(4, 256, 128, 8, 2)
+    assert w4(L, ws_bytes=need - 1) == -7
+
+
+def test_quantize_activations_argument_errors(L):
+    q = L.moe_nvfp4_quantize_activations
+    f = ctypes.c_float
+    assert q(A, 0, 64, f(1.0), A + 0x100000, A + 0x200000, None) == b.MOE_OK
+    assert q(A, 4, 64, f(0.0), A + 0x100000, A + 0x200000, None) == -6
+    assert q(A, 4, 64, f(float("nan")), A + 0x100000, A + 0x200000, None) == -5
+    assert q(A, 4, 48, f(1.0), A + 0x100000, A + 0x200000, None) == -2       # K % 32
+    assert q(A, -1, 64, f(1.0), A + 0x100000, A + 0x200000, None) == -2
+    assert q(0, 4, 64, f(1.0), A + 0x100000, A + 0x200000, None) == -1
+    assert q(A, 4, 64, f(1.0), A + 4, A + 0x200000, None) == -3
+    assert q(A, 4, 64, f(1.0), A + 0x40, A + 0x200000, None) == -1          # codes overlap x
