@@ -252,6 +252,32 @@ moe_status moe_w4a4_forward(const uint16_t *d_x, int32_t T, int32_t H, int32_t I
                             uint16_t *d_out, void *d_ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_w4a16_route_forward for callers that cannot allocate -- code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation: the
+ * same call, kernels and results, without a workspace argument.  Its
+ * workspace is a device array owned by the library, MOE_NOALLOC_SCRATCH_BYTES
+ * on every GPU the library runs on, held until the process ends; its device
+ * address is looked up (hipGetSymbolAddress) on the first call on each
+ * device.  The call allocates and frees nothing.  Shapes whose workspace
+ * (moe_w4a16_workspace_size) exceeds MOE_NOALLOC_SCRATCH_BYTES are refused
+ * with MOE_ERR_WORKSPACE: every decode shape fits, and prefill up to about
+ * 1400 (token, expert) pairs at hidden 5120 / intermediate 1536.  The array
+ * keeps the last call's contents and nothing in it needs to start at zero.
+ * All calls on one GPU share the array: calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race and
+ * give undefined results; order them on one stream.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_w4a16_route_forward_noalloc(const float *d_logits, const uint16_t *d_x,
+                                           int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                           const moe_nvfp4_tensor *gate, const moe_nvfp4_tensor *up,
+                                           const moe_nvfp4_tensor *down,
+                                           int32_t *d_topk_ids, float *d_topk_w,
+                                           int32_t *d_counts, int32_t *d_offsets,
+                                           int32_t *d_sorted_slots, int32_t *d_slot_pos,
+                                           uint16_t *d_out, hipStream_t stream);
+
+/*
  * Router logits, the step in front of moe_route_topk: the BF16 gate of the
  * layer, logits[t][e] = sum_i x[t][i] * Wr[e][i], accumulated in fp32 (the
  * routers stay BF16 and are never quantized: "GLM-5.3-Flash on Blackwell",

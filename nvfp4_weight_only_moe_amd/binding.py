@@ -63,6 +63,8 @@ _SIGS = {
     "moe_w4a4_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "moe_w4a4_forward": (_I, [_P, _I, _I, _I, _I, _I, _TP, _TP, _TP, ctypes.c_float, ctypes.c_float,
                               _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
+    "moe_w4a16_route_forward_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _I, _TP, _TP, _TP, _P, _P, _P, _P, _P, _P, _P,
+                                             _P]),
     "moe_profile_begin": (_I, [_I]),
     "moe_profile_end": (_I, [_P, _P, _P, _I]),
 }
@@ -422,3 +424,24 @@ def moe_w4a4_forward(x_bits, gate, up, down, routing, input_scale_x, input_scale
                                   _ptr(routing.offsets), _ptr(routing.sorted_slots), _ptr(routing.slot_pos),
                                   _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "moe_w4a4_forward")
     return out
+
+
+def moe_w4a16_route_forward_noalloc(logits, x_bits, gate, up, down, k, routing=None, out=None, stream=None):
+    """moe_w4a16_route_forward with the library's own device array as the
+    workspace (no workspace argument, no allocation in the call).  Returns
+    (out, routing)."""
+    _dev_tensor(x_bits, "x", _BITS16)
+    T, H = x_bits.shape
+    E, I, _ = gate.shape
+    _dev_tensor(logits, "logits", torch.float32, (T, E))
+    routing = Routing.empty(T, E, k, x_bits.device) if routing is None else routing
+    routing.check(T, E, k)
+    out = torch.empty((T, H), dtype=torch.int16, device=x_bits.device) if out is None else out
+    _dev_tensor(out, "out", _BITS16, (T, H))
+    g, u, d = gate.cstruct(), up.cstruct(), down.cstruct()
+    _check(lib().moe_w4a16_route_forward_noalloc(_ptr(logits), _ptr(x_bits), T, H, I, E, k, ctypes.byref(g),
+                                                 ctypes.byref(u), ctypes.byref(d), _ptr(routing.topk_ids),
+                                                 _ptr(routing.topk_w), _ptr(routing.counts), _ptr(routing.offsets),
+                                                 _ptr(routing.sorted_slots), _ptr(routing.slot_pos), _ptr(out),
+                                                 _stream(stream)), "moe_w4a16_route_forward_noalloc")
+    return out, routing
