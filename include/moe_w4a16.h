@@ -178,7 +178,9 @@ size_t moe_w4a16_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int3
  * significant bits), products accumulate in fp32, the global scale is
  * applied in fp32 after the K reduction, SwiGLU in fp32, the SwiGLU output is
  * rounded once to bf16, the down projection accumulates in fp32 and the
- * routing-weighted combine runs in fp32 before one rounding to bf16.
+ * routing-weighted combine runs in fp32 before one rounding to bf16.  Shapes
+ * beyond the decode kernels round each expert's down-projection row to bf16
+ * before the combine (it goes through memory; half the bytes of fp32).
  * Deterministic: no floating-point atomics.  T == 0 is a no-op.
  */
 moe_status moe_w4a16_forward(const uint16_t *d_x, int32_t T, int32_t H, int32_t I,

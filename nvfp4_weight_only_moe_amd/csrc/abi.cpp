@@ -83,16 +83,16 @@ moe_status allow_dynamic_lds(const void* kernel, size_t bytes) {
     return MOE_OK;
 }
 
-// Forward workspace: [h (bf16 [T*k][I]) | y (fp32 [T*k][H]) | route scratch].
+// Forward workspace: [h (bf16 [T*k][I]) | y (bf16 [T*k][H]) | route scratch].
 size_t forward_workspace_bytes(int T, int H, int I, int E, int k) {
     const size_t slots = (size_t)T * k;
-    return round_up(slots * I * sizeof(uint16_t), kAlign) + round_up(slots * H * sizeof(float), kAlign) +
+    return round_up(slots * I * sizeof(uint16_t), kAlign) + round_up(slots * H * sizeof(uint16_t), kAlign) +
            round_up(route_workspace_bytes(T, E, k), kAlign);
 }
 
 struct WsLayout {
     uint16_t* h;
-    float* y;
+    uint16_t* y;
     void* route;
 };
 
@@ -100,8 +100,8 @@ WsLayout ws_layout(void* d_ws, int T, int H, int I, int k) {
     uint8_t* ws = static_cast<uint8_t*>(d_ws);
     const size_t slots = (size_t)T * k;
     const size_t hb = round_up(slots * I * sizeof(uint16_t), kAlign);
-    const size_t yb = round_up(slots * H * sizeof(float), kAlign);
-    return WsLayout{reinterpret_cast<uint16_t*>(ws), reinterpret_cast<float*>(ws + hb), ws + hb + yb};
+    const size_t yb = round_up(slots * H * sizeof(uint16_t), kAlign);
+    return WsLayout{reinterpret_cast<uint16_t*>(ws), reinterpret_cast<uint16_t*>(ws + hb), ws + hb + yb};
 }
 
 // Grouped-GEMM kernels for larger T: 0 = register-staged (k_grouped_gemm)
@@ -215,7 +215,7 @@ IdRoute id_route_layout(void* d_ws, int T) {
 
 size_t linear_workspace_bytes(int T, int K, int N) {
     (void)K;
-    return id_route_bytes(T) + round_up((size_t)T * N * sizeof(float), kAlign);
+    return id_route_bytes(T) + round_up((size_t)T * N * sizeof(uint16_t), kAlign);
 }
 
 size_t shared_workspace_bytes(int T, int H, int I) { return id_route_bytes(T) + forward_workspace_bytes(T, H, I, 1, 1); }
@@ -495,11 +495,11 @@ moe_status moe_w4a16_linear(const uint16_t* d_x, int32_t T, int32_t K, int32_t N
     }
     st = launch_route_identity(T, R.ids, R.w, R.counts, R.offsets, R.sorted, R.pos, stream);
     if (st != MOE_OK) return st;
-    // the down GEMM (x as its A operand, fp32 rows in the workspace) and the
-    // combine with one slot of weight 1
+    // the down GEMM (x as its A operand, bf16 rows in the workspace) and the
+    // combine with one slot of weight 1 (which returns those rows unchanged)
     a.H = N; a.I = K;
     a.h = const_cast<uint16_t*>(d_x);
-    a.y = reinterpret_cast<float*>(R.rest);
+    a.y = reinterpret_cast<uint16_t*>(R.rest);
     const bool pipe = prefill_pipe_supported(T, 1, N, K) && T >= kPipeMinRowsPerExpert;
     st = pipe ? launch_down_pipe(a, stream) : launch_down_grouped(a, stream);
     if (st != MOE_OK) return st;

@@ -72,7 +72,7 @@ struct FwdArgs {
     const int32_t* slot_pos;
     uint16_t* out;
     uint16_t* h;  // workspace: [T*k][I] bf16, expert-sorted rows (the down GEMM's input)
-    float* y;     // workspace: [T*k][H] fp32, expert-sorted rows (prefill only)
+    uint16_t* y;  // workspace: [T*k][H] bf16, expert-sorted rows (prefill only)
     // W4A4: the activations' static input scales multiply the weights' global
     // scales in the epilogues (x: gate/up, h: down; 1 for W4A16), and the
     // gate/up output goes as fp32 to hf (when set) for the NVFP4 quantization

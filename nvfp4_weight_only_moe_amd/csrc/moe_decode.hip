@@ -102,45 +102,39 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
     extern __shared__ uint4 xs[];   // [kXT][H / 8]
     __shared__ int s_ids[kDecodeMaxSlots], s_pos[kDecodeMaxSlots], s_sorted[kDecodeMaxSlots];
     __shared__ int s_list[kDecodeMaxSlots], s_ucnt[kDecodeMaxSlots], s_uoff[kDecodeMaxSlots];
-    __shared__ int s_U;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     int my_slot, e, ne, p0, U = 0;
-    float sel_logit = 0.0f;     // wave 0 of a routing workgroup: lane j < k holds the j-th selected logit
     if constexpr (ROUTE) {
-        // nothing else is in flight while the logits load: the barriers below
-        // then wait for no memory traffic
+        // one token: the selected experts as a set (threshold search); with
+        // one token each expert holds one slot, so the sorted slot order is
+        // the ascending expert order that the selection flags give directly.
+        // The order of the slots by logit is needed for the stored routing
+        // outputs alone: the one workgroup that stores them ranks the
+        // selection after its weight loads are out.
         if (wave == 0) {
-            // the selection only: the routing weights are needed for the
-            // stored outputs alone and are computed after the loads are out
-            int id;
-            wave_topk_ids<EPL>(R.logits, E, k, id, sel_logit);
-            if (lane < k) s_ids[lane] = id;
+            uint32_t key[EPL];
+            uint64_t sel[EPL];
+            wave_topk_set<EPL>(R.logits, E, k, key, sel);
+            int base = 0;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                if ((sel[i] >> lane) & 1u) {
+                    const int u = base + __popcll(sel[i] & lanemask_lt());
+                    s_list[u] = kWave * i + lane;
+                    s_ucnt[u] = 1;
+                    s_uoff[u] = u;
+                    s_sorted[u] = (int)key[i];          // the selected keys, ascending expert
+                }
+                base += __popcll(sel[i]);
+            }
         }
         __syncthreads();
-        if (wave == 0) {
-            // rank of each slot by (expert, flat index)
-            const bool valid = lane < slots;
-            const int ex = valid ? s_ids[lane] : 0;
-            const SlotOrder o = wave_slot_order(ex, valid, E);
-            if (valid) {
-                s_pos[lane] = o.pos;
-                s_sorted[o.pos] = lane;
-            }
-            if (o.first) {
-                s_list[o.u] = ex;
-                s_ucnt[o.u] = __popcll(o.eq);
-                s_uoff[o.u] = o.less;
-            }
-            if (lane == 0) s_U = o.U;
-        }
-        __syncthreads();
-        U = s_U;
-        if ((int)blockIdx.y >= U) return;
+        U = slots;                                     // k distinct experts
         e = s_list[blockIdx.y];
-        ne = s_ucnt[blockIdx.y];
-        p0 = s_uoff[blockIdx.y];
-        my_slot = lane < slots ? s_sorted[lane] : 0;
+        ne = 1;
+        p0 = blockIdx.y;
+        my_slot = 0;                                   // token 0 for every slot
     } else {
         if constexpr (LINEAR || ONE) {   // one always-on stack: token order, no routing arrays
             my_slot = lane;
@@ -256,13 +250,30 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
     if constexpr (ROUTE) {
         if (blockIdx.y != 0) return;
         if (blockIdx.x == 0 && wave == 0) {
-            const float w = topk_softmax(sel_logit, k);
+            // rank the k selections by (logit desc, expert asc): lane j < k
+            // holds the j-th in ascending expert order (sorted position j)
+            const int j = lane < slots ? lane : 0;
+            const uint32_t kj = (uint32_t)s_sorted[j];
+            const int ej = s_list[j];
+            int rank = 0;
+            for (int m = 0; m < slots; ++m) {
+                const uint32_t km = (uint32_t)s_sorted[m];
+                rank += (km > kj || (km == kj && s_list[m] < ej)) ? 1 : 0;
+            }
             if (lane < slots) {
-                const int i = lane, pos = s_pos[i];
-                R.ids[i] = s_ids[i];
-                R.w[i] = w;
-                R.slot_pos[i] = pos;
-                R.sorted_slots[pos] = i;
+                s_ids[rank] = ej;
+                s_pos[rank] = lane;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);        // this wave's LDS writes land before the reads below
+            const int id = lane < slots ? s_ids[lane] : 0;
+            const float v = lane < slots ? topk_key_value((uint32_t)s_sorted[s_pos[lane]]) : 0.0f;
+            const float w = topk_softmax(v, k);
+            if (lane < slots) {
+                const int pos = s_pos[lane];           // slot `lane` (by logit) sits at sorted position pos
+                R.ids[lane] = id;
+                R.w[lane] = w;
+                R.slot_pos[lane] = pos;
+                R.sorted_slots[pos] = lane;
             }
         }
         const int G = gridDim.x;

@@ -11,7 +11,7 @@
 // expert-sorted permutation (offsets[e] .. offsets[e+1]):
 //   GATEUP: h[p, :] = bf16( silu(gg_e * x_t . G_e^T) * (gu_e * x_t . U_e^T) ),
 //           t = sorted_slots[p] / k          (rows gathered from x)
-//   DOWN:   y[p, :] = gd_e * h_p . D_e^T      (fp32)
+//   DOWN:   y[p, :] = bf16(gd_e * h_p . D_e^T)
 // Workgroup tile: BM rows x 128 h-columns (GATEUP, gate and up together) or
 // BM rows x 256 columns (DOWN); 4 waves, each owning 4 column subtiles of 16
 // and all BM rows, so each weight element is decoded by exactly one wave.
@@ -28,7 +28,8 @@
 // each XCD (workgroup id mod 8) works on a contiguous run of tiles: row tiles
 // that share a weight column tile meet in the same L2.
 //
-// k_combine: out[t] = bf16( sum_j w[t,j] * y[slot_pos[t*k+j]] ), fp32, j order.
+// k_combine: out[t] = bf16( sum_j w[t,j] * y[slot_pos[t*k+j]] ), fp32, j order
+// (y is stored as bf16: half the bytes of the round trip through memory).
 #include "device_common.h"
 #include "internal.h"
 
@@ -51,7 +52,7 @@ struct GemmParams {
     const float* g1;
     const int32_t* counts;
     const int32_t* offsets;
-    void* out;                  // GATEUP: h bf16 [T*k][N]; DOWN: y fp32 [T*k][N]
+    void* out;                  // GATEUP: h bf16 [T*k][N]; DOWN: y bf16 [T*k][N]
     int ntn;                    // column tiles per expert
     float gmul;                 // multiplies the global scales (W4A4 input scale; 1 for W4A16)
     float* hf;                  // gate/up: fp32 h instead of bf16 into out, when set (W4A4)
@@ -237,7 +238,7 @@ __global__ void __launch_bounds__(kGThreads, gemm_wg_per_cu<BM>()) k_grouped_gem
                 }
         } else {
             const float gd = P.g0[e] * P.gmul;
-            float* y = reinterpret_cast<float*>(P.out);
+            uint16_t* y = reinterpret_cast<uint16_t*>(P.out);
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
@@ -247,7 +248,7 @@ __global__ void __launch_bounds__(kGThreads, gemm_wg_per_cu<BM>()) k_grouped_gem
 #pragma unroll
                         for (int ns = 0; ns < NS; ++ns) {
                             const int col = nt * BN + wave * 64 + ns * 16 + lcol;
-                            y[(int64_t)(p0 + r) * P.N + col] = gd * acc[ms][ns][i];
+                            y[(int64_t)(p0 + r) * P.N + col] = f32_to_bf16_rne(gd * acc[ms][ns][i]);
                         }
                     }
                 }
@@ -257,7 +258,7 @@ __global__ void __launch_bounds__(kGThreads, gemm_wg_per_cu<BM>()) k_grouped_gem
 }
 
 // out[t, c..c+7] = bf16( sum_j w[t,j] * y[slot_pos[t*k+j], c..c+7] ), j ascending.
-__global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y, const float* __restrict__ topk_w,
+__global__ void __launch_bounds__(256) k_combine(const uint16_t* __restrict__ y, const float* __restrict__ topk_w,
                                                  const int32_t* __restrict__ slot_pos, int T, int H, int k,
                                                  uint16_t* __restrict__ out) {
     const int t = blockIdx.y;
@@ -267,10 +268,13 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y, co
     for (int j = 0; j < k; ++j) {
         const int slot = t * k + j;
         const float w = topk_w[slot];
-        const float4* src = reinterpret_cast<const float4*>(y + (int64_t)slot_pos[slot] * H + c);
-        const float4 a = src[0], b = src[1];
-        acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
-        acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
+        const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)slot_pos[slot] * H + c);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += w * bf16_bits_to_f32(u[i] & 0xFFFFu);
+            acc[2 * i + 1] += w * bf16_bits_to_f32(u[i] >> 16);
+        }
     }
     uint4 o;
     o.x = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
@@ -365,7 +369,7 @@ moe_status launch_down_grouped(const FwdArgs& a, hipStream_t s) {
 }
 
 moe_status launch_combine(const FwdArgs& a, hipStream_t s) {
-    MOE_LAUNCH("combine", k_combine, dim3((a.H + 2047) / 2048, a.T), dim3(256), 0, s, (const float*)a.y, a.topk_w,
+    MOE_LAUNCH("combine", k_combine, dim3((a.H + 2047) / 2048, a.T), dim3(256), 0, s, (const uint16_t*)a.y, a.topk_w,
                a.slot_pos, a.T, a.H, a.k, a.out);
     return MOE_OK;
 }

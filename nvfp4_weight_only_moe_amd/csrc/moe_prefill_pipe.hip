@@ -32,22 +32,24 @@ namespace {
 
 constexpr int kPT = 512;                        // threads: 8 waves, two per SIMD
 constexpr int kWaves = kPT / 64;
-constexpr int kBM = 128;                        // rows per tile
 constexpr int kBN = 512;                        // weight columns per tile (gate/up: 256 + 256)
 constexpr int kNS = kBN / kWaves / 16;          // 16-column subtiles per wave (a wave owns 64 columns)
 constexpr int kBK = 64;                         // K per stage
 constexpr int kStages = 4;                      // LDS ring
 constexpr int kAhead = kStages - 1;             // stages in flight while one is computed
-constexpr int kABytes = kBM * kBK * 2;          // 16 KiB activations
+// rows per tile, BM = 128 (experts of several hundred rows) or 64 (a few
+// dozen): activation bytes of a stage and the ring layout depend on it
+template <int BM> constexpr int a_bytes() { return BM * kBK * 2; }   // 16 / 8 KiB activations
 constexpr int kBBytes = kBN * kBK / 2;          // 16 KiB codes
 constexpr int kSBytes = kBN * kBK / 16;         // 2 KiB scales
-constexpr int kStageBytes = kABytes + kBBytes + kSBytes;
+template <int BM> constexpr int stage_bytes() { return a_bytes<BM>() + kBBytes + kSBytes; }
 // the ring is three rings, one per operand, so that every LDS read of a
 // stage is a per-stage base plus an immediate offset (all below 64 KiB)
 constexpr int kARing = 0;
-constexpr int kBRing = kStages * kABytes;
-constexpr int kSRing = kBRing + kStages * kBBytes;
+template <int BM> constexpr int b_ring() { return kStages * a_bytes<BM>(); }
+template <int BM> constexpr int s_ring() { return b_ring<BM>() + kStages * kBBytes; }
 constexpr int kMGroup = 8;                      // row tiles per scheduling group
+constexpr int64_t kPipeBM64MaxMeanRows = 96;    // mean rows per touched expert up to which tiles are 64 rows
 #ifndef MOE_PIPE_DMA_WAVES
 #define MOE_PIPE_DMA_WAVES 4
 #endif
@@ -56,13 +58,14 @@ constexpr int kMGroup = 8;                      // row tiles per scheduling grou
 // default) the other wave of each SIMD goes on with its MFMAs while its
 // partner issues; all 8 issuing measured 6 % slower on MI355X.
 constexpr int kDmaWaves = MOE_PIPE_DMA_WAVES;
-constexpr int kADma = kABytes / 1024 / kDmaWaves;
+template <int BM> constexpr int a_dma() { return a_bytes<BM>() / 1024 / kDmaWaves; }
 constexpr int kBDma = kBBytes / 1024 / kDmaWaves;
 constexpr int kSDma = kSBytes / 256 / kDmaWaves;
-constexpr int kOpsPerStage = kADma + kBDma + kSDma;
+template <int BM> constexpr int ops_per_stage() { return a_dma<BM>() + kBDma + kSDma; }
 constexpr int kDmaCols = kBN / kDmaWaves;       // weight columns one DMA wave brings in
-static_assert(kADma * kDmaWaves * 1024 == kABytes && kBDma * 32 == kDmaCols && kSDma * 64 == kDmaCols && kNS == 4,
-              "stage split over the waves");
+static_assert(a_dma<128>() * kDmaWaves * 1024 == a_bytes<128>() && a_dma<64>() * kDmaWaves * 1024 == a_bytes<64>() &&
+              kBDma * 32 == kDmaCols && kSDma * 64 == kDmaCols && kNS == 4, "stage split over the waves");
+static_assert(ops_per_stage<64>() <= 8 && ops_per_stage<128>() <= 10, "DMA points per stage");
 // point (0 .. 7: after which subtile's MFMAs) at which a DMA wave issues
 // op j of a stage; with 8 DMA waves the second wave of each SIMD is offset
 // so that the two do not stall on the load queue together
@@ -81,7 +84,7 @@ struct PipeParams {
     const float* g1;
     const int32_t* counts;
     const int32_t* offsets;
-    void* out;                  // gate/up: h bf16 [T*k][N]; down: y fp32 [T*k][N]
+    void* out;                  // gate/up: h bf16 [T*k][N]; down: y bf16 [T*k][N]
     int ntn;                    // column tiles per expert
     float gmul;                 // multiplies the global scales (W4A4 input scale; 1 for W4A16)
     float* hf;                  // gate/up: fp32 h instead of bf16 into out, when set (W4A4)
@@ -117,6 +120,7 @@ __device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // Tile t of the launch: expert, first sorted row, rows, column tile.  Tiles
 // are numbered expert by expert (prefix over experts in s_prefix) and, inside
 // an expert, in groups of kMGroup row tiles x all column tiles.
+template <int BM>
 __device__ __forceinline__ Tile pipe_tile(const PipeParams& P, const int* s_prefix, const int* s_cnt,
                                           const int* s_off, int t) {
     int lo = 0, hi = P.E - 1;
@@ -125,7 +129,7 @@ __device__ __forceinline__ Tile pipe_tile(const PipeParams& P, const int* s_pref
         if (s_prefix[mid] <= t) lo = mid; else hi = mid - 1;
     }
     const int e = lo, L = t - s_prefix[e], ne = s_cnt[e];
-    const int mte = (ne + kBM - 1) / kBM, full = mte / kMGroup;
+    const int mte = (ne + BM - 1) / BM, full = mte / kMGroup;
     int mt, nt;
     if (L < full * kMGroup * P.ntn) {
         const int g = L / (kMGroup * P.ntn), r = L % (kMGroup * P.ntn);
@@ -138,8 +142,8 @@ __device__ __forceinline__ Tile pipe_tile(const PipeParams& P, const int* s_pref
     }
     Tile d;
     d.e = e;
-    d.p0 = s_off[e] + mt * kBM;
-    d.rows = min(kBM, ne - mt * kBM);
+    d.p0 = s_off[e] + mt * BM;
+    d.rows = min(BM, ne - mt * BM);
     d.nt = nt;
     return d;
 }
@@ -148,12 +152,13 @@ __device__ __forceinline__ Tile pipe_tile(const PipeParams& P, const int* s_pref
 // vector-memory operations are outstanding; then every wave meets at a
 // workgroup barrier that also waits for its LDS reads (the ring slot about
 // to be refilled is no longer read).
+template <int BM>
 __device__ __forceinline__ void stage_barrier(bool dma_wave, int stages_after) {
     if (dma_wave) {
         switch (stages_after) {
             case 0: wait_vmem_at_most<0>(); break;
-            case 1: wait_vmem_at_most<1 * kOpsPerStage>(); break;
-            default: wait_vmem_at_most<2 * kOpsPerStage>(); break;
+            case 1: wait_vmem_at_most<1 * ops_per_stage<BM>()>(); break;
+            default: wait_vmem_at_most<2 * ops_per_stage<BM>()>(); break;
         }
     }
     wait_lds_barrier();
@@ -176,8 +181,8 @@ struct LaneLds {
     int a[2], b, s;
 };
 
-template <bool GATEUP, class Dma>
-__device__ __forceinline__ void stage_mfma(floatx4 (&acc)[8][kNS], const uint8_t* as, const uint8_t* bs,
+template <bool GATEUP, int MS, class Dma>
+__device__ __forceinline__ void stage_mfma(floatx4 (&acc)[MS][kNS], const uint8_t* as, const uint8_t* bs,
                                            const uint8_t* ss, const LaneLds& o, Dma&& dma) {
     // columns of the wave's subtiles relative to its first: gate/up waves
     // own 32 gate columns and the same 32 up columns (SwiGLU pairs them)
@@ -192,9 +197,9 @@ __device__ __forceinline__ void stage_mfma(floatx4 (&acc)[8][kNS], const uint8_t
     bf16x8 bnext = decode8s(cw[0].x, sc[0]);
     // activation fragments: k-step 0 now, k-step 1 in two halves during the
     // k-step 0 MFMAs (after subtiles 1 and 2), so their LDS latency is hidden
-    bf16x8 af[2][8];
+    bf16x8 af[2][MS];
 #pragma unroll
-    for (int ms = 0; ms < 8; ++ms) af[0][ms] = *reinterpret_cast<const bf16x8*>(as + o.a[0] + ms * 2048);
+    for (int ms = 0; ms < MS; ++ms) af[0][ms] = *reinterpret_cast<const bf16x8*>(as + o.a[0] + ms * 2048);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -203,20 +208,21 @@ __device__ __forceinline__ void stage_mfma(floatx4 (&acc)[8][kNS], const uint8_t
             const int nn = ns + 1 < kNS ? ns + 1 : 0;     // next subtile (of the next k-step after the last)
             if (ks == 0 || ns + 1 < kNS) bnext = decode8s((ns + 1 < kNS ? ks : 1) ? cw[nn].y : cw[nn].x, sc[nn]);
 #pragma unroll
-            for (int ms = 0; ms < 8; ++ms)
+            for (int ms = 0; ms < MS; ++ms)
                 acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][ms], bf, acc[ms][ns], 0, 0, 0);
-            // each MFMA followed by two VALU instructions (the next
-            // subtile's decode), so the matrix pipe does not wait for it
+            // each MFMA followed by its share of the next subtile's decode
+            // (16 VALU instructions over the MS MFMAs), so the matrix pipe
+            // does not wait for it
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU
+            for (int i = 0; i < MS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 16 / MS, 0);    // VALU
             }
             dma(ks * kNS + ns);
             if (ks == 0 && (ns == 1 || ns == 2)) {
 #pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const int ms = (ns - 1) * 4 + h;
+                for (int h = 0; h < MS / 2; ++h) {
+                    const int ms = (ns - 1) * (MS / 2) + h;
                     af[1][ms] = *reinterpret_cast<const bf16x8*>(as + o.a[1] + ms * 2048);
                 }
             }
@@ -224,12 +230,15 @@ __device__ __forceinline__ void stage_mfma(floatx4 (&acc)[8][kNS], const uint8_t
     }
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int BM>
 __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
+    constexpr int MS = BM / 16;                               // 16-row subtiles
+    constexpr int kABytes = a_bytes<BM>(), kADma = a_dma<BM>(), kOpsPerStage = ops_per_stage<BM>();
+    constexpr int kBRing = b_ring<BM>(), kSRing = s_ring<BM>();
     extern __shared__ __align__(16) uint8_t ring[];          // activation, code and scale rings
     __shared__ int s_prefix[MOE_MAX_EXPERTS + 1];
     __shared__ int s_cnt[MOE_MAX_EXPERTS], s_off[MOE_MAX_EXPERTS];   // per expert: rows, first sorted row
-    __shared__ __align__(16) int32_t s_rows[2][128];          // sorted-slot values of two tiles (gate/up)
+    __shared__ __align__(16) int32_t s_rows[2][BM];           // sorted-slot values of two tiles (gate/up)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -241,7 +250,7 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
         const int c = P.counts[e];
         s_cnt[e] = c;
         s_off[e] = P.offsets[e];
-        s_prefix[e] = ((c + kBM - 1) / kBM) * P.ntn;
+        s_prefix[e] = ((c + BM - 1) / BM) * P.ntn;
     }
     __syncthreads();
     if (wave == 0) {
@@ -287,8 +296,8 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
 #define MOE_PIPE_ROWS(j, buf)                                                                   \
     do {                                                                                        \
         if (GATEUP && wave == 0 && (j) < ntiles) {                                              \
-            const Tile d_ = pipe_tile(P, s_prefix, s_cnt, s_off, (j) * G + slot);               \
-            _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_) {                                  \
+            const Tile d_ = pipe_tile<BM>(P, s_prefix, s_cnt, s_off, (j) * G + slot);               \
+            _Pragma("unroll") for (int h_ = 0; h_ < BM / 64; ++h_) {                             \
                 const int r_ = 64 * h_ + lane;                                                  \
                 lds_dma4(P.sorted_slots + d_.p0 + (r_ < d_.rows ? r_ : 0),                      \
                          (lds_void*)&s_rows[buf][64 * h_]);                                     \
@@ -299,7 +308,7 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
     // sources of tile j for this wave's DMAs (DMA waves)
 #define MOE_PIPE_ENTER(j)                                                                       \
     do {                                                                                        \
-        const Tile d_ = pipe_tile(P, s_prefix, s_cnt, s_off, (j) * G + slot);                   \
+        const Tile d_ = pipe_tile<BM>(P, s_prefix, s_cnt, s_off, (j) * G + slot);                   \
         const int e_ = __builtin_amdgcn_readfirstlane(d_.e), nt_ = __builtin_amdgcn_readfirstlane(d_.nt); \
         const int rows_ = __builtin_amdgcn_readfirstlane(d_.rows), p0_ = __builtin_amdgcn_readfirstlane(d_.p0); \
         _Pragma("unroll") for (int i_ = 0; i_ < kADma; ++i_) {                                  \
@@ -385,7 +394,7 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
     int g = 0;            // (tile, stage) step being computed
 #pragma unroll 1
     for (int j = 0; j < ntiles; ++j) {
-        const Tile cur = pipe_tile(P, s_prefix, s_cnt, s_off, j * G + slot);
+        const Tile cur = pipe_tile<BM>(P, s_prefix, s_cnt, s_off, j * G + slot);
         // the expert's global scales, by scalar loads: a vector load would be
         // ordered behind the DMA operations in flight, and one still counted
         // as pending across the stage loop makes the compiler wait for all
@@ -393,7 +402,7 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
         const int e_cur = __builtin_amdgcn_readfirstlane(cur.e);
         const float g_a = ((const __attribute__((address_space(4))) float*)P.g0)[e_cur] * P.gmul;
         const float g_b = GATEUP ? ((const __attribute__((address_space(4))) float*)P.g1)[e_cur] * P.gmul : 0.0f;
-        floatx4 acc[8][kNS];
+        floatx4 acc[MS][kNS];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -402,13 +411,13 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
         for (int st = 0; st < nst; ++st, ++g) {
             {
                 const int after = nsteps - 1 - g;
-                stage_barrier(dma_wave, after < kAhead - 1 ? after : kAhead - 1);
+                stage_barrier<BM>(dma_wave, after < kAhead - 1 ? after : kAhead - 1);
             }
             // a DMA wave spreads stage g + kAhead's loads over this stage's MFMAs
             const bool issuing = dma_wave && g + kAhead < nsteps;
             if (issuing) MOE_PIPE_BEGIN();   /* before the first op: it may set up a new tile */
             const int rs = g & (kStages - 1);
-            stage_mfma<GATEUP>(acc, ring + kARing + rs * kABytes, ring + kBRing + rs * kBBytes,
+            stage_mfma<GATEUP, MS>(acc, ring + kARing + rs * kABytes, ring + kBRing + rs * kBBytes,
                                ring + kSRing + rs * kSBytes, lo, [&](int p) {
                 if (issuing) {
 #pragma unroll
@@ -424,7 +433,7 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
             const float gg = g_a, gu = g_b;
             uint16_t* h = reinterpret_cast<uint16_t*>(P.out);
 #pragma unroll
-            for (int ms = 0; ms < 8; ++ms)
+            for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = ms * 16 + kq * 4 + i;
@@ -443,9 +452,9 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
                 }
         } else {
             const float gd = g_a;
-            float* y = reinterpret_cast<float*>(P.out);
+            uint16_t* y = reinterpret_cast<uint16_t*>(P.out);
 #pragma unroll
-            for (int ms = 0; ms < 8; ++ms)
+            for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = ms * 16 + kq * 4 + i;
@@ -453,7 +462,7 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
 #pragma unroll
                         for (int ns = 0; ns < kNS; ++ns) {
                             const int col = cur.nt * kBN + 64 * wave + 16 * ns + lcol;
-                            y[(int64_t)(cur.p0 + r) * P.N + col] = gd * acc[ms][ns][i];
+                            y[(int64_t)(cur.p0 + r) * P.N + col] = f32_to_bf16_rne(gd * acc[ms][ns][i]);
                         }
                     }
                 }
@@ -474,16 +483,27 @@ int cu_count_pipe() {
     return n;
 }
 
-template <bool GATEUP>
-moe_status launch_pipe(const PipeParams& P, int64_t slots, hipStream_t s) {
-    const size_t shmem = (size_t)kStages * kStageBytes;
-    if (allow_dynamic_lds(reinterpret_cast<const void*>(&k_gemm_pipe<GATEUP>), shmem) != MOE_OK) return MOE_ERR_HIP;
-    const int64_t tiles_ub = (slots / kBM + std::min<int64_t>(P.E, slots)) * P.ntn;
+template <bool GATEUP, int BM>
+moe_status launch_pipe_bm(const PipeParams& P, int64_t slots, hipStream_t s) {
+    const size_t shmem = (size_t)kStages * stage_bytes<BM>();
+    if (allow_dynamic_lds(reinterpret_cast<const void*>(&k_gemm_pipe<GATEUP, BM>), shmem) != MOE_OK)
+        return MOE_ERR_HIP;
+    const int64_t tiles_ub = (slots / BM + std::min<int64_t>(P.E, slots)) * P.ntn;
     int64_t g = std::min<int64_t>(tiles_ub, cu_count_pipe());
     if (g >= 8) g = g / 8 * 8;
     g = std::max<int64_t>(g, 1);
-    MOE_LAUNCH(GATEUP ? "gemm_gateup" : "gemm_down", k_gemm_pipe<GATEUP>, dim3((unsigned)g), dim3(kPT), shmem, s, P);
+    MOE_LAUNCH(GATEUP ? "gemm_gateup" : "gemm_down", (k_gemm_pipe<GATEUP, BM>), dim3((unsigned)g), dim3(kPT), shmem, s,
+               P);
     return MOE_OK;
+}
+
+// Row tile by the mean rows per touched expert: 64-row tiles hold a whole
+// expert of a 1K-token prefill (about 32 rows, up to ~60) with half the
+// padding of 128-row tiles.
+template <bool GATEUP>
+moe_status launch_pipe(const PipeParams& P, int64_t slots, hipStream_t s) {
+    const int64_t avg = slots / std::max<int64_t>(1, std::min<int64_t>(P.E, slots));
+    return avg <= kPipeBM64MaxMeanRows ? launch_pipe_bm<GATEUP, 64>(P, slots, s) : launch_pipe_bm<GATEUP, 128>(P, slots, s);
 }
 
 }  // namespace

@@ -79,6 +79,51 @@ __device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int
     v_out = my_v;
 }
 
+// The k largest of one token's E logits as a SET, by a threshold search
+// instead of k rounds of arg-max: the k-th largest order-preserving key is
+// found bit by bit from the top (keep a bit when at least k keys reach the
+// prefix with it set; one ballot per candidate slot and bit), stopping as
+// soon as exactly k keys reach the prefix; keys equal to the final threshold
+// are then taken in ascending expert index until k are taken.  EPL = logits
+// per lane (lane l holds experts l, l + 64, ...).  On return key[i] holds the
+// key of expert 64 i + lane and bit `lane` of sel[i] says whether it is
+// selected; exactly k bits are set, and ascending (i, lane) is ascending
+// expert index.  -0.0 is folded into +0.0, a NaN logit ranks as -inf and
+// experts past E get key 0, below every real logit (the same order as
+// wave_topk_ids).
+template <int EPL>
+__device__ __forceinline__ void wave_topk_set(const float* __restrict__ row, int E, int k, uint32_t (&key)[EPL],
+                                              uint64_t (&sel)[EPL]) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int idx = lane + kWave * i;
+        const float x = idx < E ? row[idx] + 0.0f : 0.0f;
+        key[i] = idx < E ? topk_key(x != x ? -INFINITY : x) : 0u;
+    }
+    uint32_t P = 0u;                                   // count(key >= P) >= k throughout
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t T = P | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) cnt += __popcll(__ballot(key[i] >= T));
+        if (cnt >= k) {
+            P = T;
+            if (cnt == k) break;                       // exactly k keys reach P: the set is found
+        }
+    }
+    int need = k;                                      // keys above P are all selected
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) need -= __popcll(__ballot(key[i] > P));
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {                    // then keys equal to P, lowest expert first
+        const uint64_t eq = __ballot(key[i] == P);
+        const bool take = key[i] > P || (key[i] == P && __popcll(eq & lanemask_lt()) < need);
+        sel[i] = __ballot(take);
+        need -= __popcll(sel[i] & eq);
+    }
+}
+
 // Routing weights of a wave_topk_ids selection: softmax over the k selected
 // logits (lane j < k holds the j-th), computed from the largest.
 __device__ __forceinline__ float topk_softmax(float my_v, int k) {

@@ -105,7 +105,7 @@ def test_quantize_dequantize_validate_argument_errors(L):
 def test_workspace_sizes(L):
     assert L.moe_w4a16_workspace_size(0, 5120, 1536, 256, 8) == 0
     need = L.moe_w4a16_workspace_size(16, 256, 128, 8, 2)
-    assert need >= 16 * 2 * (128 * 2 + 256 * 4)
+    assert need >= 16 * 2 * (128 * 2 + 256 * 2)
     assert need % 256 == 0
 
 
@@ -131,12 +131,12 @@ def test_route_forward_argument_errors(L):
 
 
 def test_forward_workspace_layout_size(L):
-    # h (bf16 [T*k][I]) then y (fp32 [T*k][H]); nothing before them
+    # h (bf16 [T*k][I]) then y (bf16 [T*k][H]); nothing before them
     T, H, I, E, k = 3, 1024, 512, 16, 4
-    assert L.moe_w4a16_workspace_size(T, H, I, E, k) == T * k * I * 2 + T * k * H * 4
+    assert L.moe_w4a16_workspace_size(T, H, I, E, k) == T * k * I * 2 + T * k * H * 2
     # large T also carries the route scratch
     assert L.moe_w4a16_workspace_size(1000, H, I, E, k) >= (
-        1000 * k * (I * 2 + H * 4) + L.moe_route_workspace_size(1000, E, k))
+        1000 * k * (I * 2 + H * 2) + L.moe_route_workspace_size(1000, E, k))
 
 
 def test_removed_entry_points_are_gone(L):
@@ -173,7 +173,7 @@ def test_linear_argument_errors(L):
     assert lin(L, out=A) == -1                                     # out overlaps x
     assert lin(L, ws=0) == -7                                      # no workspace
     assert lin(L, ws_bytes=16) == -7                               # workspace too small
-    assert L.moe_w4a16_linear_workspace_size(4, 1024, 512) >= 4 * 512 * 4
+    assert L.moe_w4a16_linear_workspace_size(4, 1024, 512) >= 4 * 512 * 2
     assert L.moe_w4a16_linear_workspace_size(0, 1024, 512) == 0
 
 

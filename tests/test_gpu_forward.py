@@ -294,3 +294,31 @@ def test_prefill_long_expert_every_tile(T, H, I, E, k, seed, bm):
             assert max(tiles) <= 1e-2, (v, int(np.argmax(tiles)))
     finally:
         B.moe_debug_set_prefill_variant(2)
+
+
+@pytest.mark.parametrize("E,k,ties", [(300, 8, False), (1024, 32, False), (1024, 8, True), (64, 32, True),
+                                      (256, 1, False), (9, 8, True)])
+def test_one_token_in_kernel_route(E, k, ties):
+    """One token routed inside the gate/up kernel (threshold selection): every
+    routing output equals moe_route_topk's and the oracle's, and the layer
+    output equals the two-call path's, bit for bit -- wide routers (up to
+    1024 experts, 16 logits per lane), k up to 64, exact ties.  The weights
+    come from the GPU quantizer (no layer oracle needed for equality)."""
+    H, I = 1024, 512
+    g = torch.Generator(device=DEV).manual_seed(E * 100 + k)
+    stacks = [B.moe_w4a16_quantize_pack(0.02 * torch.randn((E,) + s, device=DEV, generator=g))
+              for s in ((I, H), (I, H), (H, I))]
+    r = np.random.default_rng(E + k)
+    lg_np = (r.integers(-3, 4, size=(1, E)) if ties else r.standard_normal((1, E))).astype(np.float32)
+    if ties:
+        lg_np[0, :: 7] = -0.0
+    x = to_dev(wls.to_bf16_bits(r.standard_normal((1, H)).astype(np.float32)).view(np.int16))
+    lg = to_dev(lg_np)
+    out_ref, r_ref = guarded_forward(x, *stacks, lg, k, fused=False)
+    out, r_got = guarded_forward(x, *stacks, lg, k, fused=True)
+    for name in ("topk_ids", "topk_w", "counts", "offsets", "sorted_slots", "slot_pos"):
+        assert torch.equal(getattr(r_got, name), getattr(r_ref, name)), name
+    ids, w = oracle.route_topk(lg_np, k)
+    assert np.array_equal(r_got.topk_ids.cpu().numpy(), ids)
+    assert np.max(np.abs(r_got.topk_w.cpu().numpy() - w)) <= 1e-6
+    assert torch.equal(out, out_ref)
