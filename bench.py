@@ -69,6 +69,10 @@ def parse():
                          "1 LDS-pipelined, 2 chosen per product by rows per expert (default)")
     ap.add_argument("--split", action="store_true",
                     help="step = moe_route_topk + moe_w4a16_forward (two calls) instead of route_forward")
+    ap.add_argument("--router", choices=("none", "fused", "separate"), default="none",
+                    help="start the step from the BF16 router GEMM (router weights N(0, 1/H); the routing then "
+                         "follows x, not the workload's drawn logits): fused = moe_router_route_topk + "
+                         "moe_w4a16_forward, separate = moe_router_logits + moe_w4a16_route_forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM counter scaling)")
     ap.add_argument("--op", choices=("moe", "linear", "shared", "router"), default="moe",
@@ -252,9 +256,20 @@ def bench_moe_config(args, cfg, base, cache):
     out = torch.empty((wl.T, wl.H), dtype=torch.int16, device=dev)
     ws = B.forward_workspace(wl.T, wl.H, wl.I, wl.E, wl.k, dev)
 
+    if args.router != "none":
+        _, _, wb, _ = wls.router_problem(7, 1, wl.H, wl.E)
+        wr_d = torch.from_numpy(wb.view(np.int16)).to(dev)
+        rws = B.router_route_workspace(wl.T, wl.E, wl.k, dev)
+
     def step(i):
         L = layers[i % copies]
-        if args.split:
+        if args.router == "fused":
+            B.moe_router_route_topk(x_d, wr_d, wl.k, logits=lg_d, routing=route, ws=rws)
+            B.moe_w4a16_forward(x_d, L["gate"], L["up"], L["down"], route, out=out, ws=ws)
+        elif args.router == "separate":
+            B.moe_router_logits(x_d, wr_d, out=lg_d)
+            B.moe_w4a16_route_forward(lg_d, x_d, L["gate"], L["up"], L["down"], wl.k, routing=route, out=out, ws=ws)
+        elif args.split:
             B.moe_route_topk(lg_d, wl.k, out=route)
             B.moe_w4a16_forward(x_d, L["gate"], L["up"], L["down"], route, out=out, ws=ws)
         else:
@@ -337,6 +352,8 @@ def bench_moe_config(args, cfg, base, cache):
     H, I, T, k = wl.H, wl.I, wl.T, wl.k
     w_gu, w_d = 2 * packed_bytes(I, H), packed_bytes(H, I)
     alg_bytes_step = U * (w_gu + w_d) + T * H * 2 * 2 + T * wl.E * 4
+    if args.router != "none":
+        alg_bytes_step += wl.E * H * 2                  # the BF16 router weight
     flops_step = 6.0 * T * k * H * I
     # (algorithmic bytes, flops) per launch; the grouped GEMMs read every
     # touched expert's weights once and do 2 flops per weight per row
@@ -346,6 +363,8 @@ def bench_moe_config(args, cfg, base, cache):
         "dec_down": (U * w_d + T * H * 2, None),
         "gemm_gateup": (U * w_gu + T * H * 2, 4.0 * T * k * H * I),
         "gemm_down": (U * w_d + T * H * 2, 2.0 * T * k * H * I),
+        "router_route": (wl.E * H * 2 + T * H * 2 + T * wl.E * 4, None),
+        "router_gemv": (wl.E * H * 2 + T * H * 2 + T * wl.E * 4, None),
     }
     work_bytes, work_flops = kernel_work.get(dominant, (alg_bytes_step, None))
     roofline = make_roofline(dominant, dom_us, work_bytes, work_flops, measured_traffic(dominant, wl.name))
@@ -356,7 +375,9 @@ def bench_moe_config(args, cfg, base, cache):
         "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": wl.E, "k": k, "layer_copies": copies,
                    "hip_graph": graph_ms is not None, "touched_experts": U,
                    "max_rows_per_expert": int(counts.max()),
-                   "step_calls": "route_topk+forward" if args.split else "route_forward",
+                   "step_calls": ("router_route_topk+forward" if args.router == "fused" else
+                                  "router_logits+route_forward" if args.router == "separate" else
+                                  "route_topk+forward" if args.split else "route_forward"),
                    "prefill_variant": None if decode else args.prefill_variant},
         "roofline": roofline, "cpu_baseline": None, "step_spread": spread,
         "step_algorithmic_GBps": round(alg_bytes_step / sec / 1e9, 1),

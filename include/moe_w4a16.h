@@ -299,6 +299,31 @@ moe_status moe_router_logits(const uint16_t *d_x, int32_t T, int32_t H,
                              hipStream_t stream);
 
 /*
+ * The router GEMM and the route in one call: moe_router_logits followed by
+ * moe_route_topk, with identical outputs (the logits too), for the BF16 gate
+ * in front of the top-k (routers stay BF16: "GLM-5.3-Flash on Blackwell",
+ * "The quantization"; the scoring rule is moe_route_topk's reading).  For
+ * decode token counts (1-8 tokens, T * k <= 64) it is ONE launch: every
+ * workgroup computes its expert's logits and takes a ticket, and the
+ * workgroup that takes the last one routes all tokens; other shapes run the
+ * router kernels and then the route kernels.
+ *   arguments as moe_router_logits (d_x, T, H, d_wr, E, d_logits) and
+ *   moe_route_topk (k and the six routing outputs)
+ *   d_ws   moe_router_route_workspace_size(T, E, k) bytes.  Its first 4 bytes
+ *          are the ticket counter: they must be ZERO before the first call on
+ *          a workspace (allocate it zero-filled), and every call leaves them
+ *          zero.  Calls that share a workspace must be ordered on one stream.
+ * Deterministic; graph-capturable (no memset, no allocation).
+ */
+size_t moe_router_route_workspace_size(int32_t T, int32_t E, int32_t k);
+moe_status moe_router_route_topk(const uint16_t *d_x, int32_t T, int32_t H, const uint16_t *d_wr,
+                                 int32_t E, int32_t k, float *d_logits,
+                                 int32_t *d_topk_ids, float *d_topk_w,
+                                 int32_t *d_counts, int32_t *d_offsets,
+                                 int32_t *d_sorted_slots, int32_t *d_slot_pos,
+                                 void *d_ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Dense NVFP4 weight-only projection of T tokens: out = bf16(g * x . Wd^T),
  * Wd the dequantized [N][K] weight (E2M1 code * E4M3 group scale), g its
  * FP32 global scale, products accumulated in fp32 and rounded once (the dense

@@ -65,6 +65,8 @@ _SIGS = {
                               _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
     "moe_w4a16_route_forward_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _I, _TP, _TP, _TP, _P, _P, _P, _P, _P, _P, _P,
                                              _P]),
+    "moe_router_route_workspace_size": (_S, [_I, _I, _I]),
+    "moe_router_route_topk": (_I, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
     "moe_profile_begin": (_I, [_I]),
     "moe_profile_end": (_I, [_P, _P, _P, _I]),
 }
@@ -445,3 +447,32 @@ def moe_w4a16_route_forward_noalloc(logits, x_bits, gate, up, down, k, routing=N
                                                  _ptr(routing.sorted_slots), _ptr(routing.slot_pos), _ptr(out),
                                                  _stream(stream)), "moe_w4a16_route_forward_noalloc")
     return out, routing
+
+
+def router_route_workspace(T, E, k, device="cuda"):
+    """A workspace for moe_router_route_topk, zero-filled (its ticket word
+    must start at zero; every call leaves it zero)."""
+    n = int(lib().moe_router_route_workspace_size(T, E, k))
+    return torch.zeros((max(n, 256),), dtype=torch.uint8, device=device)
+
+
+def moe_router_route_topk(x_bits, wr_bits, k, logits=None, routing=None, ws=None, stream=None):
+    """Router logits and the route in one call: bf16 bits x [T, H], router
+    weight [E, H] -> (fp32 logits [T, E], Routing)."""
+    _dev_tensor(x_bits, "x", _BITS16)
+    _dev_tensor(wr_bits, "wr", _BITS16)
+    T, H = x_bits.shape
+    E, H2 = wr_bits.shape
+    if H2 != H:
+        raise ValueError(f"wr: {H2} columns, x has {H}")
+    logits = torch.empty((T, E), dtype=torch.float32, device=x_bits.device) if logits is None else logits
+    _dev_tensor(logits, "logits", torch.float32, (T, E))
+    routing = Routing.empty(T, E, k, x_bits.device) if routing is None else routing
+    routing.check(T, E, k)
+    ws = router_route_workspace(T, E, k, x_bits.device) if ws is None else ws
+    _dev_tensor(ws, "ws", min_bytes=int(lib().moe_router_route_workspace_size(T, E, k)))
+    _check(lib().moe_router_route_topk(_ptr(x_bits), T, H, _ptr(wr_bits), E, k, _ptr(logits), _ptr(routing.topk_ids),
+                                       _ptr(routing.topk_w), _ptr(routing.counts), _ptr(routing.offsets),
+                                       _ptr(routing.sorted_slots), _ptr(routing.slot_pos), _ptr(ws), ws.numel(),
+                                       _stream(stream)), "moe_router_route_topk")
+    return logits, routing

@@ -67,5 +67,40 @@ def build(verbose=False, jobs=None):
     return LIB
 
 
+ASAN_LIB = os.path.join(BUILD, "libmoe_w4a16_asan.so")
+
+
+CLANGXX = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang++")
+
+
+def asan_runtime():
+    """Path of the host compiler's AddressSanitizer runtime (to preload)."""
+    r = subprocess.run([CLANGXX, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build_asan():
+    """A copy of the library whose host code -- the C ABI's argument checking
+    and dispatch, abi.cpp, which holds no device code -- is compiled as plain
+    C++ by the host compiler with AddressSanitizer; every other object is the
+    normal build's.  For the CPU tests of the C ABI under ASan (the runtime is
+    preloaded into that test's process).  Returns its path."""
+    if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(s)[0] + ".o")) for s in SOURCES):
+        build()
+    obj = os.path.join(BUILD, "abi_asan.o")
+    cmd = [CLANGXX, "-std=c++17", "-O1", "-fPIC", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", f"-I{INCLUDE}",
+           f"-I{CSRC}", "-fsanitize=address", "-fno-omit-frame-pointer", "-c", os.path.join(CSRC, "abi.cpp"),
+           "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"clang++ (ASan) failed for abi.cpp:\n{r.stderr}")
+    objs = [obj] + [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "abi.cpp"]
+    r = subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", ASAN_LIB],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (ASan) failed:\n{r.stdout}{r.stderr}")
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -455,6 +455,49 @@ moe_status moe_router_logits(const uint16_t* d_x, int32_t T, int32_t H, const ui
     return launch_router_logits(d_x, T, H, d_wr, E, d_logits, stream);
 }
 
+// Router + route workspace: [ticket word (zero between calls) | padding to
+// 256 B | route scratch of the unfused path].
+constexpr size_t kTicketBytes = 256;
+
+size_t moe_router_route_workspace_size(int32_t T, int32_t E, int32_t k) {
+    if (T <= 0 || E < 1 || k < 1) return kTicketBytes;
+    return kTicketBytes + round_up(route_workspace_bytes(T, E, k), kAlign);
+}
+
+moe_status moe_router_route_topk(const uint16_t* d_x, int32_t T, int32_t H, const uint16_t* d_wr, int32_t E,
+                                 int32_t k, float* d_logits, int32_t* d_topk_ids, float* d_topk_w,
+                                 int32_t* d_counts, int32_t* d_offsets, int32_t* d_sorted_slots,
+                                 int32_t* d_slot_pos, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+    if (T < 0 || H < 1 || E < 1 || k < 1 || !router_shape_supported(T, H, E)) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || k > E) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)T * H > (int64_t)INT32_MAX || (int64_t)E * H > (int64_t)INT32_MAX ||
+        (int64_t)T * E > (int64_t)INT32_MAX || (int64_t)T * k > (int64_t)INT32_MAX / 2)
+        return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    const void* ptrs[] = {d_x, d_wr, d_logits, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots,
+                          d_slot_pos};
+    for (const void* p : ptrs) {
+        if (!p) return MOE_ERR_INVALID_ARG;
+        if (!aligned16(p)) return MOE_ERR_ALIGN;
+    }
+    if (!d_ws) return MOE_ERR_WORKSPACE;
+    if (!aligned16(d_ws)) return MOE_ERR_ALIGN;
+    const size_t need = moe_router_route_workspace_size(T, E, k);
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    const size_t lb = (size_t)T * E * sizeof(float);
+    if (ranges_overlap(d_logits, lb, d_x, (size_t)T * H * 2) || ranges_overlap(d_logits, lb, d_wr, (size_t)E * H * 2) ||
+        ranges_overlap(d_ws, need, d_logits, lb))
+        return MOE_ERR_INVALID_ARG;
+    uint32_t* ticket = static_cast<uint32_t*>(d_ws);
+    if (router_route_fused_supported(T, H, E, k))
+        return launch_router_route(d_x, T, H, d_wr, E, k, d_logits, ticket, d_topk_ids, d_topk_w, d_counts,
+                                   d_offsets, d_sorted_slots, d_slot_pos, stream);
+    moe_status st = launch_router_logits(d_x, T, H, d_wr, E, d_logits, stream);
+    if (st != MOE_OK) return st;
+    return launch_route(d_logits, T, E, k, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots, d_slot_pos,
+                        static_cast<uint8_t*>(d_ws) + kTicketBytes, stream);
+}
+
 size_t moe_w4a16_linear_workspace_size(int32_t T, int32_t K, int32_t N) {
     if (T <= 0 || K <= 0 || N <= 0) return 0;
     return linear_workspace_bytes(T, K, N);

@@ -55,6 +55,13 @@ moe_status launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
 bool router_shape_supported(int T, int H, int E);
 moe_status launch_router_logits(const uint16_t* x, int T, int H, const uint16_t* w, int E, float* logits,
                                 hipStream_t s);
+// router logits and the route in one launch (decode token counts: 1-8
+// tokens, T * k <= 64); ticket: a device word that is zero on entry and is
+// left zero
+bool router_route_fused_supported(int T, int H, int E, int k);
+moe_status launch_router_route(const uint16_t* x, int T, int H, const uint16_t* w, int E, int k, float* logits,
+                               uint32_t* ticket, int32_t* ids, float* wts, int32_t* counts, int32_t* offsets,
+                               int32_t* sorted_slots, int32_t* slot_pos, hipStream_t s);
 // routing of one always-on expert (E = 1, k = 1, weight 1; sorted order = token order)
 moe_status launch_route_identity(int T, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
                                  int32_t* sorted_slots, int32_t* slot_pos, hipStream_t s);

@@ -52,7 +52,10 @@ constexpr int kDownMaxWaves = 12;
 // load sequence (each costs a memory latency).
 template <int MAXT> constexpr int down_chunk_experts() { return MAXT == 1 ? 8 : 16; }
 template <int MAXT> constexpr int down_chunk_slots() { return MAXT == 1 ? 16 : 48; }
-constexpr int kDownAhead = 3;           // experts' down codes in flight ahead of the one computed
+#ifndef MOE_DOWN_AHEAD
+#define MOE_DOWN_AHEAD 3
+#endif
+constexpr int kDownAhead = MOE_DOWN_AHEAD;   // experts' down codes in flight ahead of the one computed
 constexpr int kDownRows = 1;            // output rows per half-wave (more: fewer waves, measured slower)
 constexpr int kDecodeMaxSlots = 64;     // T * k on the decode path
 constexpr int kXTokens = 2;             // activation rows staged in LDS at a time (gate/up)
@@ -256,9 +259,12 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
             const uint32_t kj = (uint32_t)s_sorted[j];
             const int ej = s_list[j];
             int rank = 0;
-            for (int m = 0; m < slots; ++m) {
-                const uint32_t km = (uint32_t)s_sorted[m];
-                rank += (km > kj || (km == kj && s_list[m] < ej)) ? 1 : 0;
+#pragma unroll
+            for (int m = 0; m < MOE_MAX_TOPK; ++m) {   // slots = k <= 32 with one token
+                if (m < slots) {
+                    const uint32_t km = (uint32_t)s_sorted[m];
+                    rank += (km > kj || (km == kj && s_list[m] < ej)) ? 1 : 0;
+                }
             }
             if (lane < slots) {
                 s_ids[rank] = ej;

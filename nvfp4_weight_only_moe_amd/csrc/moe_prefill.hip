@@ -36,9 +36,6 @@
 namespace moe {
 namespace {
 
-constexpr int kGThreads = 256;
-constexpr int kBK = 128;                    // K per stage
-constexpr int kLdsRow = kBK * 2 + 16;       // bytes per staged activation row (padded)
 constexpr int kMGroup = 8;                  // row tiles per scheduling group
 
 struct GemmParams {
@@ -71,33 +68,63 @@ __device__ __forceinline__ bf16x8 decode8(uint32_t word, float s) {
     return __builtin_bit_cast(bf16x8, r);
 }
 
-// Workgroups per CU: the 32-row tiles fit three (164 VGPRs), which keeps
-// more weight loads in flight at the few rows per expert they serve.
-template <int BM> constexpr int gemm_wg_per_cu() { return BM >= 128 ? 1 : BM == 32 ? 3 : 2; }
+// Workgroups per CU: with four waves the 32-row tiles fit three (164
+// VGPRs), which keeps more weight loads in flight at the few rows per
+// expert they serve; eight-wave workgroups run one per CU.
+template <int BM, int NW> constexpr int gemm_wg_per_cu() {
+    return NW == 8 ? 1 : BM >= 128 ? 1 : BM == 32 ? 3 : 2;
+}
 
-template <bool GATEUP, int BM>
-__global__ void __launch_bounds__(kGThreads, gemm_wg_per_cu<BM>()) k_grouped_gemm(GemmParams P) {
+// NW waves, each owning 4 column subtiles of 16 (gate/up: 32 h columns as 32
+// gate + 32 up weight rows; down: 64 output columns) for all BM rows, so the
+// tile is BM rows x 32 NW (gate/up) or 64 NW (down) columns and each weight
+// element is decoded by exactly one wave.  BK = K per stage: 128, or 256 so
+// that a weight row's codes of one stage fill a whole 128-byte line (its
+// next bytes are not left for a later stage, when another tile's lines may
+// have evicted the line from L2).
+template <bool GATEUP, int BM, int BK, int NW>
+__global__ void __launch_bounds__(NW * kWave, (gemm_wg_per_cu<BM, NW>())) k_grouped_gemm(GemmParams P) {
+    constexpr int kThreads = NW * kWave;
     constexpr int MS = BM / 16;                 // row subtiles
     constexpr int NS = 4;                       // column subtiles per wave
-    constexpr int APASS = BM / 16;              // 16 rows per pass of the A loader
-    constexpr int BN = GATEUP ? 128 : 256;      // output columns per tile
+    constexpr int BN = (GATEUP ? 32 : 64) * NW; // output columns per tile
+    constexpr int kLdsRow = BK * 2 + 16;        // bytes per staged activation row (padded)
+    constexpr int kRowChunks = BK * 2 / 16;     // 16-byte activation chunks per row per stage
+    constexpr int APT = BM * kRowChunks / kThreads;   // activation chunks per thread per stage
+    constexpr int KSTEPS = BK / 32;             // MFMA k-steps per stage
+    constexpr int CW = BK / 128;                // 16-byte code words per lane per subtile per stage
+    static_assert(APT * kThreads == BM * kRowChunks, "activation stage split over the threads");
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_prefix[MOE_MAX_EXPERTS + 1];
-    __shared__ int s_cnt[MOE_MAX_EXPERTS];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lcol = lane & 15, kq = lane >> 4;
 
-    // tiles per expert -> exclusive prefix
-    for (int e = tid; e < P.E; e += kGThreads) s_cnt[e] = ((P.counts[e] + BM - 1) / BM) * P.ntn;
+    // tiles per expert -> exclusive prefix (wave 0, DPP scan over lane runs)
+    for (int e = tid; e < P.E; e += kThreads) s_prefix[e] = ((P.counts[e] + BM - 1) / BM) * P.ntn;
     __syncthreads();
-    block_exclusive_scan(s_cnt, s_prefix, P.E);
+    if (wave == 0) {
+        const int per = (P.E + kWave - 1) / kWave, b = lane * per;
+        int local = 0;
+        for (int i = 0; i < per; ++i)
+            if (b + i < P.E) local += s_prefix[b + i];
+        const int incl = wave_inclusive_scan_dpp(local);
+        int run = incl - local;
+        for (int i = 0; i < per; ++i)
+            if (b + i < P.E) {
+                const int c = s_prefix[b + i];
+                s_prefix[b + i] = run;
+                run += c;
+            }
+        if (lane == kWave - 1) s_prefix[P.E] = incl;
+    }
+    __syncthreads();
     const int total = s_prefix[P.E];
 
     const int G = gridDim.x;
     const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
     const bool remap = (G & 7) == 0;
-    const int nst = P.K / kBK;
+    const int nst = P.K / BK;
 
     for (int it = 0;; ++it) {
         const int tile = it * G + (remap ? xcd * (G >> 3) + q : (int)blockIdx.x);
@@ -126,17 +153,19 @@ __global__ void __launch_bounds__(kGThreads, gemm_wg_per_cu<BM>()) k_grouped_gem
         const int p0 = P.offsets[e] + mt * BM;
         const int rows = min(BM, ne - mt * BM);
 
-        // activation rows this thread stages (16 threads per row, 16 B each)
-        int64_t a_off[APASS];
+        // activation chunks this thread stages: chunk c = tid + kThreads * i
+        // of the stage, row c / kRowChunks, 16-byte unit c % kRowChunks
+        int64_t a_off[APT];
 #pragma unroll
-        for (int ps = 0; ps < APASS; ++ps) {
-            const int r = (tid >> 4) + 16 * ps;
+        for (int i = 0; i < APT; ++i) {
+            const int c = tid + kThreads * i;
+            const int r = c / kRowChunks;
             int64_t off = -1;
             if (r < rows) {
                 const int64_t src_row = GATEUP ? (int64_t)(P.sorted_slots[p0 + r] / P.topk) : (int64_t)(p0 + r);
-                off = src_row * P.K + (tid & 15) * 8;
+                off = src_row * P.K + (c % kRowChunks) * 8;
             }
-            a_off[ps] = off;
+            a_off[i] = off;
         }
         // weight rows of this wave's column subtiles
         const uint8_t* cp[NS];
@@ -155,8 +184,8 @@ __global__ void __launch_bounds__(kGThreads, gemm_wg_per_cu<BM>()) k_grouped_gem
                 sb = P.s0;
             }
             const int64_t row = (int64_t)e * P.N + col;
-            cp[ns] = cb + row * (P.K / 2) + kq * 16;
-            sp[ns] = sb + row * (P.K / 16) + kq * 2;
+            cp[ns] = cb + row * (P.K / 2) + kq * 16 * CW;
+            sp[ns] = sb + row * (P.K / 16) + kq * 2 * CW;
         }
 
         floatx4 acc[MS][NS];
@@ -165,48 +194,60 @@ __global__ void __launch_bounds__(kGThreads, gemm_wg_per_cu<BM>()) k_grouped_gem
 #pragma unroll
             for (int j = 0; j < NS; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-        uint4 a_reg[APASS];
-        uint4 b_code[NS];
+        uint4 a_reg[APT];
+        uint4 b_code[NS][CW];
         uint32_t b_scale[NS];
         auto load_stage = [&](int st) {
-            const int k0 = st * kBK;
+            const int k0 = st * BK;
 #pragma unroll
-            for (int ps = 0; ps < APASS; ++ps)
-                a_reg[ps] = a_off[ps] >= 0 ? *reinterpret_cast<const uint4*>(P.a + a_off[ps] + k0)
-                                           : make_uint4(0, 0, 0, 0);
+            for (int i = 0; i < APT; ++i)
+                a_reg[i] = a_off[i] >= 0 ? *reinterpret_cast<const uint4*>(P.a + a_off[i] + k0) : make_uint4(0, 0, 0, 0);
 #pragma unroll
             for (int ns = 0; ns < NS; ++ns) {
-                b_code[ns] = *reinterpret_cast<const uint4*>(cp[ns] + k0 / 2);
-                b_scale[ns] = *reinterpret_cast<const uint16_t*>(sp[ns] + k0 / 16);
+#pragma unroll
+                for (int w = 0; w < CW; ++w) b_code[ns][w] = *reinterpret_cast<const uint4*>(cp[ns] + k0 / 2 + 16 * w);
+                if constexpr (CW == 1) b_scale[ns] = *reinterpret_cast<const uint16_t*>(sp[ns] + k0 / 16);
+                else b_scale[ns] = *reinterpret_cast<const uint32_t*>(sp[ns] + k0 / 16);
             }
         };
         load_stage(0);
         for (int st = 0; st < nst; ++st) {
             uint8_t* buf = smem + (st & 1) * (BM * kLdsRow);
 #pragma unroll
-            for (int ps = 0; ps < APASS; ++ps)
-                *reinterpret_cast<uint4*>(buf + ((tid >> 4) + 16 * ps) * kLdsRow + (tid & 15) * 16) = a_reg[ps];
-            const uint4 cur_code[NS] = {b_code[0], b_code[1], b_code[2], b_code[3]};
-            const uint32_t cur_scale[NS] = {b_scale[0], b_scale[1], b_scale[2], b_scale[3]};
-            __syncthreads();
-            if (st + 1 < nst) load_stage(st + 1);
-            float sc[NS][2];
+            for (int i = 0; i < APT; ++i) {
+                const int c = tid + kThreads * i;
+                *reinterpret_cast<uint4*>(buf + (c / kRowChunks) * kLdsRow + (c % kRowChunks) * 16) = a_reg[i];
+            }
+            uint4 cur_code[NS][CW];
+            uint32_t cur_scale[NS];
 #pragma unroll
             for (int ns = 0; ns < NS; ++ns) {
-                sc[ns][0] = e4m3_byte_to_f32<0>(cur_scale[ns]);
-                sc[ns][1] = e4m3_byte_to_f32<1>(cur_scale[ns]);
-            }
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+                for (int w = 0; w < CW; ++w) cur_code[ns][w] = b_code[ns][w];
+                cur_scale[ns] = b_scale[ns];
+            }
+            __syncthreads();
+            if (st + 1 < nst) load_stage(st + 1);
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
                 bf16x8 bfrag[NS];
 #pragma unroll
                 for (int ns = 0; ns < NS; ++ns) {
-                    const uint32_t w = s == 0 ? cur_code[ns].x : s == 1 ? cur_code[ns].y : s == 2 ? cur_code[ns].z : cur_code[ns].w;
-                    bfrag[ns] = decode8(w, sc[ns][s >> 1]);
+                    const uint4 cw4 = cur_code[ns][s >> 2];
+                    const int sw = s & 3;
+                    const uint32_t word = sw == 0 ? cw4.x : sw == 1 ? cw4.y : sw == 2 ? cw4.z : cw4.w;
+                    // the group of k-step s: byte s / 2 of the lane's scale word
+                    const int sb = s >> 1;
+                    const float sc = sb == 0 ? e4m3_byte_to_f32<0>(cur_scale[ns])
+                                   : sb == 1 ? e4m3_byte_to_f32<1>(cur_scale[ns])
+                                   : sb == 2 ? e4m3_byte_to_f32<2>(cur_scale[ns])
+                                             : e4m3_byte_to_f32<3>(cur_scale[ns]);
+                    bfrag[ns] = decode8(word, sc);
                 }
 #pragma unroll
                 for (int ms = 0; ms < MS; ++ms) {
-                    const bf16x8 afrag = *reinterpret_cast<const bf16x8*>(buf + (ms * 16 + lcol) * kLdsRow + kq * 64 + s * 16);
+                    const bf16x8 afrag =
+                        *reinterpret_cast<const bf16x8*>(buf + (ms * 16 + lcol) * kLdsRow + kq * 64 * CW + s * 16);
 #pragma unroll
                     for (int ns = 0; ns < NS; ++ns)
                         acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[ns], acc[ms][ns], 0, 0, 0);
@@ -302,15 +343,17 @@ int persistent_grid(int64_t tiles_ub, int per_cu = 2) {
     return (int)std::max<int64_t>(g, 1);
 }
 
-template <bool GATEUP, int BM>
-moe_status launch_gemm(const GemmParams& P, int64_t slots, int E, hipStream_t s) {
+template <bool GATEUP, int BM, int BK, int NW>
+moe_status launch_gemm(GemmParams P, int64_t slots, int E, hipStream_t s) {
+    constexpr int BN = (GATEUP ? 32 : 64) * NW;
+    P.ntn = P.N / BN;
     const int64_t tiles_ub = (slots / BM + std::min<int64_t>(E, slots)) * P.ntn;
-    const size_t shmem = 2 * BM * kLdsRow;
-    if (allow_dynamic_lds(reinterpret_cast<const void*>(&k_grouped_gemm<GATEUP, BM>), shmem) != MOE_OK)
-        return MOE_ERR_HIP;
+    const size_t shmem = 2 * BM * (BK * 2 + 16);
+    auto kern = &k_grouped_gemm<GATEUP, BM, BK, NW>;
+    if (allow_dynamic_lds(reinterpret_cast<const void*>(kern), shmem) != MOE_OK) return MOE_ERR_HIP;
     const char* name = GATEUP ? "gemm_gateup" : "gemm_down";
-    MOE_LAUNCH(name, (k_grouped_gemm<GATEUP, BM>), dim3(persistent_grid(tiles_ub, gemm_wg_per_cu<BM>())),
-               dim3(kGThreads), shmem, s, P);
+    MOE_LAUNCH(name, (k_grouped_gemm<GATEUP, BM, BK, NW>), dim3(persistent_grid(tiles_ub, gemm_wg_per_cu<BM, NW>())),
+               dim3(NW * kWave), shmem, s, P);
     return MOE_OK;
 }
 
@@ -318,13 +361,22 @@ moe_status launch_gemm(const GemmParams& P, int64_t slots, int E, hipStream_t s)
 // per row tile, so tiles that hold a whole typical expert pay off even with
 // padding: at 1K tokens, top-8 of 256 (about 32 rows per expert, many with
 // 33-45) 64-row tiles take the layer from 1.61 to 1.32 ms against 32-row
-// tiles; 128-row tiles (one workgroup per CU) take 2.38 ms.
+// tiles; 128-row tiles (one workgroup per CU) take 2.38 ms.  The gate/up
+// product's 64-row tiles use eight waves (twice the columns per tile, half
+// the re-reads of the gathered activation rows) and 256-wide K stages (whole
+// 128-byte weight lines per stage) where the shape allows.  Measured on
+// MI355X at 1K tokens (gate/up, down): four waves with 128-wide stages 840 /
+// 370 us, eight waves 843 / 438 us, eight waves with 256-wide stages 779 /
+// 406 us -- so gate/up takes the last and down keeps four waves.
 template <bool GATEUP>
 moe_status launch_gemm_bm(const GemmParams& P, int64_t slots, int E, hipStream_t s) {
     const int64_t avg = slots / std::max<int64_t>(1, std::min<int64_t>(E, slots));
-    if (avg <= 16) return launch_gemm<GATEUP, 32>(P, slots, E, s);
-    if (avg <= 64) return launch_gemm<GATEUP, 64>(P, slots, E, s);
-    return launch_gemm<GATEUP, 128>(P, slots, E, s);
+    if (avg <= 16) return launch_gemm<GATEUP, 32, 128, 4>(P, slots, E, s);
+    if (avg <= 64) {
+        if (GATEUP && P.K % 256 == 0 && P.N % 256 == 0) return launch_gemm<true, 64, 256, 8>(P, slots, E, s);
+        return launch_gemm<GATEUP, 64, 128, 4>(P, slots, E, s);
+    }
+    return launch_gemm<GATEUP, 128, 128, 4>(P, slots, E, s);
 }
 
 }  // namespace
@@ -343,7 +395,6 @@ moe_status launch_gateup_grouped(const FwdArgs& a, hipStream_t s) {
     g.counts = a.counts;
     g.offsets = a.offsets;
     g.out = a.h;
-    g.ntn = a.I / 128;
     g.gmul = a.xs;
     g.hf = a.hf;
     return launch_gemm_bm<true>(g, slots, a.E, s);
@@ -362,7 +413,6 @@ moe_status launch_down_grouped(const FwdArgs& a, hipStream_t s) {
     d.counts = a.counts;
     d.offsets = a.offsets;
     d.out = a.y;
-    d.ntn = a.H / 256;
     d.gmul = a.hs;
     d.hf = nullptr;
     return launch_gemm_bm<false>(d, slots, a.E, s);

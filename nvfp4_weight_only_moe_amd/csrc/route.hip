@@ -144,14 +144,13 @@ k_route_tiny(const float* __restrict__ logits, int T, int E, int k, int32_t* __r
              float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
              int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_pos) {
     __shared__ int s_ids[kTinyMaxSlots];
-    __shared__ int s_list[kTinyMaxSlots], s_ucnt[kTinyMaxSlots], s_uoff[kTinyMaxSlots];
-    __shared__ int s_U;
+    __shared__ int s_key[kTinyMaxTokens][MOE_MAX_TOPK], s_idx[kTinyMaxTokens][MOE_MAX_TOPK];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int slots = T * k;
     if (wave < T) {
         int id;
-        float wt;
-        wave_topk_select<EPL>(logits + (int64_t)wave * E, E, k, id, wt);
+        float v;
+        wave_topk_ordered<EPL>(logits + (int64_t)wave * E, E, k, s_key[wave], s_idx[wave], id, v);
+        const float wt = topk_softmax(v, k);
         if (lane < k) {
             ids[wave * k + lane] = id;
             w[wave * k + lane] = wt;
@@ -159,33 +158,7 @@ k_route_tiny(const float* __restrict__ logits, int T, int E, int k, int32_t* __r
         }
     }
     __syncthreads();
-    if (wave == 0) {
-        const bool valid = lane < slots;
-        const int ex = valid ? s_ids[lane] : 0;
-        const SlotOrder o = wave_slot_order(ex, valid, E);
-        if (valid) {
-            sorted_slots[o.pos] = lane;
-            slot_pos[lane] = o.pos;
-        }
-        if (o.first) {
-            s_list[o.u] = ex;
-            s_ucnt[o.u] = __popcll(o.eq);
-            s_uoff[o.u] = o.less;
-        }
-        if (lane == 0) s_U = o.U;
-    }
-    __syncthreads();
-    const int U = s_U;
-    for (int e = threadIdx.x; e <= E; e += blockDim.x) {
-        int lo = 0, hi = U;                  // first touched expert >= e
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (s_list[mid] < e) lo = mid + 1;
-            else hi = mid;
-        }
-        if (e < E) counts[e] = lo < U && s_list[lo] == e ? s_ucnt[lo] : 0;
-        offsets[e] = lo < U ? s_uoff[lo] : slots;
-    }
+    tiny_route_finish(s_ids, T, E, k, counts, offsets, sorted_slots, slot_pos);
 }
 
 // Large T, step 1: top-k per token and a per-workgroup expert histogram.

@@ -124,6 +124,50 @@ __device__ __forceinline__ void wave_topk_set(const float* __restrict__ row, int
     }
 }
 
+// The same selection in wave_topk_ids' order (logit descending, ties to the
+// lower expert): wave_topk_set, then each of the k selected ranks itself
+// against the others through a small per-wave LDS scratch (s_key, s_idx:
+// at least k ints each).  On return lane j < k holds the j-th selection
+// (expert in id_out, logit in v_out), exactly as wave_topk_ids returns it.
+template <int EPL>
+__device__ __forceinline__ void wave_topk_ordered(const float* __restrict__ row, int E, int k, int* s_key,
+                                                  int* s_idx, int& id_out, float& v_out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t key[EPL];
+    uint64_t sel[EPL];
+    wave_topk_set<EPL>(row, E, k, key, sel);
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        if ((sel[i] >> lane) & 1u) {
+            const int c = base + __popcll(sel[i] & lanemask_lt());
+            s_key[c] = (int)key[i];
+            s_idx[c] = kWave * i + lane;
+        }
+        base += __popcll(sel[i]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's LDS writes land before its reads
+    const int j = lane < k ? lane : 0;
+    const uint32_t kj = (uint32_t)s_key[j];
+    const int ij = s_idx[j];
+    int rank = 0;
+#pragma unroll
+    for (int m = 0; m < MOE_MAX_TOPK; ++m) {       // a static loop: the LDS reads issue back to back
+        if (m < k) {
+            const uint32_t km = (uint32_t)s_key[m];
+            rank += (km > kj || (km == kj && s_idx[m] < ij)) ? 1 : 0;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // every read above is done before the slots are rewritten
+    if (lane < k) {
+        s_key[rank] = (int)kj;
+        s_idx[rank] = ij;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    id_out = lane < k ? s_idx[lane] : 0;
+    v_out = lane < k ? topk_key_value((uint32_t)s_key[lane]) : 0.0f;
+}
+
 // Routing weights of a wave_topk_ids selection: softmax over the k selected
 // logits (lane j < k holds the j-th), computed from the largest.
 __device__ __forceinline__ float topk_softmax(float my_v, int k) {
@@ -193,6 +237,48 @@ __device__ __forceinline__ int wave_rank_equal(int e, bool valid, int nbits, int
     }
     if (total) *total = __popcll(match);
     return __popcll(match & lanemask_lt());
+}
+
+// After the top-k of a few tokens (their ids in s_ids, LDS, all T * k slots):
+// one wave orders the slots by ballots on the expert bits (wave_slot_order:
+// the order of the counting sort) and stores sorted_slots and slot_pos, then
+// every thread fills the counts and offsets of its experts by a binary
+// search over the touched experts (ascending).  Called by a whole
+// workgroup; contains barriers.
+__device__ inline void tiny_route_finish(const int* s_ids, int T, int E, int k, int32_t* __restrict__ counts,
+                                  int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots,
+                                  int32_t* __restrict__ slot_pos) {
+    __shared__ int s_list[64], s_ucnt[64], s_uoff[64];
+    __shared__ int s_U;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int slots = T * k;
+    if (wave == 0) {
+        const bool valid = lane < slots;
+        const int ex = valid ? s_ids[lane] : 0;
+        const SlotOrder o = wave_slot_order(ex, valid, E);
+        if (valid) {
+            sorted_slots[o.pos] = lane;
+            slot_pos[lane] = o.pos;
+        }
+        if (o.first) {
+            s_list[o.u] = ex;
+            s_ucnt[o.u] = __popcll(o.eq);
+            s_uoff[o.u] = o.less;
+        }
+        if (lane == 0) s_U = o.U;
+    }
+    __syncthreads();
+    const int U = s_U;
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+        int lo = 0, hi = U;                  // first touched expert >= e
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (s_list[mid] < e) lo = mid + 1;
+            else hi = mid;
+        }
+        if (e < E) counts[e] = lo < U && s_list[lo] == e ? s_ucnt[lo] : 0;
+        offsets[e] = lo < U ? s_uoff[lo] : slots;
+    }
 }
 
 }  // namespace moe

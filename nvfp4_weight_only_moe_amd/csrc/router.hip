@@ -17,13 +17,23 @@
 //    adds them in wave order.  Splitting K rather than the tile keeps many
 //    small waves in flight to cover the load latency of each stage.
 // Both are deterministic: fixed summation order, no atomics.
+//
+// k_router_route (decode token counts): the GEMV and the route in one launch.
+// Every workgroup stores its expert's logits at device scope and, once the
+// stores are done, takes a ticket (one device-scope vector atomic); the
+// workgroup that takes the last ticket reads every logit and routes there --
+// top-k per token by a threshold search, the slot order by ballots, counts
+// and offsets -- exactly as moe_route_topk would, then puts the ticket word
+// back to zero for the next call.
 #include "device_common.h"
 #include "internal.h"
+#include "route_common.h"
 
 namespace moe {
 namespace {
 
 constexpr int kRgThreads = 128;     // GEMV: two waves per expert row
+constexpr int kRrThreads = 512;     // GEMV + route: eight waves, one token per wave in the routing workgroup
 constexpr int kRgBatch = 5;         // 16-byte chunks per lane per batch (one batch at H 5120)
 constexpr int kRmThreads = 256;     // MFMA: four waves
 constexpr int kRmSmallT = 4096;     // up to here 32-token tiles, above 64
@@ -38,21 +48,21 @@ __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
     return dot2_bf16(a.w, b.w, acc);
 }
 
-// NT = the token count exactly (one instance per count): no branch stands
-// between the loads, so every weight and x chunk of a batch is requested
-// before the first dot product waits.  Lanes past the row's end re-read its
-// last chunk and drop the result (a select, not a branch).
-template <int NT>
-__global__ void __launch_bounds__(kRgThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) k_router_gemv(const uint16_t* x, const uint16_t* w, int H, int E,
-                                                            float* __restrict__ logits) {
+// One workgroup's expert row e: the NT logits x[t] . W[e] into logits[t][e]
+// (COHERENT: stored at device scope, through to the level every CU reads,
+// for a workgroup of the same launch to read them).  Waves 0 .. NWV - 1 take
+// equal parts of the row (the split fixes the summation order); further
+// waves of a larger workgroup only meet the barrier.
+template <int NT, bool COHERENT = false, int NWV = 2>
+__device__ __forceinline__ void router_gemv_row(const uint16_t* x, const uint16_t* w, int H, int E, int e,
+                                                float* __restrict__ logits) {
     // (x and w without __restrict__: their loads would count as invariant
     // and could sink past the issue point below)
-    __shared__ float s_part[2][NT];
-    const int e = blockIdx.x;
+    __shared__ float s_part[NWV][NT];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int nch = H / 8;                          // 16-byte chunks per row
-    const int half = (nch + 1) / 2;
-    const int c0 = wave * half, c1 = min(nch, c0 + half);
+    const int part = (nch + NWV - 1) / NWV;          // chunks per wave
+    const int c0 = wave < NWV ? min(nch, wave * part) : nch, c1 = min(nch, c0 + part);
     const uint4* wr = reinterpret_cast<const uint4*>(w + (int64_t)e * H);
 
     float acc[NT];
@@ -85,10 +95,77 @@ __global__ void __launch_bounds__(kRgThreads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const float v = wave_sum_dpp(acc[t]);
-        if (lane == 0) s_part[wave][t] = v;
+        if (lane == 0 && wave < NWV) s_part[wave][t] = v;
     }
     __syncthreads();
-    if ((int)threadIdx.x < NT) logits[(int64_t)threadIdx.x * E + e] = s_part[0][threadIdx.x] + s_part[1][threadIdx.x];
+    if ((int)threadIdx.x < NT) {
+        float v = s_part[0][threadIdx.x];
+#pragma unroll
+        for (int i = 1; i < NWV; ++i) v += s_part[i][threadIdx.x];
+        float* dst = logits + (int64_t)threadIdx.x * E + e;
+        if constexpr (COHERENT) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else *dst = v;
+    }
+}
+
+// NT = the token count exactly (one instance per count): no branch stands
+// between the loads, so every weight and x chunk of a batch is requested
+// before the first dot product waits.  Lanes past the row's end re-read its
+// last chunk and drop the result (a select, not a branch).
+template <int NT>
+__global__ void __launch_bounds__(kRgThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) k_router_gemv(const uint16_t* x, const uint16_t* w, int H, int E,
+                                                            float* __restrict__ logits) {
+    router_gemv_row<NT>(x, w, H, E, blockIdx.x, logits);
+}
+
+struct RouteOut {
+    int32_t* ids;
+    float* w;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* sorted_slots;
+    int32_t* slot_pos;
+};
+
+// The hand-off needs no cache-wide flush: the logits are stored and read at
+// device scope (coherent across the XCDs' L2s), a workgroup takes its ticket
+// only after its stores have completed, and the last workgroup copies the
+// logits into LDS with device-scope loads before routing from there.
+template <int NT, int EPL>
+__global__ void __launch_bounds__(kRrThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
+k_router_route(const uint16_t* x, const uint16_t* w, int H, int E, int k, float* logits, uint32_t* ticket,
+               const RouteOut R) {
+    __shared__ int s_last;
+    __shared__ int s_ids[64];
+    __shared__ int s_key[kRrThreads / kWave][MOE_MAX_TOPK], s_idx[kRrThreads / kWave][MOE_MAX_TOPK];
+    __shared__ float s_logits[NT * 64 * EPL];
+    router_gemv_row<NT, true, 2>(x, w, H, E, blockIdx.x, logits);   // the GEMV's own split: the same logit bits
+    __syncthreads();                                    // waits for this workgroup's stores to complete
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = old == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // every other workgroup stored its logits before taking its ticket
+    for (int i = threadIdx.x; i < NT * E; i += kRrThreads)
+        s_logits[i] = __hip_atomic_load(logits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    for (int t = wave; t < NT; t += kRrThreads / kWave) {
+        int id;
+        float v;
+        wave_topk_ordered<EPL>(s_logits + t * E, E, k, s_key[wave], s_idx[wave], id, v);
+        const float wt = topk_softmax(v, k);
+        if (lane < k) {
+            R.ids[t * k + lane] = id;
+            R.w[t * k + lane] = wt;
+            s_ids[t * k + lane] = id;
+        }
+    }
+    __syncthreads();
+    tiny_route_finish(s_ids, NT, E, k, R.counts, R.offsets, R.sorted_slots, R.slot_pos);
+    if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int ROWS>
@@ -179,7 +256,47 @@ moe_status launch_gemv(const uint16_t* x, int H, const uint16_t* w, int E, float
     return MOE_OK;
 }
 
+template <int NT, int EPL>
+moe_status launch_router_route_t(const uint16_t* x, int H, const uint16_t* w, int E, int k, float* logits,
+                                 uint32_t* ticket, const RouteOut& R, hipStream_t s) {
+    MOE_LAUNCH("router_route", (k_router_route<NT, EPL>), dim3(E), dim3(kRrThreads), 0, s, x, w, H, E, k, logits,
+               ticket, R);
+    return MOE_OK;
+}
+
+template <int NT>
+moe_status launch_router_route_n(const uint16_t* x, int H, const uint16_t* w, int E, int k, float* logits,
+                                 uint32_t* ticket, const RouteOut& R, hipStream_t s) {
+    if (E <= 64) return launch_router_route_t<NT, 1>(x, H, w, E, k, logits, ticket, R, s);
+    if (E <= 128) return launch_router_route_t<NT, 2>(x, H, w, E, k, logits, ticket, R, s);
+    if (E <= 256) return launch_router_route_t<NT, 4>(x, H, w, E, k, logits, ticket, R, s);
+    if (E <= 512) return launch_router_route_t<NT, 8>(x, H, w, E, k, logits, ticket, R, s);
+    return launch_router_route_t<NT, 16>(x, H, w, E, k, logits, ticket, R, s);
+}
+
 }  // namespace
+
+bool router_route_fused_supported(int T, int H, int E, int k) {
+    return T >= 1 && T <= 8 && T * k <= 64 && k <= MOE_MAX_TOPK && E >= 1 && E <= MOE_MAX_EXPERTS &&
+           router_shape_supported(T, H, E);
+}
+
+moe_status launch_router_route(const uint16_t* x, int T, int H, const uint16_t* w, int E, int k, float* logits,
+                               uint32_t* ticket, int32_t* ids, float* wts, int32_t* counts, int32_t* offsets,
+                               int32_t* sorted_slots, int32_t* slot_pos, hipStream_t s) {
+    if (!router_route_fused_supported(T, H, E, k)) return MOE_ERR_UNSUPPORTED;
+    const RouteOut R{ids, wts, counts, offsets, sorted_slots, slot_pos};
+    switch (T) {
+        case 1: return launch_router_route_n<1>(x, H, w, E, k, logits, ticket, R, s);
+        case 2: return launch_router_route_n<2>(x, H, w, E, k, logits, ticket, R, s);
+        case 3: return launch_router_route_n<3>(x, H, w, E, k, logits, ticket, R, s);
+        case 4: return launch_router_route_n<4>(x, H, w, E, k, logits, ticket, R, s);
+        case 5: return launch_router_route_n<5>(x, H, w, E, k, logits, ticket, R, s);
+        case 6: return launch_router_route_n<6>(x, H, w, E, k, logits, ticket, R, s);
+        case 7: return launch_router_route_n<7>(x, H, w, E, k, logits, ticket, R, s);
+        default: return launch_router_route_n<8>(x, H, w, E, k, logits, ticket, R, s);
+    }
+}
 
 bool router_shape_supported(int T, int H, int E) { return T >= 0 && E >= 1 && H >= kRmK && H % kRmK == 0; }
 

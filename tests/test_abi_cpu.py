@@ -255,3 +255,21 @@ def test_quantize_activations_argument_errors(L):
     assert q(0, 4, 64, f(1.0), A + 0x100000, A + 0x200000, None) == -1
     assert q(A, 4, 64, f(1.0), A + 4, A + 0x200000, None) == -3
     assert q(A, 4, 64, f(1.0), A + 0x40, A + 0x200000, None) == -1          # codes overlap x
+
+
+def test_router_route_argument_errors(L):
+    def rr(x=A, T=4, H=1024, wr=A + 0x100000, E=256, k=8, lg=A + 0x800000, ptr=A + 0x900000, ws=A + 0xA00000,
+           ws_bytes=1 << 20):
+        return L.moe_router_route_topk(x, T, H, wr, E, k, lg, ptr, ptr, ptr, ptr, ptr, ptr, ws, ws_bytes, None)
+    assert rr(T=0) == b.MOE_OK
+    assert rr(T=-1) == -2
+    assert rr(H=100) == -2
+    assert rr(k=9, E=8) == -4
+    assert rr(k=33) == -4
+    assert rr(x=0) == -1
+    assert rr(lg=A + 0x800004) == -3
+    assert rr(ws=0) == -7
+    assert rr(ws_bytes=8) == -7
+    assert rr(lg=A + 0x100) == -1                                   # logits overlap x
+    assert L.moe_router_route_workspace_size(8, 256, 8) >= 4
+    assert L.moe_router_route_workspace_size(100000, 256, 8) > L.moe_route_workspace_size(100000, 256, 8)

@@ -134,3 +134,84 @@ def test_router_and_layer_in_one_graph(T):
         assert torch.equal(lg, ref_lg), f"replay {i}: logits"
         assert torch.equal(out, ref_out), f"replay {i}: output"
     log(f"router + route_forward graph T={T}: 3 replays bit-identical")
+
+
+# ------------------------------------------------------------------ router + route in one call
+ROUTER_ROUTE_CASES = [
+    # decode token counts: one launch (every workgroup a ticket, the last one routes)
+    (1, 5120, 256, 8), (2, 1024, 64, 4), (8, 5120, 256, 8), (4, 2048, 300, 16), (8, 1024, 1024, 8),
+    (1, 128, 7, 7), (3, 512, 33, 32),
+    # other shapes: the router kernels, then the route kernels
+    (9, 1024, 256, 8), (100, 512, 64, 4),
+]
+
+
+@pytest.mark.parametrize("T,H,E,k", ROUTER_ROUTE_CASES)
+def test_router_route_equals_router_then_route(T, H, E, k):
+    """moe_router_route_topk gives the logits of moe_router_logits and the
+    routing of moe_route_topk on them, bit for bit; the ids also match the
+    oracle's routing of those logits; repeated calls on one workspace keep
+    working (the ticket word is left at zero); guard bands stay intact."""
+    from gpu_util import Guarded, check_guards, guarded_routing
+    xb, _, wb, _ = wls.router_problem(700 + T + E, T, H, E)
+    xd, wd = to_dev(xb, torch.int16), to_dev(wb, torch.int16)
+    lg_ref = B.moe_router_logits(xd, wd)
+    r_ref = B.moe_route_topk(lg_ref, k)
+    torch.cuda.synchronize()
+    ws = Guarded((B.lib().moe_router_route_workspace_size(T, E, k),), torch.uint8)
+    ws.t.zero_()
+    for rep in range(3):
+        r, parts = guarded_routing(T, E, k)
+        parts["logits"] = Guarded((T, E), torch.float32)
+        B.moe_router_route_topk(xd, wd, k, logits=parts["logits"].t, routing=r, ws=ws.t)
+        torch.cuda.synchronize()
+        check_guards(parts, f"router_route T{T} E{E} k{k} call {rep}")
+        ws.check(f"router_route workspace call {rep}")
+        assert int(ws.t[:4].view(torch.int32)[0]) == 0, "ticket word not left at zero"
+        assert torch.equal(parts["logits"].t, lg_ref)
+        for name in ("topk_ids", "topk_w", "counts", "offsets", "sorted_slots", "slot_pos"):
+            assert torch.equal(getattr(r, name), getattr(r_ref, name)), (rep, name)
+    ids, w = oracle.route_topk(lg_ref.cpu().numpy(), k)
+    assert np.array_equal(r.topk_ids.cpu().numpy(), ids)
+    assert float(np.max(np.abs(r.topk_w.cpu().numpy() - w))) <= 1e-6
+    log(f"router_route T={T} H={H} E={E} k={k}: identical to router + route_topk")
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_router_route_and_layer_in_one_graph(T):
+    """moe_router_route_topk then moe_w4a16_forward captured in one HIP graph:
+    every replay reproduces the eager output and routing bit for bit."""
+    H, I, E, k = 1024, 512, 32, 4
+    _, ms, _, _, _ = wls.random_problem(80 + T, T, H, I, E, k)
+    xb, _, wb, _ = wls.router_problem(90 + T, T, H, E)
+    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in ms)
+    xd, wd = to_dev(xb, torch.int16), to_dev(wb, torch.int16)
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda:0")
+    route = B.Routing.empty(T, E, k, "cuda:0")
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda:0")
+    ws = B.forward_workspace(T, H, I, E, k, "cuda:0")
+    rws = B.router_route_workspace(T, E, k, "cuda:0")
+
+    def step():
+        B.moe_router_route_topk(xd, wd, k, logits=lg, routing=route, ws=rws)
+        B.moe_w4a16_forward(xd, gate, up, down, route, out=out, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_ids = out.clone(), route.topk_ids.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        out.fill_(i + 1)
+        route.topk_ids.fill_(-1)
+        B.moe_router_logits(wd[:1].contiguous(), wd)             # unrelated eager work
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"replay {i}: output"
+        assert torch.equal(route.topk_ids, ref_ids), f"replay {i}: ids"
