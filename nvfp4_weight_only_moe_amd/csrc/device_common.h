@@ -51,7 +51,8 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) { return e4m3_byte_to_f
 // fp32 pair -> bf16 pair by truncation.  Only used on values that are exact
 // in bf16 (E2M1 * E4M3 products), where truncation is exact.
 __device__ __forceinline__ uint32_t pack_bf16x2_exact(float lo, float hi) {
-    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+    // one v_perm_b32: bytes 2, 3 of lo, then bytes 2, 3 of hi
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).

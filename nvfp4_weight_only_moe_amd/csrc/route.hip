@@ -12,7 +12,7 @@
 // deterministic.
 //
 //   decode T (T * k <= 64, T <= 16; one workgroup):  k_route_tiny   (1 launch)
-//   small T (one workgroup):  k_route_small                 (1 launch)
+//   small T (T <= 64, one workgroup):  k_route_small       (1 launch)
 //   large T:  k_route_topk_hist -> k_route_colscan -> k_route_scatter
 #include <float.h>
 #include <limits.h>
@@ -26,8 +26,14 @@ namespace {
 
 constexpr int kRT = 256;                 // threads per route workgroup
 constexpr int kRW = kRT / kWave;         // waves per route workgroup
-constexpr int kTokensPerBlock = 64;      // large-T path
-constexpr int kSmallMaxSlots = kTokensPerBlock * MOE_MAX_TOPK;  // small path: T <= 64
+constexpr int kSmallMaxTokens = 64;      // one-workgroup path: T <= 64
+constexpr int kSmallMaxSlots = kSmallMaxTokens * MOE_MAX_TOPK;
+// Large-T path: a workgroup of 16 waves selects the top-k of 16 tokens, one
+// token per wave, so the logits loads of a launch are all in flight at once
+// (with 64 tokens per 4-wave workgroup each wave loaded and routed 16 tokens
+// one after the other: 41 us at 1K tokens on MI355X).
+constexpr int kTokensPerBlock = 16;
+constexpr int kHistThreads = kTokensPerBlock * kWave;
 
 // One wave: top-k of one token's E logits (wave_topk_select) written to
 // ids/weights, and to LDS when ids_lds is given.
@@ -110,7 +116,7 @@ __device__ void block_scatter(const int32_t* ids, int f0, int f1, const int* bas
     }
 }
 
-// Whole route in one workgroup (T <= kTokensPerBlock).
+// Whole route in one workgroup (T <= kSmallMaxTokens).
 __global__ void __launch_bounds__(kRT) k_route_small(const float* __restrict__ logits, int T, int E, int k,
                                                      int32_t* __restrict__ ids, float* __restrict__ w,
                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -161,20 +167,33 @@ k_route_tiny(const float* __restrict__ logits, int T, int E, int k, int32_t* __r
     tiny_route_finish(s_ids, T, E, k, counts, offsets, sorted_slots, slot_pos);
 }
 
-// Large T, step 1: top-k per token and a per-workgroup expert histogram.
-__global__ void __launch_bounds__(kRT) k_route_topk_hist(const float* __restrict__ logits, int T, int E, int k,
-                                                         int32_t* __restrict__ ids, float* __restrict__ w,
-                                                         int32_t* __restrict__ block_hist /* [B][E] */) {
-    __shared__ int32_t s_ids[kTokensPerBlock * MOE_MAX_TOPK];
+// Large T, step 1: top-k per token (one wave each: wave_topk_ordered, the
+// threshold selection ranked in wave_topk_ids' order) and a per-workgroup
+// expert histogram.
+template <int EPL>
+__global__ void __launch_bounds__(kHistThreads) k_route_topk_hist(const float* __restrict__ logits, int T, int E,
+                                                                  int k, int32_t* __restrict__ ids,
+                                                                  float* __restrict__ w,
+                                                                  int32_t* __restrict__ block_hist /* [B][E] */) {
+    __shared__ int s_key[kTokensPerBlock][MOE_MAX_TOPK], s_idx[kTokensPerBlock][MOE_MAX_TOPK];
     __shared__ int s_cnt[MOE_MAX_EXPERTS];
-    const int t0 = blockIdx.x * kTokensPerBlock;
-    const int t1 = min(T, t0 + kTokensPerBlock);
-    topk_tokens_any(logits, t0, t1, E, k, ids, w, s_ids);
-    for (int e = threadIdx.x; e < E; e += kRT) s_cnt[e] = 0;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int t = blockIdx.x * kTokensPerBlock + wave;
+    for (int e = threadIdx.x; e < E; e += kHistThreads) s_cnt[e] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < (t1 - t0) * k; i += kRT) atomicAdd(&s_cnt[s_ids[i]], 1);
+    if (t < T) {
+        int id;
+        float v;
+        wave_topk_ordered<EPL>(logits + (int64_t)t * E, E, k, s_key[wave], s_idx[wave], id, v);
+        const float wt = topk_softmax(v, k);
+        if (lane < k) {
+            ids[(int64_t)t * k + lane] = id;
+            w[(int64_t)t * k + lane] = wt;
+            atomicAdd(&s_cnt[id], 1);
+        }
+    }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += kRT) block_hist[(int64_t)blockIdx.x * E + e] = s_cnt[e];
+    for (int e = threadIdx.x; e < E; e += kHistThreads) block_hist[(int64_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
 // Large T, step 2: one wave per expert column: exclusive prefix over the
@@ -246,7 +265,7 @@ __global__ void __launch_bounds__(256) k_route_identity(int T, int32_t* __restri
 
 size_t route_workspace_bytes(int T, int E, int k) {
     (void)k;
-    if (T <= kTokensPerBlock) return 0;
+    if (T <= kSmallMaxTokens) return 0;
     const int64_t B = (T + kTokensPerBlock - 1) / kTokensPerBlock;
     return (size_t)(B * E * sizeof(int32_t));
 }
@@ -274,14 +293,19 @@ moe_status launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
                         sorted_slots, slot_pos);
         return MOE_OK;
     }
-    if (T <= kTokensPerBlock) {
+    if (T <= kSmallMaxTokens) {
         MOE_LAUNCH("route_small", k_route_small, dim3(1), dim3(kRT), 0, s, logits, T, E, k, ids, w, counts,
                    offsets, sorted_slots, slot_pos);
         return MOE_OK;
     }
     const int B = (T + kTokensPerBlock - 1) / kTokensPerBlock;
     int32_t* hist = reinterpret_cast<int32_t*>(ws);
-    MOE_LAUNCH("route_topk_hist", k_route_topk_hist, dim3(B), dim3(kRT), 0, s, logits, T, E, k, ids, w, hist);
+    const dim3 hg(B), hb(kHistThreads);
+    if (E <= 64) MOE_LAUNCH("route_topk_hist", k_route_topk_hist<1>, hg, hb, 0, s, logits, T, E, k, ids, w, hist);
+    else if (E <= 128) MOE_LAUNCH("route_topk_hist", k_route_topk_hist<2>, hg, hb, 0, s, logits, T, E, k, ids, w, hist);
+    else if (E <= 256) MOE_LAUNCH("route_topk_hist", k_route_topk_hist<4>, hg, hb, 0, s, logits, T, E, k, ids, w, hist);
+    else if (E <= 512) MOE_LAUNCH("route_topk_hist", k_route_topk_hist<8>, hg, hb, 0, s, logits, T, E, k, ids, w, hist);
+    else MOE_LAUNCH("route_topk_hist", k_route_topk_hist<16>, hg, hb, 0, s, logits, T, E, k, ids, w, hist);
     MOE_LAUNCH("route_colscan", k_route_colscan, dim3((E + kRW - 1) / kRW), dim3(kRT), 0, s, hist, B, E, counts);
     MOE_LAUNCH("route_scatter", k_route_scatter, dim3(B), dim3(kRT), 0, s, (const int32_t*)ids, T, E, k,
                (const int32_t*)counts, (const int32_t*)hist, offsets, sorted_slots, slot_pos);
