@@ -87,24 +87,9 @@ def packed_bytes(N, K):
     return N * K // 2 + N * K // 16 + 4
 
 
-# Sources that determine each kernel's memory traffic; the counters stored in
-# profiles/traffic.json are only reported while these files are unchanged.
-KERNEL_SOURCES = {
-    "dec_gateup": ["moe_decode.hip", "device_common.h", "route_common.h"],
-    "dec_gateup_route": ["moe_decode.hip", "device_common.h", "route_common.h"],
-    "dec_down": ["moe_decode.hip", "device_common.h", "route_common.h"],
-    "gemm_gateup": ["moe_prefill.hip", "moe_prefill_pipe.hip", "device_common.h"],
-    "gemm_down": ["moe_prefill.hip", "moe_prefill_pipe.hip", "device_common.h"],
-}
-
-
 def kernel_source_hash(kernel):
-    import hashlib
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES.get(kernel, []):
-        with open(os.path.join(ROOT, "nvfp4_weight_only_moe_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
+    from nvfp4_weight_only_moe_amd import pmc
+    return pmc.kernel_source_hash(kernel)
 
 
 def measured_traffic(kernel, workload):

@@ -197,26 +197,39 @@ __global__ void __launch_bounds__(kHistThreads) k_route_topk_hist(const float* _
 }
 
 // Large T, step 2: one wave per expert column: exclusive prefix over the
-// workgroups (in place) and the expert's total count.
+// workgroups (in place) and the expert's total count.  Lane l owns the
+// contiguous run of workgroups [l * per, (l + 1) * per): its loads are
+// independent of each other (all in flight at once), one DPP scan combines
+// the lane sums, and a second pass over the run (L2 hits) writes it.
 __global__ void __launch_bounds__(kRT) k_route_colscan(int32_t* __restrict__ block_hist, int B, int E,
                                                        int32_t* __restrict__ counts) {
     const int lane = threadIdx.x & (kWave - 1);
     const int e = blockIdx.x * kRW + threadIdx.x / kWave;
     if (e >= E) return;
-    int run = 0;
-    for (int b0 = 0; b0 < B; b0 += kWave) {
-        const int b = b0 + lane;
-        const int v = b < B ? block_hist[(int64_t)b * E + e] : 0;
-        int incl = v;
+    constexpr int kBatch = 16;                 // loads issued together
+    const int per = (B + kWave - 1) / kWave;
+    const int b0 = lane * per, b1 = min(B, b0 + per);
+    int local = 0;
+    for (int c = b0; c < b1; c += kBatch) {
+        int v[kBatch];
 #pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int t = __shfl_up(incl, o, kWave);
-            if (lane >= o) incl += t;
-        }
-        if (b < B) block_hist[(int64_t)b * E + e] = run + incl - v;
-        run += __shfl(incl, kWave - 1, kWave);
+        for (int i = 0; i < kBatch; ++i) v[i] = c + i < b1 ? block_hist[(int64_t)(c + i) * E + e] : 0;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) local += v[i];
     }
-    if (lane == 0) counts[e] = run;
+    const int incl = wave_inclusive_scan_dpp(local);
+    int run = incl - local;
+    for (int c = b0; c < b1; c += kBatch) {
+        int v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) v[i] = c + i < b1 ? block_hist[(int64_t)(c + i) * E + e] : 0;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            if (c + i < b1) block_hist[(int64_t)(c + i) * E + e] = run;
+            run += v[i];
+        }
+    }
+    if (lane == kWave - 1) counts[e] = incl;
 }
 
 // Large T, step 3: offsets (every workgroup recomputes them; workgroup 0
