@@ -329,8 +329,13 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
         int ex = 0;
         float wv = valid ? 1.0f : 0.0f;
         if constexpr (!ONE) {
-            ex = valid ? ids[lane] : 0;
-            wv = valid ? topk_w[lane] : 0.0f;
+            // both loads issued together (clamped index, no branch around
+            // either): one memory round trip before the slot order
+            const int j = lane < slots ? lane : 0;
+            const int ex_ = ids[j];
+            const float wv_ = topk_w[j];
+            ex = valid ? ex_ : 0;
+            wv = valid ? wv_ : 0.0f;
         }
         ex = min(max(ex, 0), E - 1);     // keeps every weight address inside the stacks
         const SlotOrder o = wave_slot_order(ex, valid, E);
@@ -400,8 +405,6 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
     const int sh_pair = 16 * (l32 & 1), sh_single = 8 * (l32 & 3);
     const int64_t code_stride = (int64_t)H * (I / 2), scale_stride = (int64_t)H * ngroups;
 
-    // every touched expert's global scale in one vector load (lane u: expert u)
-    const float gvv = dg[s_list[min(lane, s_U - 1)]] * h_scale;
 
     float acc[MAXT][R];
 #pragma unroll
@@ -440,9 +443,14 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
         uint4 cw[kDownChunkExperts][R][NP > 0 ? NP : 1];
         uint2 cs[kDownChunkExperts][R];
         uint32_t sw[kDownChunkExperts][R];
+        // each expert's global scale by a scalar load issued with its codes: a
+        // vector load would sit in the same in-order queue as the weight and
+        // h loads, and waiting for it would wait for them
+        float gsc[kDownChunkExperts];
 #define MOE_DOWN_LOAD(u)                                                                        \
         do {                                                                                    \
             const int e_ = __builtin_amdgcn_readfirstlane(s_list[min(u0 + (u), u1 - 1)]);       \
+            gsc[u] = ((const __attribute__((address_space(4))) float*)dg)[e_];                   \
             const uint8_t* cb_ = dc + e_ * code_stride;                                         \
             const uint8_t* sb_ = ds + e_ * scale_stride;                                        \
             _Pragma("unroll") for (int r = 0; r < R; ++r) {                                     \
@@ -464,8 +472,7 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
         for (int u = 0; u < kDownChunkExperts; ++u) {
             if (u + kDownAhead < kDownChunkExperts) MOE_DOWN_LOAD(u + kDownAhead);
             if (u0 + u < u1) {
-                const float ge = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gvv), u0 + u));
+                const float ge = gsc[u] * h_scale;
                 const int q0 = s_uoff[u0 + u] - pA;
                 float sp0[R][NP > 0 ? NP : 1], sp1[R][NP > 0 ? NP : 1], s1[R];
 #pragma unroll

@@ -37,10 +37,13 @@ __device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int
                                               float& v_out) {
     const int lane = threadIdx.x & (kWave - 1);
     uint64_t kk[EPL];
+    float xs[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) xs[i] = row[min(lane + kWave * i, E - 1)];   // all loads before any use
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int idx = lane + kWave * i;
-        const float x = idx < E ? row[idx] + 0.0f : -INFINITY;
+        const float x = idx < E ? xs[i] + 0.0f : -INFINITY;
         kk[i] = ((uint64_t)topk_key(x != x ? -INFINITY : x) << 32) | (uint32_t)~idx;
     }
 #pragma unroll
@@ -95,10 +98,15 @@ template <int EPL>
 __device__ __forceinline__ void wave_topk_set(const float* __restrict__ row, int E, int k, uint32_t (&key)[EPL],
                                               uint64_t (&sel)[EPL]) {
     const int lane = threadIdx.x & (kWave - 1);
+    // every lane loads all its logits before any is used (clamped indices,
+    // no branch around a load), so the EPL loads take one memory round trip
+    float xs[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) xs[i] = row[min(lane + kWave * i, E - 1)];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int idx = lane + kWave * i;
-        const float x = idx < E ? row[idx] + 0.0f : 0.0f;
+        const float x = xs[i] + 0.0f;
         key[i] = idx < E ? topk_key(x != x ? -INFINITY : x) : 0u;
     }
     uint32_t P = 0u;                                   // count(key >= P) >= k throughout
