@@ -353,6 +353,21 @@ def bench_moe_config(args, cfg, base, cache):
     }
     work_bytes, work_flops = kernel_work.get(dominant, (alg_bytes_step, None))
     roofline = make_roofline(dominant, dom_us, work_bytes, work_flops, measured_traffic(dominant, wl.name))
+    if decode and not args.no_peaks and args.router == "none":
+        # what a kernel that only reads reaches on the same byte counts: the
+        # two decode kernels' bytes, each alone (event-timed like the
+        # kernels) and back to back (graph-replayed like the steps)
+        gu_key = "dec_gateup_route" if "dec_gateup_route" in prof else "dec_gateup"
+        ref = stream_reference([kernel_work[gu_key][0], kernel_work["dec_down"][0]], copies)
+        dom_ref = ref["kernel_us"][0] if dominant == gu_key else ref["kernel_us"][1] if dominant == "dec_down" else None
+        roofline["achievable"] = {
+            "what": "plain streaming read of the same bytes (moe_bench_stream_read)",
+            "kernel_bytes": ref["bytes"], "kernel_us": ref["kernel_us"],
+            "dominant_kernel_frac": round(dom_ref / dom_us, 4) if dom_ref else None,
+            "step_pair_us": ref["pair_us"],
+            "step_frac": round(ref["pair_us"] / (ms_per_step * 1e3), 4),
+        }
+        log(f"{wl.name}: plain reads of the same bytes {ref}")
     sec = ms_per_step * 1e-3
     return {
         "value": round(T / sec, 2), "unit": "tokens/s", "steps": steps_timed, "steps_requested": steps_req,
@@ -373,6 +388,67 @@ def bench_moe_config(args, cfg, base, cache):
         "eager_ms_per_step": round(eager_ms, 6), "per_kernel_us": per_kernel_us,
         "gpu_clocks_after_timing": clocks,
     }
+
+
+def stream_reference(sizes, launches):
+    """moe_bench_stream_read on the given byte counts (rounded down to 16):
+    each size's per-launch time from the launches' own events (as the
+    kernels' times), and the time of the sizes read back to back, from
+    replays of a HIP graph of `launches` such sequences (as the steps).  The
+    reads rotate through a pool of at least 1 GiB so that the 256 MB Infinity
+    Cache cannot serve them."""
+    import torch
+    from nvfp4_weight_only_moe_amd import binding as B
+    sizes = [int(b) // 16 * 16 for b in sizes]
+    seq = sum(sizes)
+    pool = torch.empty(max(1 << 30, 3 * seq), dtype=torch.uint8, device="cuda:0")
+    pool.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    slots = max(1, (pool.numel() - seq) // seq + 1)
+
+    def one(i):
+        o = (i % slots) * seq
+        for b in sizes:
+            B.moe_bench_stream_read(pool[o:o + b], b, sink)
+            o += b
+
+    for i in range(4):
+        one(i)
+    torch.cuda.synchronize()
+    # per-size event times (the profile merges launches by name: one size at a time)
+    n = 20
+    kernel_us = []
+    for j, b in enumerate(sizes):
+        B.moe_profile_begin(n)
+        for i in range(n):
+            o = (i % slots) * seq + sum(sizes[:j])
+            B.moe_bench_stream_read(pool[o:o + b], b, sink)
+        prof = B.moe_profile_end()
+        c, ms = prof["stream_read"]
+        kernel_us.append(round(ms / c * 1e3, 3))
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        one(0)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(launches):
+            one(i)
+    for _ in range(3):
+        g.replay()
+    reps = 10
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    pair_us = a.elapsed_time(e) / (reps * launches) * 1e3
+    del g, pool
+    return {"bytes": sizes, "kernel_us": kernel_us, "pair_us": round(pair_us, 3)}
 
 
 def achievable_peaks():

@@ -380,6 +380,21 @@ moe_status moe_w4a16_shared_expert(const uint16_t *d_x, int32_t T, int32_t H, in
 moe_status moe_debug_set_prefill_variant(int32_t variant);
 
 /*
+ * A plain streaming read of `bytes` bytes from d_src, for benchmarks: the
+ * rate at which a kernel that only reads (16-byte non-temporal loads, all of
+ * a thread's loads issued before any is used, as in the decode kernels)
+ * streams a buffer of that size on this GPU -- the achievable reference that
+ * bench.py reports beside the spec HBM peak.  Not part of the layer.  d_src:
+ * device, 16-byte aligned, `bytes` a multiple of 16; d_sink: one device
+ * uint32 that the kernel writes only if its reduction of the data equals a
+ * fixed magic value (it exists so that the loads are kept).  bytes == 0 is a
+ * no-op.  Errors: MOE_ERR_INVALID_ARG (null pointer), MOE_ERR_SHAPE (bytes
+ * not a multiple of 16), MOE_ERR_ALIGN, MOE_ERR_HIP.  Asynchronous on
+ * `stream`; allocates nothing.
+ */
+moe_status moe_bench_stream_read(const void *d_src, size_t bytes, uint32_t *d_sink, hipStream_t stream);
+
+/*
  * Per-kernel timing for benchmarks.  moe_profile_begin(n) makes the calls that
  * follow (on any stream) launch each kernel with a pair of HIP timing events
  * that the launch stamps with the kernel's own start and end

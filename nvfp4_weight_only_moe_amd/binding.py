@@ -59,6 +59,7 @@ _SIGS = {
     "moe_w4a16_shared_expert_workspace_size": (_S, [_I, _I, _I]),
     "moe_w4a16_shared_expert": (_I, [_P, _I, _I, _I, _TP, _TP, _TP, _P, _P, _S, _P]),
     "moe_debug_set_prefill_variant": (_I, [_I]),
+    "moe_bench_stream_read": (_I, [_P, _S, _P, _P]),
     "moe_nvfp4_quantize_activations": (_I, [_P, _I, _I, ctypes.c_float, _P, _P, _P]),
     "moe_w4a4_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "moe_w4a4_forward": (_I, [_P, _I, _I, _I, _I, _I, _TP, _TP, _TP, ctypes.c_float, ctypes.c_float,
@@ -259,6 +260,15 @@ def moe_route_topk(logits, k, out=None, stream=None):
 def forward_workspace(T, H, I, E, k, device="cuda"):
     """A forward workspace (needs no initialisation)."""
     return torch.empty((max(moe_w4a16_workspace_size(T, H, I, E, k), 256),), dtype=torch.uint8, device=device)
+
+
+def moe_bench_stream_read(src, nbytes, sink, stream=None):
+    """Stream-read the first nbytes of the device tensor src (a benchmark
+    reference; see the header); sink: a device int32/uint32 tensor of >= 1
+    element."""
+    _dev_tensor(src, "src", min_bytes=nbytes)
+    _dev_tensor(sink, "sink", min_bytes=4)
+    _check(lib().moe_bench_stream_read(_ptr(src), int(nbytes), _ptr(sink), _stream(stream)), "moe_bench_stream_read")
 
 
 def moe_debug_set_prefill_variant(variant):

@@ -34,7 +34,7 @@ COMMON = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 SOURCES = ["abi.cpp", "quantize.hip", "route.hip", "moe_decode.hip", "moe_prefill.hip", "moe_prefill_pipe.hip",
-           "router.hip", "noalloc.hip"]
+           "router.hip", "noalloc.hip", "probe.hip"]
 
 
 def _compile(src, verbose):

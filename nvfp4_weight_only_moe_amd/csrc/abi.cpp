@@ -578,6 +578,14 @@ moe_status moe_w4a16_shared_expert(const uint16_t* d_x, int32_t T, int32_t H, in
     return launch_prefill(a, stream);
 }
 
+moe_status moe_bench_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink, hipStream_t stream) {
+    if (bytes == 0) return MOE_OK;
+    if (!d_src || !d_sink) return MOE_ERR_INVALID_ARG;
+    if (bytes % 16) return MOE_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(d_src) % 16 || reinterpret_cast<uintptr_t>(d_sink) % 4) return MOE_ERR_ALIGN;
+    return launch_stream_read(d_src, bytes, d_sink, stream);
+}
+
 moe_status moe_debug_set_prefill_variant(int32_t variant) {
     if (variant < 0 || variant > 2) return MOE_ERR_INVALID_ARG;
     g_prefill_variant.store(variant, std::memory_order_relaxed);

@@ -109,6 +109,9 @@ moe_status launch_forward_decode_routed(const FwdArgs& a, const float* logits, i
 // no routing arrays are read -- K = a.H, N = a.I, out written through a.h)
 bool linear_decode_supported(int T, int K, int N);
 moe_status launch_linear_decode(const FwdArgs& a, hipStream_t s);
+
+// Plain streaming read of `bytes` (a multiple of 16) for benchmarks (probe.hip).
+moe_status launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 // moe_prefill.hip: register-staged grouped GEMMs and the combine
 moe_status launch_gateup_grouped(const FwdArgs& a, hipStream_t s);
 moe_status launch_down_grouped(const FwdArgs& a, hipStream_t s);

@@ -273,3 +273,12 @@ def test_router_route_argument_errors(L):
     assert rr(lg=A + 0x100) == -1                                   # logits overlap x
     assert L.moe_router_route_workspace_size(8, 256, 8) >= 4
     assert L.moe_router_route_workspace_size(100000, 256, 8) > L.moe_route_workspace_size(100000, 256, 8)
+
+
+def test_stream_read_probe_argument_errors(L):
+    assert L.moe_bench_stream_read(None, 0, None, None) == 0                  # nothing to read
+    assert L.moe_bench_stream_read(None, 64, A + 0x4000000, None) == -1
+    assert L.moe_bench_stream_read(A, 64, None, None) == -1
+    assert L.moe_bench_stream_read(A, 40, A + 0x4000000, None) == -2         # not a multiple of 16
+    assert L.moe_bench_stream_read(A + 8, 64, A + 0x4000000, None) == -3
+    assert L.moe_bench_stream_read(A, 64, A + 0x4000002, None) == -3
