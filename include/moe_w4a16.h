@@ -263,7 +263,7 @@ moe_status moe_w4a4_forward(const uint16_t *d_x, int32_t T, int32_t H, int32_t I
  * device.  The call allocates and frees nothing.  Shapes whose workspace
  * (moe_w4a16_workspace_size) exceeds MOE_NOALLOC_SCRATCH_BYTES are refused
  * with MOE_ERR_WORKSPACE: every decode shape fits, and prefill up to about
- * 1400 (token, expert) pairs at hidden 5120 / intermediate 1536.  The array
+ * 2500 (token, expert) pairs at hidden 5120 / intermediate 1536.  The array
  * keeps the last call's contents and nothing in it needs to start at zero.
  * All calls on one GPU share the array: calls that overlap on one GPU (on
  * different streams, or from different threads without ordering) race and

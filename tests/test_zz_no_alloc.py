@@ -39,7 +39,7 @@ def test_noalloc_matches_route_forward_twice_then_smaller():
 
 
 def test_noalloc_refuses_a_workspace_beyond_the_array():
-    T, H, I, E, k = 2048, 1024, 512, 16, 4
+    T, H, I, E, k = 4096, 1024, 512, 16, 4      # h and y rows of 16,384 token-expert pairs: 48 MiB
     need = B.moe_w4a16_workspace_size(T, H, I, E, k)
     assert need > (32 << 20)
     p = Problem(T, H, I, E, k, 903)
