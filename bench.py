@@ -75,8 +75,10 @@ def parse():
                          "moe_w4a16_forward, separate = moe_router_logits + moe_w4a16_route_forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM counter scaling)")
-    ap.add_argument("--op", choices=("moe", "linear", "shared", "router"), default="moe",
-                    help="moe: the routed layer (default); linear: a dense H x H NVFP4 projection "
+    ap.add_argument("--op", choices=("moe", "w4a4", "linear", "shared", "router"), default="moe",
+                    help="moe: the routed layer (default); w4a4: the same layer with NVFP4 activations under "
+                         "the static input scales (moe_route_topk + moe_w4a4_forward per step); "
+                         "linear: a dense H x H NVFP4 projection "
                          "(moe_w4a16_linear); shared: the shared expert (moe_w4a16_shared_expert); "
                          "router: the BF16 router logits (moe_router_logits); all at the workload's "
                          "token count and shapes")
@@ -117,7 +119,7 @@ def main():
     from nvfp4_weight_only_moe_amd import binding as B
     from nvfp4_weight_only_moe_amd import workloads as wls
 
-    if args.op != "moe":
+    if args.op not in ("moe", "w4a4"):
         return bench_single(args, wls.WORKLOADS[args.config])
     B.moe_debug_set_prefill_variant(args.prefill_variant)
     torch.cuda.set_device(0)
@@ -149,7 +151,8 @@ def main():
     # the oracle on the host, per workload, after every GPU measurement
     if not args.no_cpu:
         for cfg in cfgs:
-            results[cfg]["cpu_baseline"] = cpu_baseline(wls.WORKLOADS[cfg], args.cpu_seconds)
+            results[cfg]["cpu_baseline"] = cpu_baseline(wls.WORKLOADS[cfg], args.cpu_seconds,
+                                                        w4a4=args.op == "w4a4")
             log(f"cpu baseline {wls.WORKLOADS[cfg].name}: {results[cfg]['cpu_baseline']['value']} tokens/s")
 
     head = results[cfgs[0]]
@@ -246,9 +249,17 @@ def bench_moe_config(args, cfg, base, cache):
         wr_d = torch.from_numpy(wb.view(np.int16)).to(dev)
         rws = B.router_route_workspace(wl.T, wl.E, wl.k, dev)
 
+    if args.op == "w4a4":
+        sx, sh = wls.W4A4_INPUT_SCALES
+        ws4 = torch.empty((max(B.moe_w4a4_workspace_size(wl.T, wl.H, wl.I, wl.E, wl.k), 256),), dtype=torch.uint8,
+                          device=dev)
+
     def step(i):
         L = layers[i % copies]
-        if args.router == "fused":
+        if args.op == "w4a4":
+            B.moe_route_topk(lg_d, wl.k, out=route)
+            B.moe_w4a4_forward(x_d, L["gate"], L["up"], L["down"], route, sx, sh, out=out, ws=ws4)
+        elif args.router == "fused":
             B.moe_router_route_topk(x_d, wr_d, wl.k, logits=lg_d, routing=route, ws=rws)
             B.moe_w4a16_forward(x_d, L["gate"], L["up"], L["down"], route, out=out, ws=ws)
         elif args.router == "separate":
@@ -352,7 +363,8 @@ def bench_moe_config(args, cfg, base, cache):
         "router_gemv": (wl.E * H * 2 + T * H * 2 + T * wl.E * 4, None),
     }
     work_bytes, work_flops = kernel_work.get(dominant, (alg_bytes_step, None))
-    roofline = make_roofline(dominant, dom_us, work_bytes, work_flops, measured_traffic(dominant, wl.name))
+    traffic = None if args.op == "w4a4" else measured_traffic(dominant, wl.name)   # counters are of W4A16 runs
+    roofline = make_roofline(dominant, dom_us, work_bytes, work_flops, traffic)
     if decode and not args.no_peaks and args.router == "none":
         # what a kernel that only reads reaches on the same byte counts: the
         # two decode kernels' bytes, each alone (event-timed like the
@@ -375,10 +387,14 @@ def bench_moe_config(args, cfg, base, cache):
         "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": wl.E, "k": k, "layer_copies": copies,
                    "hip_graph": graph_ms is not None, "touched_experts": U,
                    "max_rows_per_expert": int(counts.max()),
-                   "step_calls": ("router_route_topk+forward" if args.router == "fused" else
+                   "step_calls": ("route_topk+w4a4_forward" if args.op == "w4a4" else
+                                  "router_route_topk+forward" if args.router == "fused" else
                                   "router_logits+route_forward" if args.router == "separate" else
                                   "route_topk+forward" if args.split else "route_forward"),
-                   "prefill_variant": None if decode else args.prefill_variant},
+                   "prefill_variant": None if decode else args.prefill_variant,
+                   "activations": ("NVFP4 (W4A4, static input scales "
+                                   f"{wls.W4A4_INPUT_SCALES[0]:.6g}, {wls.W4A4_INPUT_SCALES[1]:.6g})"
+                                   if args.op == "w4a4" else "bf16 (W4A16)")},
         "roofline": roofline, "cpu_baseline": None, "step_spread": spread,
         "step_algorithmic_GBps": round(alg_bytes_step / sec / 1e9, 1),
         "step_hbm_frac": round(alg_bytes_step / sec / 1e9 / HBM_PEAK_GBPS, 4),
@@ -482,18 +498,21 @@ def achievable_peaks():
     return res
 
 
-def cpu_baseline(wl, budget_s):
+def cpu_baseline(wl, budget_s, w4a4=False):
     """The oracle (fp64 numpy, BLAS on the host's cores) on a bounded sample
     of the workload, expert quantization excluded.  Decode workloads: route +
     FFN + combine of the first tokens (1, or 2 of the 8), repeated within the
     budget.  Prefill workloads: the route of every token, then the experts
     one at a time in ascending index, each adding its weighted FFN rows into
     an fp64 [T, H] output, until the budget is spent; the rate counts the
-    rows processed (k rows make one token)."""
+    rows processed (k rows make one token).  w4a4: the W4A4 oracle (the
+    activations and the hidden rows quantized under the static input
+    scales)."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
     from oracle import moe as omoe
+    from oracle import w4a4 as ow4
     from nvfp4_weight_only_moe_amd import workloads as wls
     try:
         from threadpoolctl import threadpool_info
@@ -522,19 +541,27 @@ def cpu_baseline(wl, budget_s):
         while t_total < budget_s and runs < 50:
             t0 = time.perf_counter()
             ids_s, w_s = oracle.route_topk(logits[:n_tok], wl.k)
-            oracle.moe_forward(x[:n_tok], layer, ids_s, w_s, tokens=range(n_tok))
+            if w4a4:
+                ow4.moe_forward_w4a4(x[:n_tok], layer, ids_s, w_s, *wls.W4A4_INPUT_SCALES, tokens=range(n_tok))
+            else:
+                oracle.moe_forward(x[:n_tok], layer, ids_s, w_s, tokens=range(n_tok))
             t_total += time.perf_counter() - t0
             runs += 1
         rate = n_tok * runs / t_total
-        sample = (f"{n_tok} of {wl.T} token(s): route + SwiGLU FFN of {len(experts)} experts (dequantize + fp64) "
-                  f"+ combine, {runs} runs, {t_total:.1f} s; expert quantization excluded")
+        sample = (f"{n_tok} of {wl.T} token(s): route + {'W4A4 ' if w4a4 else ''}SwiGLU FFN of {len(experts)} "
+                  f"experts (dequantize + fp64) + combine, {runs} runs, {t_total:.1f} s; expert quantization excluded")
     else:
         t0 = time.perf_counter()
         ids, w = oracle.route_topk(logits, wl.k)
         t_route = time.perf_counter() - t0
         present = sorted(set(int(e) for e in ids.ravel()))
         out = np.zeros((wl.T, wl.H))
-        xf = x.astype(np.float64)
+        if w4a4:
+            t0 = time.perf_counter()
+            xf = ow4.fake_quantize(x, wls.W4A4_INPUT_SCALES[0]).astype(np.float64)
+            t_route += time.perf_counter() - t0
+        else:
+            xf = x.astype(np.float64)
         t_total, rows, done, i = t_route, 0, [], 0
         while i < len(present) and t_total < budget_s:
             batch = present[i:i + 4]
@@ -543,13 +570,16 @@ def cpu_baseline(wl, budget_s):
                 t0 = time.perf_counter()
                 r, sl = np.nonzero(ids == e)
                 wg, wu, wd = omoe.dequantize_expert(layer, e)
-                out[r] += w[r, sl][:, None] * omoe.expert_ffn(xf[r], wg, wu, wd)
+                y = (ow4.expert_ffn_w4a4(xf[r], wg, wu, wd, wls.W4A4_INPUT_SCALES[1]) if w4a4
+                     else omoe.expert_ffn(xf[r], wg, wu, wd))
+                out[r] += w[r, sl][:, None] * y
                 t_total += time.perf_counter() - t0
                 rows += r.size
                 done.append(e)
             i += len(batch)
         rate = rows / wl.k / t_total
-        sample = (f"route of all {wl.T} tokens ({t_route:.1f} s), then {len(done)} of {len(present)} touched experts "
+        sample = (f"route of all {wl.T} tokens{' and their activations quantized' if w4a4 else ''} ({t_route:.1f} s), "
+                  f"then {len(done)} of {len(present)} touched experts "
                   f"one at a time (ascending index), {rows} of {wl.T * wl.k} (token, expert) rows, dequantize + "
                   f"fp64 SwiGLU FFN accumulated into an fp64 [T, H] output, {t_total:.1f} s; rate = rows / k / time; "
                   f"expert quantization excluded")
