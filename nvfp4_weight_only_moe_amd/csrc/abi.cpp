@@ -425,9 +425,16 @@ moe_status moe_w4a4_forward(const uint16_t* d_x, int32_t T, int32_t H, int32_t I
     a.xs = input_scale_x;
     a.hs = input_scale_h;
     a.hf = hf;
-    // x -> NVFP4 values; gate/up + SwiGLU in fp32; h -> NVFP4 values; down
+    // x -> NVFP4 values; gate/up + SwiGLU in fp32; h -> NVFP4 values; down.
+    // With one token the decode gate/up kernel quantizes its own groups of h.
     if ((st = launch_quant_act(d_x, false, T, H, input_scale_x, nullptr, nullptr, xq, stream)) != MOE_OK) return st;
     const bool decode = decode_path_supported(T, k, H, I);
+    if (decode && T == 1) {
+        a.hf = nullptr;
+        a.hq = input_scale_h;
+        if ((st = launch_forward_decode_gateup(a, stream)) != MOE_OK) return st;
+        return launch_forward_decode_down(a, stream);
+    }
     const bool pipe = !decode && use_pipe(a);
     st = decode ? launch_forward_decode_gateup(a, stream)
                 : (pipe ? launch_gateup_pipe(a, stream) : launch_gateup_grouped(a, stream));

@@ -87,6 +87,10 @@ struct FwdArgs {
     float xs = 1.0f;
     float hs = 1.0f;
     float* hf = nullptr;
+    // W4A4 on the decode path: when > 0, the decode gate/up kernel quantizes
+    // its own output groups of h under this input scale (h gets the groups'
+    // NVFP4 values as bf16) and no hf round trip is made
+    float hq = 0.0f;
 };
 
 size_t forward_workspace_bytes(int T, int H, int I, int E, int k);

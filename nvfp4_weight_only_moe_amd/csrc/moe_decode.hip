@@ -38,6 +38,7 @@
 //     the whole chunk are loaded before any of them is used.
 #include "device_common.h"
 #include "internal.h"
+#include "quant_common.h"
 #include "route_common.h"
 
 namespace moe {
@@ -94,15 +95,22 @@ struct GuRoute {
 // the global scale go out as bf16 (a dense projection; h is then the output).
 // ONE: a single always-on expert (a shared expert): tokens in order, no
 // routing arrays read (LINEAR implies it).
-template <int CPL, int RW, int EPL, bool ROUTE, bool LINEAR = false, bool ONE = false>
+// QH (W4A4, RW == 2): a workgroup's 16 features of a token are one 16-group
+// of h; the workgroup quantizes it to NVFP4 under h_qscale and stores the
+// group's values E2M1 * E4M3 as bf16 (exact; the down kernel applies the
+// input scale), so no separate quantization pass over h is needed.
+template <int CPL, int RW, int EPL, bool ROUTE, bool LINEAR = false, bool ONE = false, bool QH = false>
 __global__ void __launch_bounds__(kGuThreads, RW == 1 ? 4 : 3)
 k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slots,
              const uint8_t* gc, const uint8_t* gs, const float* __restrict__ gg,
              const uint8_t* uc, const uint8_t* us, const float* __restrict__ ug,
              const int32_t* __restrict__ counts, const int32_t* __restrict__ sorted_slots,
-             uint16_t* __restrict__ h, const GuRoute R, float x_scale, float* __restrict__ hf) {
+             uint16_t* __restrict__ h, const GuRoute R, float x_scale, float* __restrict__ hf, float h_qscale) {
+    static_assert(!QH || (RW == 2 && !LINEAR), "a 16-feature workgroup per h group");
     constexpr int kXT = x_stage_tokens<LINEAR>();
+    constexpr int kGroupFeatures = kGuWaves * 2 * RW;          // features of I per workgroup
     extern __shared__ uint4 xs[];   // [kXT][H / 8]
+    __shared__ float s_hq[QH ? 8 : 1][QH ? kGroupFeatures : 1];  // this workgroup's h values per token (QH)
     __shared__ int s_ids[kDecodeMaxSlots], s_pos[kDecodeMaxSlots], s_sorted[kDecodeMaxSlots];
     __shared__ int s_list[kDecodeMaxSlots], s_ucnt[kDecodeMaxSlots], s_uoff[kDecodeMaxSlots];
     const int lane = threadIdx.x & (kWave - 1);
@@ -240,11 +248,28 @@ k_dec_gateup(const uint16_t* __restrict__ x, int H, int I, int E, int k, int slo
                 if (lane < 2 && n + lane < I) {
                     const float av = lane ? a1 : a0, bv = lane ? b1 : b0;
                     const float v = LINEAR ? g_gate * av : silu(g_gate * av) * (g_up * bv);
-                    const int64_t idx = (int64_t)(p0 + qt) * I + n + lane;
-                    if (hf) hf[idx] = v;
-                    else h[idx] = f32_to_bf16_rne(v);
+                    if constexpr (QH) {
+                        s_hq[qt][n + lane - (int)blockIdx.x * kGroupFeatures] = v;
+                    } else {
+                        const int64_t idx = (int64_t)(p0 + qt) * I + n + lane;
+                        if (hf) hf[idx] = v;
+                        else h[idx] = f32_to_bf16_rne(v);
+                    }
                 }
             }
+        }
+    }
+
+    if constexpr (QH) {
+        // 16 lanes per token quantize the token's 16-feature group, one
+        // feature each (every lane of a wave takes part in the group maximum)
+        __syncthreads();
+        const int t = (int)threadIdx.x;
+        if (t < kWave * ((ne * 16 + kWave - 1) / kWave)) {        // whole waves
+            const int q = t / 16, f = t % 16;
+            const float v = q < ne ? s_hq[q][f] : 0.0f;
+            const uint16_t b = nvfp4_lane_value_bf16(v, h_qscale);
+            if (q < ne) h[(int64_t)(p0 + q) * I + (int64_t)blockIdx.x * kGroupFeatures + f] = b;
         }
     }
 
@@ -541,17 +566,17 @@ k_dec_down(const uint16_t* __restrict__ h, int T, int H, int I, int E, int k,
 // larger than one resident round anyway (a column per slot, most of them
 // empty after the lookup), and smaller workgroups start streaming sooner
 // (measured on MI355X at 8 tokens, 35 experts: 70 us against 75).
-template <int CPL, int RW, int EPL, bool ROUTE, bool ONE = false>
+template <int CPL, int RW, int EPL, bool ROUTE, bool ONE = false, bool QH = false>
 moe_status launch_gateup_epl(const FwdArgs& a, const GuRoute& R, hipStream_t s) {
     const int rows_per_block = kGuWaves * 2 * RW;
     const dim3 grid((a.I + rows_per_block - 1) / rows_per_block, std::min(a.T * a.k, a.E));
     const size_t shmem = (size_t)std::min(a.T, kXTokens) * a.H * sizeof(uint16_t);
-    auto kern = k_dec_gateup<CPL, RW, EPL, ROUTE, false, ONE>;
+    auto kern = k_dec_gateup<CPL, RW, EPL, ROUTE, false, ONE, QH>;
     if (allow_dynamic_lds(reinterpret_cast<const void*>(kern), shmem) != MOE_OK) return MOE_ERR_HIP;
     MOE_LAUNCH(ROUTE ? "dec_gateup_route" : "dec_gateup", kern, grid, dim3(kGuThreads), shmem, s, a.x, a.H, a.I,
                a.E, a.k, a.T * a.k, (const uint8_t*)a.gate->codes, (const uint8_t*)a.gate->scales,
                (const float*)a.gate->global_scale, (const uint8_t*)a.up->codes, (const uint8_t*)a.up->scales,
-               (const float*)a.up->global_scale, a.counts, a.sorted_slots, a.h, R, a.xs, a.hf);
+               (const float*)a.up->global_scale, a.counts, a.sorted_slots, a.h, R, a.xs, QH ? nullptr : a.hf, a.hq);
     return MOE_OK;
 }
 
@@ -566,6 +591,11 @@ moe_status launch_gateup_rw(const FwdArgs& a, const GuRoute* R, hipStream_t s) {
 template <int CPL>
 moe_status launch_gateup_gpl(const FwdArgs& a, const GuRoute* R, hipStream_t s, bool one) {
     if (one) return launch_gateup_epl<CPL, 1, 4, false, true>(a, GuRoute{}, s);
+    if (a.hq > 0.0f) {      // W4A4, one token: 16-feature workgroups that quantize their own h groups
+        if (R || a.T != 1) return MOE_ERR_UNSUPPORTED;
+        return a.E <= 256 ? launch_gateup_epl<CPL, 2, 4, false, false, true>(a, GuRoute{}, s)
+                          : launch_gateup_epl<CPL, 2, 16, false, false, true>(a, GuRoute{}, s);
+    }
     // two stages per wave when enough expert columns fill the chip with
     // resident workgroups; with one or two experts (a shared expert) one
     // stage, which doubles the workgroups streaming at once
@@ -682,7 +712,7 @@ moe_status launch_linear_rw(const FwdArgs& a, hipStream_t s) {
     MOE_LAUNCH("dec_linear", kern, grid, dim3(kGuThreads), shmem, s, a.x, a.H, a.I, 1, 1, a.T,
                (const uint8_t*)a.gate->codes, (const uint8_t*)a.gate->scales, (const float*)a.gate->global_scale,
                (const uint8_t*)a.gate->codes, (const uint8_t*)a.gate->scales, (const float*)a.gate->global_scale,
-               a.counts, a.sorted_slots, a.h, none, 1.0f, (float*)nullptr);
+               a.counts, a.sorted_slots, a.h, none, 1.0f, (float*)nullptr, 0.0f);
     return MOE_OK;
 }
 

@@ -14,6 +14,7 @@
 // contraction is off in this file.
 #include "device_common.h"
 #include "internal.h"
+#include "quant_common.h"
 
 #pragma clang fp contract(off)
 
@@ -25,30 +26,6 @@ constexpr int kQBlock = 256;
 __device__ __forceinline__ float global_scale_from_amax(uint32_t amax_bits) {
     const float g = __uint_as_float(amax_bits) / 2688.0f;
     return (g > 0.0f) ? g : 1.0f;  // all-zero (or underflowing) tensor
-}
-
-// Round a non-negative fp32 value to the nearest E4M3 byte, ties to even,
-// saturating at 448 (0x7E).  Works on the integer significand: the value is
-// scaled by a power of two (exact) so that its E4M3 grid step becomes 1, then
-// rounded half-to-even.
-__device__ __forceinline__ uint32_t e4m3_encode_rne_sat(float x) {
-    if (!(x < 448.0f)) return 0x7Eu;                       // also NaN -> saturate
-    if (x < 0x1p-6f) return (uint32_t)rintf(x * 512.0f);   // subnormal grid 2^-9
-    const int e = (int)((__float_as_uint(x) >> 23) & 0xFF) - 127;   // -6..8
-    const float q = x * __uint_as_float((uint32_t)(127 + 3 - e) << 23);  // [8, 16)
-    const uint32_t code = (uint32_t)((e + 7) << 3) + (uint32_t)rintf(q) - 8u;
-    return code > 0x7Eu ? 0x7Eu : code;
-}
-
-// Nearest E2M1 code of q (ties to the even code, saturating at 6), sign bit
-// copied from q.  The decision points are the midpoints between neighbouring
-// magnitudes; ">=" where the upper neighbour has the even code.
-__device__ __forceinline__ uint32_t e2m1_encode_rne_sat(float q) {
-    const float a = fabsf(q);
-    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                       (uint32_t)(a > 5.0f);
-    return c | ((__float_as_uint(q) >> 31) << 3);
 }
 
 __global__ void k_amax_clear(uint32_t* amax_bits, int E) {
@@ -228,18 +205,9 @@ __global__ void __launch_bounds__(kQBlock) k_quant_act(const void* __restrict__ 
             }
         }
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    const float s_f = (amax / 6.0f) / input_scale;
-    const uint32_t sb = e4m3_encode_rne_sat(s_f);
-    const float s_q = e4m3_to_f32(sb);
-    const float d = s_q * input_scale;
-    uint32_t c[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-        c[i] = (d == 0.0f) ? ((__float_as_uint(v[i]) >> 31) << 3) : e2m1_encode_rne_sat(v[i] / d);
     if constexpr (PACKED) {
+        uint32_t c[16];
+        const uint32_t sb = nvfp4_group_codes(v, input_scale, c);
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -249,14 +217,8 @@ __global__ void __launch_bounds__(kQBlock) k_quant_act(const void* __restrict__ 
         reinterpret_cast<uint2*>(codes)[gi] = make_uint2(lo, hi);
         scales[gi] = (uint8_t)sb;
     } else {
-        // E2M1 magnitude * scale, exact in fp32 and in bf16 (truncation exact)
         uint32_t o[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t pair = c[2 * i] | (c[2 * i + 1] << 4);
-            const floatx2 f = e2m1x2_to_f32<0>(pair);
-            o[i] = pack_bf16x2_exact(f[0] * s_q, f[1] * s_q);
-        }
+        nvfp4_group_values_bf16(v, input_scale, o);
         uint4* dst = reinterpret_cast<uint4*>(deq) + gi * 2;
         dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
         dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
