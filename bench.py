@@ -77,7 +77,7 @@ def parse():
                     help="also run a plain 256 MiB device copy (reference for HBM counter scaling)")
     ap.add_argument("--op", choices=("moe", "w4a4", "linear", "shared", "router"), default="moe",
                     help="moe: the routed layer (default); w4a4: the same layer with NVFP4 activations under "
-                         "the static input scales (moe_route_topk + moe_w4a4_forward per step); "
+                         "the static input scales (moe_w4a4_route_forward per step); "
                          "linear: a dense H x H NVFP4 projection "
                          "(moe_w4a16_linear); shared: the shared expert (moe_w4a16_shared_expert); "
                          "router: the BF16 router logits (moe_router_logits); all at the workload's "
@@ -257,8 +257,8 @@ def bench_moe_config(args, cfg, base, cache):
     def step(i):
         L = layers[i % copies]
         if args.op == "w4a4":
-            B.moe_route_topk(lg_d, wl.k, out=route)
-            B.moe_w4a4_forward(x_d, L["gate"], L["up"], L["down"], route, sx, sh, out=out, ws=ws4)
+            B.moe_w4a4_route_forward(lg_d, x_d, L["gate"], L["up"], L["down"], wl.k, sx, sh, routing=route, out=out,
+                                     ws=ws4)
         elif args.router == "fused":
             B.moe_router_route_topk(x_d, wr_d, wl.k, logits=lg_d, routing=route, ws=rws)
             B.moe_w4a16_forward(x_d, L["gate"], L["up"], L["down"], route, out=out, ws=ws)
@@ -387,7 +387,7 @@ def bench_moe_config(args, cfg, base, cache):
         "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": wl.E, "k": k, "layer_copies": copies,
                    "hip_graph": graph_ms is not None, "touched_experts": U,
                    "max_rows_per_expert": int(counts.max()),
-                   "step_calls": ("route_topk+w4a4_forward" if args.op == "w4a4" else
+                   "step_calls": ("w4a4_route_forward" if args.op == "w4a4" else
                                   "router_route_topk+forward" if args.router == "fused" else
                                   "router_logits+route_forward" if args.router == "separate" else
                                   "route_topk+forward" if args.split else "route_forward"),

@@ -241,6 +241,14 @@ moe_status moe_w4a16_route_forward(const float *d_logits, const uint16_t *d_x,
  *   bf16) and the input scale multiplies the weight's global scale in each
  *   epilogue; products accumulate in fp32.  d_ws of moe_w4a4_workspace_size
  *   bytes (no initialisation).  Deterministic; graph-capturable.
+ *
+ * moe_w4a4_route_forward: moe_route_topk on d_logits (fp32 [T][E]) and
+ *   moe_w4a4_forward in one call, as moe_w4a16_route_forward is for the
+ *   W4A16 layer: the routing outputs are stored exactly as moe_route_topk
+ *   stores them and the output is exactly moe_w4a4_forward's on them; with one
+ *   token the gate/up kernel routes itself (no route launch).  Same workspace
+ *   and errors as moe_w4a4_forward, plus MOE_ERR_INVALID_ARG for a null
+ *   d_logits.
  */
 moe_status moe_nvfp4_quantize_activations(const uint16_t *d_x, int32_t T, int32_t K, float input_scale,
                                           uint8_t *d_codes, uint8_t *d_scales, hipStream_t stream);
@@ -252,6 +260,13 @@ moe_status moe_w4a4_forward(const uint16_t *d_x, int32_t T, int32_t H, int32_t I
                             const int32_t *d_counts, const int32_t *d_offsets,
                             const int32_t *d_sorted_slots, const int32_t *d_slot_pos,
                             uint16_t *d_out, void *d_ws, size_t ws_bytes, hipStream_t stream);
+moe_status moe_w4a4_route_forward(const float *d_logits, const uint16_t *d_x, int32_t T, int32_t H, int32_t I,
+                                  int32_t E, int32_t k, const moe_nvfp4_tensor *gate,
+                                  const moe_nvfp4_tensor *up, const moe_nvfp4_tensor *down,
+                                  float input_scale_x, float input_scale_h, int32_t *d_topk_ids,
+                                  float *d_topk_w, int32_t *d_counts, int32_t *d_offsets,
+                                  int32_t *d_sorted_slots, int32_t *d_slot_pos, uint16_t *d_out,
+                                  void *d_ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * moe_w4a16_route_forward for callers that cannot allocate -- code under HIP

@@ -64,6 +64,8 @@ _SIGS = {
     "moe_w4a4_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "moe_w4a4_forward": (_I, [_P, _I, _I, _I, _I, _I, _TP, _TP, _TP, ctypes.c_float, ctypes.c_float,
                               _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
+    "moe_w4a4_route_forward": (_I, [_P, _P, _I, _I, _I, _I, _I, _TP, _TP, _TP, ctypes.c_float, ctypes.c_float,
+                                    _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
     "moe_w4a16_route_forward_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _I, _TP, _TP, _TP, _P, _P, _P, _P, _P, _P, _P,
                                              _P]),
     "moe_router_route_workspace_size": (_S, [_I, _I, _I]),
@@ -436,6 +438,33 @@ def moe_w4a4_forward(x_bits, gate, up, down, routing, input_scale_x, input_scale
                                   _ptr(routing.offsets), _ptr(routing.sorted_slots), _ptr(routing.slot_pos),
                                   _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "moe_w4a4_forward")
     return out
+
+
+def moe_w4a4_route_forward(logits, x_bits, gate, up, down, k, input_scale_x, input_scale_h, routing=None,
+                           out=None, ws=None, stream=None):
+    """Route (as moe_route_topk, outputs stored in `routing`) and run the W4A4
+    layer (with one token the gate/up kernel routes itself).  Returns
+    (out, routing)."""
+    sx = _input_scale(input_scale_x, "input_scale_x")
+    sh = _input_scale(input_scale_h, "input_scale_h")
+    _dev_tensor(x_bits, "x", _BITS16)
+    T, H = x_bits.shape
+    E, I, _ = gate.shape
+    _dev_tensor(logits, "logits", torch.float32, (T, E))
+    routing = Routing.empty(T, E, k, x_bits.device) if routing is None else routing
+    routing.check(T, E, k)
+    out = torch.empty((T, H), dtype=torch.int16, device=x_bits.device) if out is None else out
+    _dev_tensor(out, "out", _BITS16, (T, H))
+    need = moe_w4a4_workspace_size(T, H, I, E, k)
+    ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=x_bits.device) if ws is None else ws
+    _dev_tensor(ws, "ws", min_bytes=need)
+    g, u, d = gate.cstruct(), up.cstruct(), down.cstruct()
+    _check(lib().moe_w4a4_route_forward(_ptr(logits), _ptr(x_bits), T, H, I, E, k, ctypes.byref(g), ctypes.byref(u),
+                                        ctypes.byref(d), sx, sh, _ptr(routing.topk_ids), _ptr(routing.topk_w),
+                                        _ptr(routing.counts), _ptr(routing.offsets), _ptr(routing.sorted_slots),
+                                        _ptr(routing.slot_pos), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_w4a4_route_forward")
+    return out, routing
 
 
 def moe_w4a16_route_forward_noalloc(logits, x_bits, gate, up, down, k, routing=None, out=None, stream=None):

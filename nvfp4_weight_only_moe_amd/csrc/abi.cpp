@@ -401,6 +401,58 @@ moe_status moe_nvfp4_quantize_activations(const uint16_t* d_x, int32_t T, int32_
     return launch_quant_act(d_x, false, T, K, input_scale, d_codes, d_scales, nullptr, stream);
 }
 
+namespace {
+
+// The W4A4 layer after the argument checks: x -> NVFP4 values; gate/up +
+// SwiGLU in fp32; h -> NVFP4 values; down.  With one token the decode gate/up
+// kernel quantizes its own groups of h (and, given R, routes itself).
+moe_status w4a4_run(const uint16_t* d_x, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                    const moe_nvfp4_tensor* gate, const moe_nvfp4_tensor* up, const moe_nvfp4_tensor* down,
+                    float input_scale_x, float input_scale_h, const float* d_logits, int32_t* d_topk_ids,
+                    float* d_topk_w, int32_t* d_counts, int32_t* d_offsets, int32_t* d_sorted_slots,
+                    int32_t* d_slot_pos, uint16_t* d_out, void* d_ws, hipStream_t stream) {
+    uint8_t* ws = static_cast<uint8_t*>(d_ws);
+    const size_t slots = (size_t)T * k;
+    uint16_t* xq = reinterpret_cast<uint16_t*>(ws);
+    float* hf = reinterpret_cast<float*>(ws + round_up((size_t)T * H * sizeof(uint16_t), kAlign));
+    void* fws = ws + round_up((size_t)T * H * sizeof(uint16_t), kAlign) + round_up(slots * I * sizeof(float), kAlign);
+    const WsLayout L = ws_layout(fws, T, H, I, k);
+    FwdArgs a = make_args(xq, T, H, I, E, k, gate, up, down, d_topk_ids, d_topk_w, d_counts, d_offsets,
+                          d_sorted_slots, d_slot_pos, d_out, L);
+    a.xs = input_scale_x;
+    a.hs = input_scale_h;
+    a.hf = hf;
+    const bool decode = decode_path_supported(T, k, H, I);
+    moe_status st;
+    if (d_logits && !(decode && T == 1)) {
+        st = launch_route(d_logits, T, E, k, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots, d_slot_pos,
+                          L.route, stream);
+        if (st != MOE_OK) return st;
+    }
+    if ((st = launch_quant_act(d_x, false, T, H, input_scale_x, nullptr, nullptr, xq, stream)) != MOE_OK) return st;
+    if (decode && T == 1) {
+        a.hf = nullptr;
+        a.hq = input_scale_h;
+        st = d_logits ? launch_forward_decode_gateup_routed(a, d_logits, d_topk_ids, d_topk_w, d_counts, d_offsets,
+                                                            d_sorted_slots, d_slot_pos, stream)
+                      : launch_forward_decode_gateup(a, stream);
+        if (st != MOE_OK) return st;
+        return launch_forward_decode_down(a, stream);
+    }
+    const bool pipe = !decode && use_pipe(a);
+    st = decode ? launch_forward_decode_gateup(a, stream)
+                : (pipe ? launch_gateup_pipe(a, stream) : launch_gateup_grouped(a, stream));
+    if (st != MOE_OK) return st;
+    if ((st = launch_quant_act(hf, true, (int64_t)slots, I, input_scale_h, nullptr, nullptr, L.h, stream)) != MOE_OK)
+        return st;
+    if (decode) return launch_forward_decode_down(a, stream);
+    st = pipe ? launch_down_pipe(a, stream) : launch_down_grouped(a, stream);
+    if (st != MOE_OK) return st;
+    return launch_combine(a, stream);
+}
+
+}  // namespace
+
 moe_status moe_w4a4_forward(const uint16_t* d_x, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                             const moe_nvfp4_tensor* gate, const moe_nvfp4_tensor* up, const moe_nvfp4_tensor* down,
                             float input_scale_x, float input_scale_h, const int32_t* d_topk_ids,
@@ -414,37 +466,27 @@ moe_status moe_w4a4_forward(const uint16_t* d_x, int32_t T, int32_t H, int32_t I
     const size_t need = T > 0 && k > 0 && H > 0 && I > 0 ? w4a4_workspace_bytes(T, H, I, E, k) : 0;
     st = check_forward(d_x, T, H, I, E, k, gate, up, down, ptrs, 6, d_out, d_ws, ws_bytes, need);
     if (st != MOE_OK || T == 0) return st;
-    uint8_t* ws = static_cast<uint8_t*>(d_ws);
-    const size_t slots = (size_t)T * k;
-    uint16_t* xq = reinterpret_cast<uint16_t*>(ws);
-    float* hf = reinterpret_cast<float*>(ws + round_up((size_t)T * H * sizeof(uint16_t), kAlign));
-    void* fws = ws + round_up((size_t)T * H * sizeof(uint16_t), kAlign) + round_up(slots * I * sizeof(float), kAlign);
-    const WsLayout L = ws_layout(fws, T, H, I, k);
-    FwdArgs a = make_args(xq, T, H, I, E, k, gate, up, down, d_topk_ids, d_topk_w, d_counts, d_offsets,
-                          d_sorted_slots, d_slot_pos, d_out, L);
-    a.xs = input_scale_x;
-    a.hs = input_scale_h;
-    a.hf = hf;
-    // x -> NVFP4 values; gate/up + SwiGLU in fp32; h -> NVFP4 values; down.
-    // With one token the decode gate/up kernel quantizes its own groups of h.
-    if ((st = launch_quant_act(d_x, false, T, H, input_scale_x, nullptr, nullptr, xq, stream)) != MOE_OK) return st;
-    const bool decode = decode_path_supported(T, k, H, I);
-    if (decode && T == 1) {
-        a.hf = nullptr;
-        a.hq = input_scale_h;
-        if ((st = launch_forward_decode_gateup(a, stream)) != MOE_OK) return st;
-        return launch_forward_decode_down(a, stream);
-    }
-    const bool pipe = !decode && use_pipe(a);
-    st = decode ? launch_forward_decode_gateup(a, stream)
-                : (pipe ? launch_gateup_pipe(a, stream) : launch_gateup_grouped(a, stream));
+    return w4a4_run(d_x, T, H, I, E, k, gate, up, down, input_scale_x, input_scale_h, nullptr,
+                    const_cast<int32_t*>(d_topk_ids), const_cast<float*>(d_topk_w), const_cast<int32_t*>(d_counts),
+                    const_cast<int32_t*>(d_offsets), const_cast<int32_t*>(d_sorted_slots),
+                    const_cast<int32_t*>(d_slot_pos), d_out, d_ws, stream);
+}
+
+moe_status moe_w4a4_route_forward(const float* d_logits, const uint16_t* d_x, int32_t T, int32_t H, int32_t I,
+                                  int32_t E, int32_t k, const moe_nvfp4_tensor* gate, const moe_nvfp4_tensor* up,
+                                  const moe_nvfp4_tensor* down, float input_scale_x, float input_scale_h,
+                                  int32_t* d_topk_ids, float* d_topk_w, int32_t* d_counts, int32_t* d_offsets,
+                                  int32_t* d_sorted_slots, int32_t* d_slot_pos, uint16_t* d_out, void* d_ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+    moe_status st = check_input_scale(input_scale_x);
     if (st != MOE_OK) return st;
-    if ((st = launch_quant_act(hf, true, (int64_t)slots, I, input_scale_h, nullptr, nullptr, L.h, stream)) != MOE_OK)
-        return st;
-    if (decode) return launch_forward_decode_down(a, stream);
-    st = pipe ? launch_down_pipe(a, stream) : launch_down_grouped(a, stream);
-    if (st != MOE_OK) return st;
-    return launch_combine(a, stream);
+    if ((st = check_input_scale(input_scale_h)) != MOE_OK) return st;
+    const void* ptrs[] = {d_logits, d_topk_ids, d_topk_w, d_counts, d_offsets, d_sorted_slots, d_slot_pos};
+    const size_t need = T > 0 && k > 0 && H > 0 && I > 0 ? w4a4_workspace_bytes(T, H, I, E, k) : 0;
+    st = check_forward(d_x, T, H, I, E, k, gate, up, down, ptrs, 7, d_out, d_ws, ws_bytes, need);
+    if (st != MOE_OK || T == 0) return st;
+    return w4a4_run(d_x, T, H, I, E, k, gate, up, down, input_scale_x, input_scale_h, d_logits, d_topk_ids,
+                    d_topk_w, d_counts, d_offsets, d_sorted_slots, d_slot_pos, d_out, d_ws, stream);
 }
 
 moe_status moe_router_logits(const uint16_t* d_x, int32_t T, int32_t H, const uint16_t* d_wr, int32_t E,

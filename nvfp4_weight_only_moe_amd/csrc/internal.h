@@ -99,6 +99,10 @@ moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s);
 // its two halves (gate/up + SwiGLU, down + combine) as separate calls
 moe_status launch_forward_decode_gateup(const FwdArgs& a, hipStream_t s);
 moe_status launch_forward_decode_down(const FwdArgs& a, hipStream_t s);
+// the gate/up half routing a single token itself (stores the routing outputs)
+moe_status launch_forward_decode_gateup_routed(const FwdArgs& a, const float* logits, int32_t* ids, float* w,
+                                               int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* pos,
+                                               hipStream_t s);
 // the same kernels for one always-on expert (E = 1, k = 1, weight 1, tokens
 // in order): no routing arrays are read
 moe_status launch_forward_decode_one(const FwdArgs& a, hipStream_t s);

@@ -592,7 +592,10 @@ template <int CPL>
 moe_status launch_gateup_gpl(const FwdArgs& a, const GuRoute* R, hipStream_t s, bool one) {
     if (one) return launch_gateup_epl<CPL, 1, 4, false, true>(a, GuRoute{}, s);
     if (a.hq > 0.0f) {      // W4A4, one token: 16-feature workgroups that quantize their own h groups
-        if (R || a.T != 1) return MOE_ERR_UNSUPPORTED;
+        if (a.T != 1) return MOE_ERR_UNSUPPORTED;
+        if (R)
+            return a.E <= 256 ? launch_gateup_epl<CPL, 2, 4, true, false, true>(a, *R, s)
+                              : launch_gateup_epl<CPL, 2, 16, true, false, true>(a, *R, s);
         return a.E <= 256 ? launch_gateup_epl<CPL, 2, 4, false, false, true>(a, GuRoute{}, s)
                           : launch_gateup_epl<CPL, 2, 16, false, false, true>(a, GuRoute{}, s);
     }
@@ -691,6 +694,14 @@ moe_status launch_forward_decode_gateup(const FwdArgs& a, hipStream_t s) {
     return launch_decode_gateup_part(a, nullptr, s, false);
 }
 moe_status launch_forward_decode_down(const FwdArgs& a, hipStream_t s) { return launch_decode_down_part(a, s, false); }
+
+moe_status launch_forward_decode_gateup_routed(const FwdArgs& a, const float* logits, int32_t* ids, float* w,
+                                               int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* pos,
+                                               hipStream_t s) {
+    if (a.T != 1) return MOE_ERR_UNSUPPORTED;
+    const GuRoute R{logits, ids, w, counts, offsets, sorted, pos};
+    return launch_decode_gateup_part(a, &R, s, false);
+}
 
 moe_status launch_forward_decode(const FwdArgs& a, hipStream_t s) { return launch_decode_pair(a, nullptr, s); }
 

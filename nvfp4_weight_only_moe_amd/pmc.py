@@ -34,9 +34,9 @@ CALIBRATION_COPIES = 3
 # Sources that determine each kernel's memory traffic; the stored counters
 # are valid while these files are unchanged.
 KERNEL_SOURCES = {
-    "dec_gateup": ["moe_decode.hip", "device_common.h", "route_common.h"],
-    "dec_gateup_route": ["moe_decode.hip", "device_common.h", "route_common.h"],
-    "dec_down": ["moe_decode.hip", "device_common.h", "route_common.h"],
+    "dec_gateup": ["moe_decode.hip", "device_common.h", "route_common.h", "quant_common.h"],
+    "dec_gateup_route": ["moe_decode.hip", "device_common.h", "route_common.h", "quant_common.h"],
+    "dec_down": ["moe_decode.hip", "device_common.h", "route_common.h", "quant_common.h"],
     "gemm_gateup": ["moe_prefill.hip", "moe_prefill_pipe.hip", "device_common.h"],
     "gemm_down": ["moe_prefill.hip", "moe_prefill_pipe.hip", "device_common.h"],
 }

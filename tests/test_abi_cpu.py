@@ -244,6 +244,30 @@ def test_w4a4_argument_errors(L):
     assert w4(L, ws_bytes=need - 1) == -7
 
 
+def w4r(L, logits=A + 0x3000000, x=A, T=4, H=256, I=128, E=8, k=2, sx=0.01, sh=0.02, ptr=A + 0x3100000,
+        out=A + 0x800000, ws=A + 0x900000, ws_bytes=1 << 30):
+    gate, up, down = T_(E, I, H), T_(E, I, H, A + 0x1000000), T_(E, H, I, A + 0x2000000)
+    p = [ptr] * 6
+    return L.moe_w4a4_route_forward(logits, x, T, H, I, E, k, ctypes.byref(gate), ctypes.byref(up),
+                                    ctypes.byref(down), ctypes.c_float(sx), ctypes.c_float(sh), *p, out, ws,
+                                    ws_bytes, None)
+
+
+def test_w4a4_route_forward_argument_errors(L):
+    L.moe_w4a4_route_forward.argtypes = b._SIGS["moe_w4a4_route_forward"][1]
+    assert w4r(L, T=0) == b.MOE_OK
+    for bad in (0.0, -1.0):
+        assert w4r(L, sx=bad) == -6
+        assert w4r(L, sh=bad) == -6
+        assert w4r(L, T=0, sh=bad) == -6
+    assert w4r(L, sx=float("nan")) == -5
+    assert w4r(L, logits=0) == -1
+    assert w4r(L, x=0) == -1
+    assert w4r(L, H=200) == -2
+    assert w4r(L, ws=0) == -7
+    assert w4r(L, ws_bytes=L.moe_w4a4_workspace_size(4, 256, 128, 8, 2) - 1) == -7
+
+
 def test_quantize_activations_argument_errors(L):
     q = L.moe_nvfp4_quantize_activations
     f = ctypes.c_float

@@ -108,6 +108,34 @@ def test_w4a4_forward_parity(T, H, I, E, k, seed):
     assert d > 5e-3
 
 
+@pytest.mark.parametrize("T,H,I,E,k,seed", [
+    (1, 1024, 512, 16, 8, 620),       # one token: the gate/up kernel routes itself
+    (1, 2048, 1024, 12, 3, 621),      # one token, another shape
+    (8, 1024, 512, 16, 4, 622),       # decode kernels after the route launch
+    (100, 512, 256, 16, 4, 623),      # grouped GEMMs after the route launch
+])
+def test_w4a4_route_forward_equals_route_then_forward(T, H, I, E, k, seed):
+    """moe_w4a4_route_forward stores exactly moe_route_topk's routing and
+    returns exactly moe_w4a4_forward's output on it, bit for bit."""
+    p = Problem(T, H, I, E, k, seed)
+    gate, up, down = (B.moe_w4a16_quantize_pack(to_dev(m)) for m in p.ms)
+    sx, sh = np.float32(5.0 / 2688.0), np.float32(4.0 / 2688.0)
+    xb, lg = to_dev(p.xb, torch.int16), to_dev(p.logits)
+    r_ref = B.moe_route_topk(lg, k)
+    ref = B.moe_w4a4_forward(xb, gate, up, down, r_ref, sx, sh)
+    r, parts = guarded_routing(T, E, k)
+    parts["out"] = Guarded((T, H), torch.int16)
+    parts["ws"] = Guarded((max(B.moe_w4a4_workspace_size(T, H, I, E, k), 16),), torch.uint8)
+    B.moe_w4a4_route_forward(lg, xb, gate, up, down, k, sx, sh, routing=r, out=parts["out"].t, ws=parts["ws"].t)
+    torch.cuda.synchronize()
+    check_guards(parts, f"w4a4 route_forward T{T} E{E} k{k}")
+    for name in ("topk_ids", "topk_w", "counts", "offsets", "sorted_slots", "slot_pos"):
+        assert torch.equal(getattr(r, name), getattr(r_ref, name)), (T, name)
+    assert torch.equal(parts["out"].t, ref), T
+    compare_out(bf16_bits_to_f64(ref), ow4.moe_forward_w4a4(p.x, p.layer, p.ids, p.w, sx, sh),
+                f"w4a4 route_forward T{T} H{H} E{E} k{k}")
+
+
 @pytest.mark.parametrize("variant", [0, 1])
 def test_w4a4_long_expert_every_tile(variant):
     T, H, I, E, k, seed = 2200, 1024, 512, 4, 2, 610
