@@ -75,30 +75,186 @@ template <int BM, int NW> constexpr int gemm_wg_per_cu() {
     return NW == 8 ? 1 : BM >= 128 ? 1 : BM == 32 ? 3 : 2;
 }
 
-// NW waves, each owning 4 column subtiles of 16 (gate/up: 32 h columns as 32
-// gate + 32 up weight rows; down: 64 output columns) for all BM rows, so the
-// tile is BM rows x 32 NW (gate/up) or 64 NW (down) columns and each weight
-// element is decoded by exactly one wave.  BK = K per stage: 128, or 256 so
-// that a weight row's codes of one stage fill a whole 128-byte line (its
-// next bytes are not left for a later stage, when another tile's lines may
-// have evicted the line from L2).
+// One tile: the tile's rows (rows <= 16 MSR) of NW waves, each owning 4
+// column subtiles of 16 (gate/up: 32 h columns as 32 gate + 32 up weight
+// rows; down: 64 output columns) for all 16 MSR rows, so the tile is
+// 16 MSR rows x 32 NW (gate/up) or 64 NW (down) columns and each weight
+// element is decoded by exactly one wave.  MSR is the number of 16-row
+// subtiles the tile's rows need: a tile of an expert with 20 rows issues half
+// the MFMAs and activation-fragment reads of a full 64-row tile.  BK = K per
+// stage: 128, or 256 so that a weight row's codes of one stage fill a whole
+// 128-byte line (its next bytes are not left for a later stage, when another
+// tile's lines may have evicted the line from L2).
+template <bool GATEUP, int BK, int NW, int MSR>
+__device__ __forceinline__ void grouped_tile(const GemmParams& P, uint8_t* smem, int e, int nt, int p0, int rows) {
+    constexpr int kThreads = NW * kWave;
+    constexpr int NS = 4;                       // column subtiles per wave
+    constexpr int BN = (GATEUP ? 32 : 64) * NW; // output columns per tile
+    constexpr int kRows = 16 * MSR;             // rows staged and computed
+    constexpr int kLdsRow = BK * 2 + 16;        // bytes per staged activation row (padded)
+    constexpr int kRowChunks = BK * 2 / 16;     // 16-byte activation chunks per row per stage
+    constexpr int APT = kRows * kRowChunks / kThreads;   // activation chunks per thread per stage
+    constexpr int KSTEPS = BK / 32;             // MFMA k-steps per stage
+    constexpr int CW = BK / 128;                // 16-byte code words per lane per subtile per stage
+    static_assert(APT * kThreads == kRows * kRowChunks, "activation stage split over the threads");
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lcol = lane & 15, kq = lane >> 4;
+    const int nst = P.K / BK;
+
+    // activation chunks this thread stages: chunk c = tid + kThreads * i
+    // of the stage, row c / kRowChunks, 16-byte unit c % kRowChunks
+    int64_t a_off[APT];
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+        const int c = tid + kThreads * i;
+        const int r = c / kRowChunks;
+        int64_t off = -1;
+        if (r < rows) {
+            const int64_t src_row = GATEUP ? (int64_t)(P.sorted_slots[p0 + r] / P.topk) : (int64_t)(p0 + r);
+            off = src_row * P.K + (c % kRowChunks) * 8;
+        }
+        a_off[i] = off;
+    }
+    // weight rows of this wave's column subtiles
+    const uint8_t* cp[NS];
+    const uint8_t* sp[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+        int col;
+        const uint8_t *cb, *sb;
+        if (GATEUP) {
+            col = nt * BN + wave * 32 + (ns & 1) * 16 + lcol;
+            cb = ns < 2 ? P.c0 : P.c1;
+            sb = ns < 2 ? P.s0 : P.s1;
+        } else {
+            col = nt * BN + wave * 64 + ns * 16 + lcol;
+            cb = P.c0;
+            sb = P.s0;
+        }
+        const int64_t row = (int64_t)e * P.N + col;
+        cp[ns] = cb + row * (P.K / 2) + kq * 16 * CW;
+        sp[ns] = sb + row * (P.K / 16) + kq * 2 * CW;
+    }
+
+    floatx4 acc[MSR][NS];
+#pragma unroll
+    for (int i = 0; i < MSR; ++i)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    uint4 a_reg[APT];
+    uint4 b_code[NS][CW];
+    uint32_t b_scale[NS];
+    auto load_stage = [&](int st) {
+        const int k0 = st * BK;
+#pragma unroll
+        for (int i = 0; i < APT; ++i)
+            a_reg[i] = a_off[i] >= 0 ? *reinterpret_cast<const uint4*>(P.a + a_off[i] + k0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+#pragma unroll
+            for (int w = 0; w < CW; ++w) b_code[ns][w] = *reinterpret_cast<const uint4*>(cp[ns] + k0 / 2 + 16 * w);
+            if constexpr (CW == 1) b_scale[ns] = *reinterpret_cast<const uint16_t*>(sp[ns] + k0 / 16);
+            else b_scale[ns] = *reinterpret_cast<const uint32_t*>(sp[ns] + k0 / 16);
+        }
+    };
+    load_stage(0);
+    for (int st = 0; st < nst; ++st) {
+        uint8_t* buf = smem + (st & 1) * (kRows * kLdsRow);
+#pragma unroll
+        for (int i = 0; i < APT; ++i) {
+            const int c = tid + kThreads * i;
+            *reinterpret_cast<uint4*>(buf + (c / kRowChunks) * kLdsRow + (c % kRowChunks) * 16) = a_reg[i];
+        }
+        uint4 cur_code[NS][CW];
+        uint32_t cur_scale[NS];
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+#pragma unroll
+            for (int w = 0; w < CW; ++w) cur_code[ns][w] = b_code[ns][w];
+            cur_scale[ns] = b_scale[ns];
+        }
+        __syncthreads();
+        if (st + 1 < nst) load_stage(st + 1);
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+            bf16x8 bfrag[NS];
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) {
+                const uint4 cw4 = cur_code[ns][s >> 2];
+                const int sw = s & 3;
+                const uint32_t word = sw == 0 ? cw4.x : sw == 1 ? cw4.y : sw == 2 ? cw4.z : cw4.w;
+                // the group of k-step s: byte s / 2 of the lane's scale word
+                const int sb = s >> 1;
+                const float sc = sb == 0 ? e4m3_byte_to_f32<0>(cur_scale[ns])
+                               : sb == 1 ? e4m3_byte_to_f32<1>(cur_scale[ns])
+                               : sb == 2 ? e4m3_byte_to_f32<2>(cur_scale[ns])
+                                         : e4m3_byte_to_f32<3>(cur_scale[ns]);
+                bfrag[ns] = decode8(word, sc);
+            }
+#pragma unroll
+            for (int ms = 0; ms < MSR; ++ms) {
+                const bf16x8 afrag =
+                    *reinterpret_cast<const bf16x8*>(buf + (ms * 16 + lcol) * kLdsRow + kq * 64 * CW + s * 16);
+#pragma unroll
+                for (int ns = 0; ns < NS; ++ns)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[ns], acc[ms][ns], 0, 0, 0);
+            }
+        }
+    }
+
+    // epilogue: lane holds rows 4*kq + i (i < 4) of each 16-row subtile, column lcol
+    if (GATEUP) {
+        const float gg = P.g0[e] * P.gmul, gu = P.g1[e] * P.gmul;
+        uint16_t* h = reinterpret_cast<uint16_t*>(P.out);
+#pragma unroll
+        for (int ms = 0; ms < MSR; ++ms)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = ms * 16 + kq * 4 + i;
+                if (r < rows) {
+#pragma unroll
+                    for (int ns = 0; ns < 2; ++ns) {
+                        const float a = gg * acc[ms][ns][i];
+                        const float b = gu * acc[ms][ns + 2][i];
+                        const int col = nt * BN + wave * 32 + ns * 16 + lcol;
+                        const int64_t idx = (int64_t)(p0 + r) * P.N + col;
+                        const float v = silu(a) * b;
+                        if (P.hf) P.hf[idx] = v;
+                        else h[idx] = f32_to_bf16_rne(v);
+                    }
+                }
+            }
+    } else {
+        const float gd = P.g0[e] * P.gmul;
+        uint16_t* y = reinterpret_cast<uint16_t*>(P.out);
+#pragma unroll
+        for (int ms = 0; ms < MSR; ++ms)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = ms * 16 + kq * 4 + i;
+                if (r < rows) {
+#pragma unroll
+                    for (int ns = 0; ns < NS; ++ns) {
+                        const int col = nt * BN + wave * 64 + ns * 16 + lcol;
+                        y[(int64_t)(p0 + r) * P.N + col] = f32_to_bf16_rne(gd * acc[ms][ns][i]);
+                    }
+                }
+            }
+    }
+}
+
+// Persistent grouped GEMM over tiles of up to BM rows (each computed by
+// grouped_tile with the row subtiles its rows need).
 template <bool GATEUP, int BM, int BK, int NW>
 __global__ void __launch_bounds__(NW * kWave, (gemm_wg_per_cu<BM, NW>())) k_grouped_gemm(GemmParams P) {
     constexpr int kThreads = NW * kWave;
-    constexpr int MS = BM / 16;                 // row subtiles
-    constexpr int NS = 4;                       // column subtiles per wave
-    constexpr int BN = (GATEUP ? 32 : 64) * NW; // output columns per tile
-    constexpr int kLdsRow = BK * 2 + 16;        // bytes per staged activation row (padded)
-    constexpr int kRowChunks = BK * 2 / 16;     // 16-byte activation chunks per row per stage
-    constexpr int APT = BM * kRowChunks / kThreads;   // activation chunks per thread per stage
-    constexpr int KSTEPS = BK / 32;             // MFMA k-steps per stage
-    constexpr int CW = BK / 128;                // 16-byte code words per lane per subtile per stage
-    static_assert(APT * kThreads == BM * kRowChunks, "activation stage split over the threads");
+    constexpr int MS = BM / 16;                 // row subtiles of a full tile
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_prefix[MOE_MAX_EXPERTS + 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lcol = lane & 15, kq = lane >> 4;
 
     // tiles per expert -> exclusive prefix (wave 0, DPP scan over lane runs)
     for (int e = tid; e < P.E; e += kThreads) s_prefix[e] = ((P.counts[e] + BM - 1) / BM) * P.ntn;
@@ -124,7 +280,6 @@ __global__ void __launch_bounds__(NW * kWave, (gemm_wg_per_cu<BM, NW>())) k_grou
     const int G = gridDim.x;
     const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
     const bool remap = (G & 7) == 0;
-    const int nst = P.K / BK;
 
     for (int it = 0;; ++it) {
         const int tile = it * G + (remap ? xcd * (G >> 3) + q : (int)blockIdx.x);
@@ -135,7 +290,7 @@ __global__ void __launch_bounds__(NW * kWave, (gemm_wg_per_cu<BM, NW>())) k_grou
             const int mid = (lo + hi + 1) >> 1;
             if (s_prefix[mid] <= tile) lo = mid; else hi = mid - 1;
         }
-        const int e = lo;
+        const int e = __builtin_amdgcn_readfirstlane(lo);
         const int L = tile - s_prefix[e];
         const int ne = P.counts[e];
         const int mte = (ne + BM - 1) / BM;
@@ -150,150 +305,14 @@ __global__ void __launch_bounds__(NW * kWave, (gemm_wg_per_cu<BM, NW>())) k_grou
             nt = r / last;
             mt = full * kMGroup + r % last;
         }
-        const int p0 = P.offsets[e] + mt * BM;
-        const int rows = min(BM, ne - mt * BM);
-
-        // activation chunks this thread stages: chunk c = tid + kThreads * i
-        // of the stage, row c / kRowChunks, 16-byte unit c % kRowChunks
-        int64_t a_off[APT];
-#pragma unroll
-        for (int i = 0; i < APT; ++i) {
-            const int c = tid + kThreads * i;
-            const int r = c / kRowChunks;
-            int64_t off = -1;
-            if (r < rows) {
-                const int64_t src_row = GATEUP ? (int64_t)(P.sorted_slots[p0 + r] / P.topk) : (int64_t)(p0 + r);
-                off = src_row * P.K + (c % kRowChunks) * 8;
-            }
-            a_off[i] = off;
-        }
-        // weight rows of this wave's column subtiles
-        const uint8_t* cp[NS];
-        const uint8_t* sp[NS];
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
-            int col;
-            const uint8_t *cb, *sb;
-            if (GATEUP) {
-                col = nt * BN + wave * 32 + (ns & 1) * 16 + lcol;
-                cb = ns < 2 ? P.c0 : P.c1;
-                sb = ns < 2 ? P.s0 : P.s1;
-            } else {
-                col = nt * BN + wave * 64 + ns * 16 + lcol;
-                cb = P.c0;
-                sb = P.s0;
-            }
-            const int64_t row = (int64_t)e * P.N + col;
-            cp[ns] = cb + row * (P.K / 2) + kq * 16 * CW;
-            sp[ns] = sb + row * (P.K / 16) + kq * 2 * CW;
-        }
-
-        floatx4 acc[MS][NS];
-#pragma unroll
-        for (int i = 0; i < MS; ++i)
-#pragma unroll
-            for (int j = 0; j < NS; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-        uint4 a_reg[APT];
-        uint4 b_code[NS][CW];
-        uint32_t b_scale[NS];
-        auto load_stage = [&](int st) {
-            const int k0 = st * BK;
-#pragma unroll
-            for (int i = 0; i < APT; ++i)
-                a_reg[i] = a_off[i] >= 0 ? *reinterpret_cast<const uint4*>(P.a + a_off[i] + k0) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int ns = 0; ns < NS; ++ns) {
-#pragma unroll
-                for (int w = 0; w < CW; ++w) b_code[ns][w] = *reinterpret_cast<const uint4*>(cp[ns] + k0 / 2 + 16 * w);
-                if constexpr (CW == 1) b_scale[ns] = *reinterpret_cast<const uint16_t*>(sp[ns] + k0 / 16);
-                else b_scale[ns] = *reinterpret_cast<const uint32_t*>(sp[ns] + k0 / 16);
-            }
-        };
-        load_stage(0);
-        for (int st = 0; st < nst; ++st) {
-            uint8_t* buf = smem + (st & 1) * (BM * kLdsRow);
-#pragma unroll
-            for (int i = 0; i < APT; ++i) {
-                const int c = tid + kThreads * i;
-                *reinterpret_cast<uint4*>(buf + (c / kRowChunks) * kLdsRow + (c % kRowChunks) * 16) = a_reg[i];
-            }
-            uint4 cur_code[NS][CW];
-            uint32_t cur_scale[NS];
-#pragma unroll
-            for (int ns = 0; ns < NS; ++ns) {
-#pragma unroll
-                for (int w = 0; w < CW; ++w) cur_code[ns][w] = b_code[ns][w];
-                cur_scale[ns] = b_scale[ns];
-            }
-            __syncthreads();
-            if (st + 1 < nst) load_stage(st + 1);
-#pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                bf16x8 bfrag[NS];
-#pragma unroll
-                for (int ns = 0; ns < NS; ++ns) {
-                    const uint4 cw4 = cur_code[ns][s >> 2];
-                    const int sw = s & 3;
-                    const uint32_t word = sw == 0 ? cw4.x : sw == 1 ? cw4.y : sw == 2 ? cw4.z : cw4.w;
-                    // the group of k-step s: byte s / 2 of the lane's scale word
-                    const int sb = s >> 1;
-                    const float sc = sb == 0 ? e4m3_byte_to_f32<0>(cur_scale[ns])
-                                   : sb == 1 ? e4m3_byte_to_f32<1>(cur_scale[ns])
-                                   : sb == 2 ? e4m3_byte_to_f32<2>(cur_scale[ns])
-                                             : e4m3_byte_to_f32<3>(cur_scale[ns]);
-                    bfrag[ns] = decode8(word, sc);
-                }
-#pragma unroll
-                for (int ms = 0; ms < MS; ++ms) {
-                    const bf16x8 afrag =
-                        *reinterpret_cast<const bf16x8*>(buf + (ms * 16 + lcol) * kLdsRow + kq * 64 * CW + s * 16);
-#pragma unroll
-                    for (int ns = 0; ns < NS; ++ns)
-                        acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[ns], acc[ms][ns], 0, 0, 0);
-                }
-            }
-        }
-
-        // epilogue: lane holds rows 4*kq + i (i < 4) of each 16-row subtile, column lcol
-        if (GATEUP) {
-            const float gg = P.g0[e] * P.gmul, gu = P.g1[e] * P.gmul;
-            uint16_t* h = reinterpret_cast<uint16_t*>(P.out);
-#pragma unroll
-            for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = ms * 16 + kq * 4 + i;
-                    if (r < rows) {
-#pragma unroll
-                        for (int ns = 0; ns < 2; ++ns) {
-                            const float a = gg * acc[ms][ns][i];
-                            const float b = gu * acc[ms][ns + 2][i];
-                            const int col = nt * BN + wave * 32 + ns * 16 + lcol;
-                            const int64_t idx = (int64_t)(p0 + r) * P.N + col;
-                            const float v = silu(a) * b;
-                            if (P.hf) P.hf[idx] = v;
-                            else h[idx] = f32_to_bf16_rne(v);
-                        }
-                    }
-                }
-        } else {
-            const float gd = P.g0[e] * P.gmul;
-            uint16_t* y = reinterpret_cast<uint16_t*>(P.out);
-#pragma unroll
-            for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = ms * 16 + kq * 4 + i;
-                    if (r < rows) {
-#pragma unroll
-                        for (int ns = 0; ns < NS; ++ns) {
-                            const int col = nt * BN + wave * 64 + ns * 16 + lcol;
-                            y[(int64_t)(p0 + r) * P.N + col] = f32_to_bf16_rne(gd * acc[ms][ns][i]);
-                        }
-                    }
-                }
-        }
+        nt = __builtin_amdgcn_readfirstlane(nt);
+        const int p0 = __builtin_amdgcn_readfirstlane(P.offsets[e] + mt * BM);
+        const int rows = __builtin_amdgcn_readfirstlane(min(BM, ne - mt * BM));
+        // the tile's 16-row subtiles: half, three quarters or all of BM
+        const int need = (rows + 15) >> 4;
+        if (need <= MS / 2) grouped_tile<GATEUP, BK, NW, MS / 2>(P, smem, e, nt, p0, rows);
+        else if (need <= 3 * MS / 4) grouped_tile<GATEUP, BK, NW, 3 * MS / 4>(P, smem, e, nt, p0, rows);
+        else grouped_tile<GATEUP, BK, NW, MS>(P, smem, e, nt, p0, rows);
         __syncthreads();   // LDS buffers are rewritten by the next tile
     }
 }
