@@ -177,29 +177,50 @@ __device__ __forceinline__ void grouped_tile(const GemmParams& P, uint8_t* smem,
         }
         __syncthreads();
         if (st + 1 < nst) load_stage(st + 1);
+        // decoded weights of subtile ns at k-step s (8 codes times their
+        // group's E4M3 scale, exact in bf16)
+        auto decode_sub = [&](int ns, int s) {
+            const uint4 cw4 = cur_code[ns][s >> 2];
+            const int sw = s & 3;
+            const uint32_t word = sw == 0 ? cw4.x : sw == 1 ? cw4.y : sw == 2 ? cw4.z : cw4.w;
+            // the group of k-step s: byte s / 2 of the lane's scale word
+            const int sb = s >> 1;
+            const float sc = sb == 0 ? e4m3_byte_to_f32<0>(cur_scale[ns])
+                           : sb == 1 ? e4m3_byte_to_f32<1>(cur_scale[ns])
+                           : sb == 2 ? e4m3_byte_to_f32<2>(cur_scale[ns])
+                                     : e4m3_byte_to_f32<3>(cur_scale[ns]);
+            return decode8(word, sc);
+        };
+        auto read_frag = [&](int ms, int s) {
+            return *reinterpret_cast<const bf16x8*>(buf + (ms * 16 + lcol) * kLdsRow + kq * 64 * CW + s * 16);
+        };
+        // Each subtile's MFMAs are interleaved with the decode of the next
+        // subtile (the last one's with the next k-step's first), and the next
+        // k-step's activation fragments are read during this one's MFMAs, so
+        // the matrix pipe of a SIMD and its vector ALU work at the same time.
+        bf16x8 af[2][MSR];
+#pragma unroll
+        for (int ms = 0; ms < MSR; ++ms) af[0][ms] = read_frag(ms, 0);
+        bf16x8 bnext = decode_sub(0, 0);
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-            bf16x8 bfrag[NS];
 #pragma unroll
             for (int ns = 0; ns < NS; ++ns) {
-                const uint4 cw4 = cur_code[ns][s >> 2];
-                const int sw = s & 3;
-                const uint32_t word = sw == 0 ? cw4.x : sw == 1 ? cw4.y : sw == 2 ? cw4.z : cw4.w;
-                // the group of k-step s: byte s / 2 of the lane's scale word
-                const int sb = s >> 1;
-                const float sc = sb == 0 ? e4m3_byte_to_f32<0>(cur_scale[ns])
-                               : sb == 1 ? e4m3_byte_to_f32<1>(cur_scale[ns])
-                               : sb == 2 ? e4m3_byte_to_f32<2>(cur_scale[ns])
-                                         : e4m3_byte_to_f32<3>(cur_scale[ns]);
-                bfrag[ns] = decode8(word, sc);
-            }
+                const bf16x8 bf = bnext;
+                if (ns + 1 < NS) bnext = decode_sub(ns + 1, s);
+                else if (s + 1 < KSTEPS) bnext = decode_sub(0, s + 1);
 #pragma unroll
-            for (int ms = 0; ms < MSR; ++ms) {
-                const bf16x8 afrag =
-                    *reinterpret_cast<const bf16x8*>(buf + (ms * 16 + lcol) * kLdsRow + kq * 64 * CW + s * 16);
+                for (int ms = 0; ms < MSR; ++ms)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s & 1][ms], bf, acc[ms][ns], 0, 0, 0);
 #pragma unroll
-                for (int ns = 0; ns < NS; ++ns)
-                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[ns], acc[ms][ns], 0, 0, 0);
+                for (int i = 0; i < MSR; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 18 / MSR, 0);       // VALU
+                }
+                if (ns == 1 && s + 1 < KSTEPS) {
+#pragma unroll
+                    for (int ms = 0; ms < MSR; ++ms) af[(s + 1) & 1][ms] = read_frag(ms, s + 1);
+                }
             }
         }
     }
