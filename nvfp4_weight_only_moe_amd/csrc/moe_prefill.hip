@@ -401,19 +401,21 @@ moe_status launch_gemm(GemmParams P, int64_t slots, int E, hipStream_t s) {
 // per row tile, so tiles that hold a whole typical expert pay off even with
 // padding: at 1K tokens, top-8 of 256 (about 32 rows per expert, many with
 // 33-45) 64-row tiles take the layer from 1.61 to 1.32 ms against 32-row
-// tiles; 128-row tiles (one workgroup per CU) take 2.38 ms.  The gate/up
-// product's 64-row tiles use eight waves (twice the columns per tile, half
-// the re-reads of the gathered activation rows) and 256-wide K stages (whole
-// 128-byte weight lines per stage) where the shape allows.  Measured on
-// MI355X at 1K tokens (gate/up, down): four waves with 128-wide stages 840 /
-// 370 us, eight waves 843 / 438 us, eight waves with 256-wide stages 779 /
-// 406 us -- so gate/up takes the last and down keeps four waves.
+// tiles; 128-row tiles (one workgroup per CU) take 2.38 ms.  The 64-row
+// tiles use eight waves (twice the columns per tile, half the re-reads of
+// the gathered activation rows) and 256-wide K stages (whole 128-byte weight
+// lines per stage) where the shape allows.  Measured on MI355X at 1K tokens
+// with tiles cut to their rows' subtiles and the decode interleaved with the
+// MFMAs: gate/up 615 us with eight waves and 256-wide stages (four waves:
+// 704 us, or 789 us with 128-wide stages), down 325 us (four waves with
+// 128-wide stages: 357 us).
 template <bool GATEUP>
 moe_status launch_gemm_bm(const GemmParams& P, int64_t slots, int E, hipStream_t s) {
     const int64_t avg = slots / std::max<int64_t>(1, std::min<int64_t>(E, slots));
     if (avg <= 16) return launch_gemm<GATEUP, 32, 128, 4>(P, slots, E, s);
     if (avg <= 64) {
         if (GATEUP && P.K % 256 == 0 && P.N % 256 == 0) return launch_gemm<true, 64, 256, 8>(P, slots, E, s);
+        if (!GATEUP && P.K % 256 == 0 && P.N % 512 == 0) return launch_gemm<false, 64, 256, 8>(P, slots, E, s);
         return launch_gemm<GATEUP, 64, 128, 4>(P, slots, E, s);
     }
     return launch_gemm<GATEUP, 128, 128, 4>(P, slots, E, s);
