@@ -86,7 +86,8 @@ template <int BM, int NW> constexpr int gemm_wg_per_cu() {
 // 128-byte line (its next bytes are not left for a later stage, when another
 // tile's lines may have evicted the line from L2).
 template <bool GATEUP, int BK, int NW, int MSR>
-__device__ __forceinline__ void grouped_tile(const GemmParams& P, uint8_t* smem, int e, int nt, int p0, int rows) {
+__device__ __forceinline__ void grouped_tile(const GemmParams& P, uint8_t* smem, uint8_t* sscale, int e, int nt,
+                                             int p0, int rows) {
     constexpr int kThreads = NW * kWave;
     constexpr int NS = 4;                       // column subtiles per wave
     constexpr int BN = (GATEUP ? 32 : 64) * NW; // output columns per tile
@@ -96,7 +97,19 @@ __device__ __forceinline__ void grouped_tile(const GemmParams& P, uint8_t* smem,
     constexpr int APT = kRows * kRowChunks / kThreads;   // activation chunks per thread per stage
     constexpr int KSTEPS = BK / 32;             // MFMA k-steps per stage
     constexpr int CW = BK / 128;                // 16-byte code words per lane per subtile per stage
+    // Scales through LDS (eight-wave tiles): each weight row's E4M3 bytes of
+    // SB stages (64 bytes) go to LDS by LDS-DMA as four 16-byte pieces, the
+    // next block while the current one is used; a lane then reads its scale
+    // word of a stage from LDS.  Loaded straight from memory instead, every
+    // stage costs each lane one 2- or 4-byte load per subtile, 16 rows of 16
+    // bytes per wave instruction: at 1K tokens those loads alone took ~145 of
+    // the gate/up kernel's ~570 us of loads and staging.
+    constexpr bool SDMA = NW == 8;
+    constexpr int SB = 1024 / BK;               // stages per scale block (64 bytes of a row)
+    constexpr int kSRows = 64 * NW;             // weight rows of the tile
+    constexpr int kSBlock = kSRows * 64;        // bytes per scale block
     static_assert(APT * kThreads == kRows * kRowChunks, "activation stage split over the threads");
+    static_assert(!SDMA || kSRows * 4 == 4 * kThreads, "four 16-byte scale pieces per thread per block");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lcol = lane & 15, kq = lane >> 4;
@@ -143,6 +156,38 @@ __device__ __forceinline__ void grouped_tile(const GemmParams& P, uint8_t* smem,
 #pragma unroll
         for (int j = 0; j < NS; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    // scale block b -> LDS buffer b & 1: piece c = tid + kThreads i is bytes
+    // 16 (c % 4) .. + 15 of the block in tile weight row c / 4 (gate/up:
+    // rows [0, BN) of the gate matrix, then [BN, 2 BN) of the up matrix), so
+    // each wave instruction fills 1 KiB of LDS in order (lane j at + 16 j)
+    auto load_scale_block = [&](int b) {
+        if constexpr (SDMA) {
+            uint8_t* dst = sscale + (b & 1) * kSBlock;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = tid + kThreads * i;
+                const int r = c >> 2, boff = b * 64 + (c & 3) * 16;
+                const uint8_t* sb;
+                int64_t row;
+                if (GATEUP) {
+                    sb = r < BN ? P.s0 : P.s1;
+                    row = (int64_t)e * P.N + nt * BN + (r < BN ? r : r - BN);
+                } else {
+                    sb = P.s0;
+                    row = (int64_t)e * P.N + nt * BN + r;
+                }
+                if (boff < P.K / 16)       // whole pieces: K % 256 == 0 on this path
+                    lds_dma16(sb + row * (P.K / 16) + boff, (lds_void*)(dst + (c - lane) * 16));
+            }
+        }
+    };
+    // this lane's scale row in the block, per subtile
+    int s_lds[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+        const int r = GATEUP ? (ns < 2 ? 0 : BN) + wave * 32 + (ns & 1) * 16 + lcol : wave * 64 + ns * 16 + lcol;
+        s_lds[ns] = r * 64 + kq * 2 * CW;
+    }
     uint4 a_reg[APT];
     uint4 b_code[NS][CW];
     uint32_t b_scale[NS];
@@ -155,10 +200,14 @@ __device__ __forceinline__ void grouped_tile(const GemmParams& P, uint8_t* smem,
         for (int ns = 0; ns < NS; ++ns) {
 #pragma unroll
             for (int w = 0; w < CW; ++w) b_code[ns][w] = *reinterpret_cast<const uint4*>(cp[ns] + k0 / 2 + 16 * w);
-            if constexpr (CW == 1) b_scale[ns] = *reinterpret_cast<const uint16_t*>(sp[ns] + k0 / 16);
-            else b_scale[ns] = *reinterpret_cast<const uint32_t*>(sp[ns] + k0 / 16);
+            if constexpr (!SDMA) {
+                if constexpr (CW == 1) b_scale[ns] = *reinterpret_cast<const uint16_t*>(sp[ns] + k0 / 16);
+                else b_scale[ns] = *reinterpret_cast<const uint32_t*>(sp[ns] + k0 / 16);
+            }
         }
     };
+    // block 0 before stage 0's loads: waiting for those (in order) covers it
+    load_scale_block(0);
     load_stage(0);
     for (int st = 0; st < nst; ++st) {
         uint8_t* buf = smem + (st & 1) * (kRows * kLdsRow);
@@ -173,9 +222,22 @@ __device__ __forceinline__ void grouped_tile(const GemmParams& P, uint8_t* smem,
         for (int ns = 0; ns < NS; ++ns) {
 #pragma unroll
             for (int w = 0; w < CW; ++w) cur_code[ns][w] = b_code[ns][w];
-            cur_scale[ns] = b_scale[ns];
+            if constexpr (!SDMA) cur_scale[ns] = b_scale[ns];
         }
         __syncthreads();
+        if constexpr (SDMA) {
+            // this stage's scale words; at a block's first stage the next
+            // block's DMA goes out ahead of the next stage's loads (the
+            // wave's wait for those loads, in order, covers the DMA, and
+            // the barrier of the next block's first stage publishes it)
+            const int b = st / SB, j = st - b * SB;
+            const uint8_t* blk = sscale + (b & 1) * kSBlock + j * (BK / 16);
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns)
+                cur_scale[ns] = CW == 1 ? (uint32_t) * reinterpret_cast<const uint16_t*>(blk + s_lds[ns])
+                                        : *reinterpret_cast<const uint32_t*>(blk + s_lds[ns]);
+            if (j == 0 && (b + 1) * SB < nst) load_scale_block(b + 1);
+        }
         if (st + 1 < nst) load_stage(st + 1);
         // decoded weights of subtile ns at k-step s (8 codes times their
         // group's E4M3 scale, exact in bf16)
@@ -331,9 +393,10 @@ __global__ void __launch_bounds__(NW * kWave, (gemm_wg_per_cu<BM, NW>())) k_grou
         const int rows = __builtin_amdgcn_readfirstlane(min(BM, ne - mt * BM));
         // the tile's 16-row subtiles: half, three quarters or all of BM
         const int need = (rows + 15) >> 4;
-        if (need <= MS / 2) grouped_tile<GATEUP, BK, NW, MS / 2>(P, smem, e, nt, p0, rows);
-        else if (need <= 3 * MS / 4) grouped_tile<GATEUP, BK, NW, 3 * MS / 4>(P, smem, e, nt, p0, rows);
-        else grouped_tile<GATEUP, BK, NW, MS>(P, smem, e, nt, p0, rows);
+        uint8_t* sscale = smem + 2 * BM * (BK * 2 + 16);   // after the activation buffers
+        if (need <= MS / 2) grouped_tile<GATEUP, BK, NW, MS / 2>(P, smem, sscale, e, nt, p0, rows);
+        else if (need <= 3 * MS / 4) grouped_tile<GATEUP, BK, NW, 3 * MS / 4>(P, smem, sscale, e, nt, p0, rows);
+        else grouped_tile<GATEUP, BK, NW, MS>(P, smem, sscale, e, nt, p0, rows);
         __syncthreads();   // LDS buffers are rewritten by the next tile
     }
 }
@@ -388,7 +451,8 @@ moe_status launch_gemm(GemmParams P, int64_t slots, int E, hipStream_t s) {
     constexpr int BN = (GATEUP ? 32 : 64) * NW;
     P.ntn = P.N / BN;
     const int64_t tiles_ub = (slots / BM + std::min<int64_t>(E, slots)) * P.ntn;
-    const size_t shmem = 2 * BM * (BK * 2 + 16);
+    // activation double buffer, then (eight waves) the scale blocks' double buffer
+    const size_t shmem = 2 * BM * (BK * 2 + 16) + (NW == 8 ? 2 * 64 * NW * 64 : 0);
     auto kern = &k_grouped_gemm<GATEUP, BM, BK, NW>;
     if (allow_dynamic_lds(reinterpret_cast<const void*>(kern), shmem) != MOE_OK) return MOE_ERR_HIP;
     const char* name = GATEUP ? "gemm_gateup" : "gemm_down";
