@@ -85,7 +85,7 @@ template <int BM, int NW> constexpr int gemm_wg_per_cu() {
 // stage: 128, or 256 so that a weight row's codes of one stage fill a whole
 // 128-byte line (its next bytes are not left for a later stage, when another
 // tile's lines may have evicted the line from L2).
-template <bool GATEUP, int BK, int NW, int MSR>
+template <bool GATEUP, int BK, int NW, bool SDMA, int MSR>
 __device__ __forceinline__ void grouped_tile(const GemmParams& P, uint8_t* smem, uint8_t* sscale, int e, int nt,
                                              int p0, int rows) {
     constexpr int kThreads = NW * kWave;
@@ -97,14 +97,13 @@ __device__ __forceinline__ void grouped_tile(const GemmParams& P, uint8_t* smem,
     constexpr int APT = kRows * kRowChunks / kThreads;   // activation chunks per thread per stage
     constexpr int KSTEPS = BK / 32;             // MFMA k-steps per stage
     constexpr int CW = BK / 128;                // 16-byte code words per lane per subtile per stage
-    // Scales through LDS (eight-wave tiles): each weight row's E4M3 bytes of
+    // Scales through LDS (SDMA, when K % 256 == 0): each weight row's E4M3 bytes of
     // SB stages (64 bytes) go to LDS by LDS-DMA as four 16-byte pieces, the
     // next block while the current one is used; a lane then reads its scale
     // word of a stage from LDS.  Loaded straight from memory instead, every
     // stage costs each lane one 2- or 4-byte load per subtile, 16 rows of 16
     // bytes per wave instruction: at 1K tokens those loads alone took ~145 of
     // the gate/up kernel's ~570 us of loads and staging.
-    constexpr bool SDMA = NW == 8;
     constexpr int SB = 1024 / BK;               // stages per scale block (64 bytes of a row)
     constexpr int kSRows = 64 * NW;             // weight rows of the tile
     constexpr int kSBlock = kSRows * 64;        // bytes per scale block
@@ -330,7 +329,7 @@ __device__ __forceinline__ void grouped_tile(const GemmParams& P, uint8_t* smem,
 
 // Persistent grouped GEMM over tiles of up to BM rows (each computed by
 // grouped_tile with the row subtiles its rows need).
-template <bool GATEUP, int BM, int BK, int NW>
+template <bool GATEUP, int BM, int BK, int NW, bool SDMA>
 __global__ void __launch_bounds__(NW * kWave, (gemm_wg_per_cu<BM, NW>())) k_grouped_gemm(GemmParams P) {
     constexpr int kThreads = NW * kWave;
     constexpr int MS = BM / 16;                 // row subtiles of a full tile
@@ -394,9 +393,9 @@ __global__ void __launch_bounds__(NW * kWave, (gemm_wg_per_cu<BM, NW>())) k_grou
         // the tile's 16-row subtiles: half, three quarters or all of BM
         const int need = (rows + 15) >> 4;
         uint8_t* sscale = smem + 2 * BM * (BK * 2 + 16);   // after the activation buffers
-        if (need <= MS / 2) grouped_tile<GATEUP, BK, NW, MS / 2>(P, smem, sscale, e, nt, p0, rows);
-        else if (need <= 3 * MS / 4) grouped_tile<GATEUP, BK, NW, 3 * MS / 4>(P, smem, sscale, e, nt, p0, rows);
-        else grouped_tile<GATEUP, BK, NW, MS>(P, smem, sscale, e, nt, p0, rows);
+        if (need <= MS / 2) grouped_tile<GATEUP, BK, NW, SDMA, MS / 2>(P, smem, sscale, e, nt, p0, rows);
+        else if (need <= 3 * MS / 4) grouped_tile<GATEUP, BK, NW, SDMA, 3 * MS / 4>(P, smem, sscale, e, nt, p0, rows);
+        else grouped_tile<GATEUP, BK, NW, SDMA, MS>(P, smem, sscale, e, nt, p0, rows);
         __syncthreads();   // LDS buffers are rewritten by the next tile
     }
 }
@@ -446,19 +445,32 @@ int persistent_grid(int64_t tiles_ub, int per_cu = 2) {
     return (int)std::max<int64_t>(g, 1);
 }
 
-template <bool GATEUP, int BM, int BK, int NW>
-moe_status launch_gemm(GemmParams P, int64_t slots, int E, hipStream_t s) {
+// Scales through LDS where a row's scale bytes split into whole 16-byte
+// pieces (K % 256 == 0) and the LDS allows: every tile height but 32 rows,
+// whose three workgroups per CU would not fit the scale blocks beside their
+// activation buffers.
+template <int BM> constexpr bool gemm_sdma_fits() { return BM >= 64; }
+
+template <bool GATEUP, int BM, int BK, int NW, bool SDMA>
+moe_status launch_gemm_s(GemmParams P, int64_t slots, int E, hipStream_t s) {
     constexpr int BN = (GATEUP ? 32 : 64) * NW;
     P.ntn = P.N / BN;
     const int64_t tiles_ub = (slots / BM + std::min<int64_t>(E, slots)) * P.ntn;
-    // activation double buffer, then (eight waves) the scale blocks' double buffer
-    const size_t shmem = 2 * BM * (BK * 2 + 16) + (NW == 8 ? 2 * 64 * NW * 64 : 0);
-    auto kern = &k_grouped_gemm<GATEUP, BM, BK, NW>;
+    // activation double buffer, then the scale blocks' double buffer
+    const size_t shmem = 2 * BM * (BK * 2 + 16) + (SDMA ? 2 * 64 * NW * 64 : 0);
+    auto kern = &k_grouped_gemm<GATEUP, BM, BK, NW, SDMA>;
     if (allow_dynamic_lds(reinterpret_cast<const void*>(kern), shmem) != MOE_OK) return MOE_ERR_HIP;
     const char* name = GATEUP ? "gemm_gateup" : "gemm_down";
-    MOE_LAUNCH(name, (k_grouped_gemm<GATEUP, BM, BK, NW>), dim3(persistent_grid(tiles_ub, gemm_wg_per_cu<BM, NW>())),
-               dim3(NW * kWave), shmem, s, P);
+    MOE_LAUNCH(name, (k_grouped_gemm<GATEUP, BM, BK, NW, SDMA>),
+               dim3(persistent_grid(tiles_ub, gemm_wg_per_cu<BM, NW>())), dim3(NW * kWave), shmem, s, P);
     return MOE_OK;
+}
+
+template <bool GATEUP, int BM, int BK, int NW>
+moe_status launch_gemm(GemmParams P, int64_t slots, int E, hipStream_t s) {
+    if constexpr (gemm_sdma_fits<BM>())
+        if (P.K % 256 == 0) return launch_gemm_s<GATEUP, BM, BK, NW, true>(P, slots, E, s);
+    return launch_gemm_s<GATEUP, BM, BK, NW, false>(P, slots, E, s);
 }
 
 // Row tile by the mean rows per touched expert.  A weight tile is decoded once
