@@ -21,8 +21,10 @@ device copies of the packed layer so that the 256 MB Infinity Cache cannot
 serve the weights (a model has one such layer per MoE block); prefill
 workloads read all of a layer's touched experts (GBs) per step and use one.
 The timed region replays a HIP graph of `copies` consecutive steps at least
-10 times (more when --steps asks for more steps); "steps" is the number of
-steps actually timed and "step_spread" gives p10/p50/p90 over the replays.
+10 times (more when --steps asks for more steps; without --steps, 400 decode
+steps and 200 prefill steps after 40 and 20 warm-up steps); "steps" is the
+number of steps actually timed and "step_spread" gives p10/p50/p90 over the
+replays.
 
 Each workload also carries "roofline" (the dominant kernel, timed by HIP
 events that its own launches stamp, against the roofline that binds it) and
@@ -230,8 +232,8 @@ def bench_moe_config(args, cfg, base, cache):
     wl = wls.WORKLOADS[cfg]
     dev = "cuda:0"
     decode = wl.T <= 8
-    steps_req = args.steps or (400 if decode else 20)
-    warmup = args.warmup if args.warmup is not None else (40 if decode else 3)
+    steps_req = args.steps or (400 if decode else 200)
+    warmup = args.warmup if args.warmup is not None else (40 if decode else 20)
     copies = args.copies or (16 if decode else 1)
     layers = layer_copies(base, copies, cache)
     torch.cuda.synchronize()
@@ -630,8 +632,8 @@ def bench_single(args, wl):
     else:
         ws = torch.empty((B.lib().moe_w4a16_shared_expert_workspace_size(T, H, I),), dtype=torch.uint8, device=dev)
         step = lambda i: B.moe_w4a16_shared_expert(x_d, *sets[i % copies], out=out, ws=ws)
-    steps = args.steps or (400 if decode else 20)
-    warmup = args.warmup if args.warmup is not None else (40 if decode else 3)
+    steps = args.steps or (400 if decode else 200)
+    warmup = args.warmup if args.warmup is not None else (40 if decode else 20)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
