@@ -7,21 +7,24 @@
 // weight up to the FP32 global scale, which is applied once per output in
 // the epilogue.
 //
-// k_grouped_gemm<GATEUP, BM> computes, for every expert e and its rows of the
-// expert-sorted permutation (offsets[e] .. offsets[e+1]):
+// k_grouped_gemm<GATEUP, BM, BK, NW, SDMA> computes, for every expert e and
+// its rows of the expert-sorted permutation (offsets[e] .. offsets[e+1]):
 //   GATEUP: h[p, :] = bf16( silu(gg_e * x_t . G_e^T) * (gu_e * x_t . U_e^T) ),
 //           t = sorted_slots[p] / k          (rows gathered from x)
 //   DOWN:   y[p, :] = bf16(gd_e * h_p . D_e^T)
-// Workgroup tile: BM rows x 128 h-columns (GATEUP, gate and up together) or
-// BM rows x 256 columns (DOWN); 4 waves, each owning 4 column subtiles of 16
-// and all BM rows, so each weight element is decoded by exactly one wave.
-// The BM x 128 activation tile of a K stage is staged in LDS (double
-// buffered); weights stream from HBM straight into registers with 16-byte
-// loads and are decoded there.  MFMA: v_mfma_f32_16x16x32_bf16.
+// Workgroup tile: up to BM rows x 32 NW h-columns (GATEUP, gate and up
+// together) or x 64 NW columns (DOWN); NW waves (4 or 8), each owning 4
+// column subtiles of 16 and all the tile's rows, so each weight element is
+// decoded by exactly one wave; a tile computes only the 16-row subtiles its
+// rows need.  The activation tile of a K stage (BK = 128 or 256) is staged
+// in LDS (double buffered); weights stream from HBM straight into registers
+// with 16-byte loads and are decoded there; their E4M3 scales come through
+// LDS in blocks (SDMA).  MFMA: v_mfma_f32_16x16x32_bf16.
 //
-// The K order inside a 128-wide stage is permuted identically for both
-// operands (lane group q holds k = 32q + 8s .. 32q + 8s + 7 at step s), which
-// lets one 16-byte load feed a lane's weight codes for all four steps.
+// The K order inside a stage is permuted identically for both operands (in
+// each 128-wide part, lane group q holds k = 32q + 8s .. 32q + 8s + 7 at
+// step s), which lets one 16-byte load feed a lane's weight codes for four
+// steps.
 //
 // The grid is persistent; tiles are numbered expert by expert, within an
 // expert in groups of 8 row tiles x all column tiles, and handed out so that
