@@ -21,10 +21,9 @@
 // with 16-byte loads and are decoded there; their E4M3 scales come through
 // LDS in blocks (SDMA).  MFMA: v_mfma_f32_16x16x32_bf16.
 //
-// The K order inside a stage is permuted identically for both operands (in
-// each 128-wide part, lane group q holds k = 32q + 8s .. 32q + 8s + 7 at
-// step s), which lets one 16-byte load feed a lane's weight codes for four
-// steps.
+// The K order inside a stage is permuted identically for both operands
+// (lane group q holds k = (BK / 4) q + 8 s .. + 7 at k-step s), which lets
+// one 16-byte load feed a lane's weight codes for four k-steps.
 //
 // The grid is persistent; tiles are numbered expert by expert, within an
 // expert in groups of 8 row tiles x all column tiles, and handed out so that
