@@ -226,6 +226,7 @@ PREFILL_CASES = [
     (600, 2048, 1536, 8, 4, 95),     # longer K: the ring runs across tile boundaries
     (100, 512, 384, 16, 4, 96),      # I % 256 != 0: the register-staged kernels in every variant
     (700, 512, 256, 8, 4, 97),       # 350 rows per expert: variant 2 takes the LDS-pipelined kernels
+    (300, 512, 384, 4, 2, 98),       # 128-row tiles, I % 256 != 0: down without the LDS scale blocks
 ]
 
 
