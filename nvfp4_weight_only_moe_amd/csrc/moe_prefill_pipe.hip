@@ -206,7 +206,15 @@ __device__ __forceinline__ void stage_mfma(floatx4 (&acc)[MS][kNS], const uint8_
         for (int ns = 0; ns < kNS; ++ns) {
             const bf16x8 bf = bnext;
             const int nn = ns + 1 < kNS ? ns + 1 : 0;     // next subtile (of the next k-step after the last)
-            if (ks == 0 || ns + 1 < kNS) bnext = decode8s((ns + 1 < kNS ? ks : 1) ? cw[nn].y : cw[nn].x, sc[nn]);
+            if (ks == 0 || ns + 1 < kNS) {
+                bnext = decode8s((ns + 1 < kNS ? ks : 1) ? cw[nn].y : cw[nn].x, sc[nn]);
+                // keep the decode in this subtile's block: dma(p) below is a
+                // branch, and the compiler would otherwise sink the decode
+                // past it to its use, ahead of the next subtile's MFMAs
+                u32x4 pin = __builtin_bit_cast(u32x4, bnext);
+                asm volatile("" : "+v"(pin));
+                bnext = __builtin_bit_cast(bf16x8, pin);
+            }
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms)
                 acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][ms], bf, acc[ms][ns], 0, 0, 0);
