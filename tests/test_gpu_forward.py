@@ -154,6 +154,8 @@ DECODE_CASES = [
     (4, 2048, 1024, 32, 8, 72),
     (8, 1024, 1536, 8, 8, 73),       # k == E
     (8, 3072, 512, 300, 8, 74),      # E > 256: five logits per lane in the top-k
+    (1, 8192, 2048, 4, 2, 76),       # the largest decode shape: H = 8192, I = 2048
+    (8, 8192, 2048, 4, 3, 77),
 ]
 
 
