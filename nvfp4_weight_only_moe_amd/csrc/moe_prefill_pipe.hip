@@ -8,9 +8,9 @@
 // flop, and how the operands reach the matrix cores:
 //   * every operand of a K stage (BK = 64) -- the tile's 128 activation
 //     rows, the packed codes of its 512 weight columns and their E4M3 scales
-//     -- goes from memory straight to LDS with gfx950 LDS-DMA
-//     (global_load_lds), so no register holds data in flight and every wait
-//     is an explicit vmcnt;
+//     (those in blocks of four stages) -- goes from memory straight to LDS
+//     with gfx950 LDS-DMA (global_load_lds), so no register holds data in
+//     flight and every wait is an explicit vmcnt;
 //   * a ring of kStages stages keeps kStages - 1 stages in flight while one
 //     is computed, across tile boundaries (a workgroup walks its tiles as one
 //     sequence of (tile, stage) steps);
@@ -41,27 +41,35 @@ constexpr int kAhead = kStages - 1;             // stages in flight while one is
 // dozen): activation bytes of a stage and the ring layout depend on it
 template <int BM> constexpr int a_bytes() { return BM * kBK * 2; }   // 16 / 8 KiB activations
 constexpr int kBBytes = kBN * kBK / 2;          // 16 KiB codes
-constexpr int kSBytes = kBN * kBK / 16;         // 2 KiB scales
-template <int BM> constexpr int stage_bytes() { return a_bytes<BM>() + kBBytes + kSBytes; }
+// The E4M3 scales travel in blocks of kSBlk stages: 16 bytes of each weight
+// row (one 16-byte piece per lane), where one stage's 4 bytes per row would
+// cost the load path one request per row for 4 bytes.  Two block buffers: a
+// block is issued with its first stage, three stages ahead, when the buffer
+// it replaces (two blocks back) is no longer read.
+constexpr int kSBlk = 4;                        // stages per scale block
+constexpr int kSRowBytes = kSBlk * kBK / 16;    // 16 bytes of a row's scales per block
+constexpr int kSBlkBytes = kBN * kSRowBytes;    // 8 KiB
 // the ring is three rings, one per operand, so that every LDS read of a
 // stage is a per-stage base plus an immediate offset (all below 64 KiB)
 constexpr int kARing = 0;
 template <int BM> constexpr int b_ring() { return kStages * a_bytes<BM>(); }
 template <int BM> constexpr int s_ring() { return b_ring<BM>() + kStages * kBBytes; }
+template <int BM> constexpr int ring_bytes() { return s_ring<BM>() + 2 * kSBlkBytes; }
 constexpr int kMGroup = 8;                      // row tiles per scheduling group
 constexpr int64_t kPipeBM64MaxMeanRows = 96;    // mean rows per touched expert up to which tiles are 64 rows
 #ifndef MOE_PIPE_DMA_WAVES
 #define MOE_PIPE_DMA_WAVES 4
 #endif
 // Waves 0 .. kDmaWaves - 1 issue a stage's LDS-DMA operations: 1 KiB
-// activation and code runs, 256-byte scale runs.  With 4 (one per SIMD, the
+// activation, code and (every kSBlk stages) scale runs.  With 4 (one per SIMD, the
 // default) the other wave of each SIMD goes on with its MFMAs while its
 // partner issues; all 8 issuing measured 6 % slower on MI355X.
 constexpr int kDmaWaves = MOE_PIPE_DMA_WAVES;
 template <int BM> constexpr int a_dma() { return a_bytes<BM>() / 1024 / kDmaWaves; }
 constexpr int kBDma = kBBytes / 1024 / kDmaWaves;
-constexpr int kSDma = kSBytes / 256 / kDmaWaves;
-template <int BM> constexpr int ops_per_stage() { return a_dma<BM>() + kBDma + kSDma; }
+constexpr int kSDma = kSBlkBytes / 1024 / kDmaWaves;
+template <int BM> constexpr int ops_plain() { return a_dma<BM>() + kBDma; }   // a stage without a scale block
+template <int BM> constexpr int ops_per_stage() { return ops_plain<BM>() + kSDma; }
 constexpr int kDmaCols = kBN / kDmaWaves;       // weight columns one DMA wave brings in
 static_assert(a_dma<128>() * kDmaWaves * 1024 == a_bytes<128>() && a_dma<64>() * kDmaWaves * 1024 == a_bytes<64>() &&
               kBDma * 32 == kDmaCols && kSDma * 64 == kDmaCols && kNS == 4, "stage split over the waves");
@@ -148,17 +156,23 @@ __device__ __forceinline__ Tile pipe_tile(const PipeParams& P, const int* s_pref
     return d;
 }
 
-// A DMA wave waits until at most n (0 .. kAhead - 1 stages) of its
-// vector-memory operations are outstanding; then every wave meets at a
+// Before step g a DMA wave waits until only the operations of the steps
+// issued after g (0 .. kAhead - 1 of them) are outstanding -- a step whose
+// stage opens a scale block has kSDma more -- then every wave meets at a
 // workgroup barrier that also waits for its LDS reads (the ring slot about
 // to be refilled is no longer read).
 template <int BM>
-__device__ __forceinline__ void stage_barrier(bool dma_wave, int stages_after) {
+__device__ __forceinline__ void stage_barrier(bool dma_wave, int stages_after, int g) {
     if (dma_wave) {
-        switch (stages_after) {
-            case 0: wait_vmem_at_most<0>(); break;
-            case 1: wait_vmem_at_most<1 * ops_per_stage<BM>()>(); break;
-            default: wait_vmem_at_most<2 * ops_per_stage<BM>()>(); break;
+        constexpr int P = ops_plain<BM>(), S = kSDma;
+        const bool blk1 = ((g + 1) % kSBlk) == 0, blk2 = ((g + 2) % kSBlk) == 0;
+        if (stages_after == 0) wait_vmem_at_most<0>();
+        else if (stages_after == 1) {
+            if (blk1) wait_vmem_at_most<P + S>();
+            else wait_vmem_at_most<P>();
+        } else {
+            if (blk1 || blk2) wait_vmem_at_most<2 * P + S>();
+            else wait_vmem_at_most<2 * P>();
         }
     }
     wait_lds_barrier();
@@ -192,7 +206,7 @@ __device__ __forceinline__ void stage_mfma(floatx4 (&acc)[MS][kNS], const uint8_
 #pragma unroll
     for (int ns = 0; ns < kNS; ++ns) {
         cw[ns] = *reinterpret_cast<const uint2*>(bs + o.b + cb[ns] * 32);
-        sc[ns] = e4m3_to_f32(ss[o.s + cb[ns] * 4]);
+        sc[ns] = e4m3_to_f32(ss[o.s + cb[ns] * kSRowBytes]);
     }
     bf16x8 bnext = decode8s(cw[0].x, sc[0]);
     // activation fragments: k-step 0 now, k-step 1 in two halves during the
@@ -294,10 +308,10 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
     const uint8_t* b_base = nullptr;
     const uint8_t* s_base = nullptr;
     const uint32_t b_vo = (uint32_t)((lane >> 1) * (P.K / 2) + 16 * ((lane & 1) ^ ((lane >> 4) & 1)));
-    const uint32_t s_vo = (uint32_t)(lane * (P.K / 16));
+    const uint32_t s_vo = (uint32_t)(lane * (P.K / 16));   // scale row of the lane (16-byte piece)
     const int64_t b_step = (int64_t)32 * (P.K / 2), s_step = (int64_t)64 * (P.K / 16);
-    // next (tile, stage) to prefetch and its ring slot
-    int iss_j = 0, iss_st = 0, iss_slot = 0;
+    // next (tile, stage) to prefetch, its ring slot and its step index
+    int iss_j = 0, iss_st = 0, iss_slot = 0, iss_g = 0;
 
     // gate/up: the sorted-slot values of tile j into s_rows[buf] (two dword
     // DMAs by wave 0; lanes past the tile's rows read its first slot)
@@ -334,7 +348,8 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
 
     // the loads of the next (tile, stage) into its ring slot, by the DMA
     // waves: BEGIN sets up a new tile's sources, OP(p) issues op p (0 .. 3:
-    // activation runs, 4 .. 7: code runs, 8, 9: scale runs), END moves on
+    // activation runs, 4 .. 7: code runs, 8, 9: scale runs of the block
+    // that the stage opens, if it opens one), END moves on
 #define MOE_PIPE_BEGIN()                                                                        \
     do {                                                                                        \
         if (iss_st == 0) {                                                                      \
@@ -357,15 +372,17 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
             const int i_ = (p) - kADma;                                                         \
             lds_dma16_sv(b_base + (i_ * b_step + k0_ / 2), b_vo,                                \
                          (lds_void*)(ring + kBRing + iss_slot * kBBytes + (wave * kBDma + i_) * 1024)); \
-        } else {                                                                                \
+        } else if (iss_st % kSBlk == 0) {                                                       \
             const int i_ = (p) - kADma - kBDma;                                                 \
-            lds_dma4_sv(s_base + (i_ * s_step + k0_ / 16), s_vo,                                \
-                        (lds_void*)(ring + kSRing + iss_slot * kSBytes + (wave * kSDma + i_) * 256)); \
+            lds_dma16_sv(s_base + (i_ * s_step + k0_ / 16), s_vo,                               \
+                         (lds_void*)(ring + kSRing + ((iss_g / kSBlk) & 1) * kSBlkBytes +       \
+                                     (wave * kSDma + i_) * 1024));                              \
         }                                                                                       \
     } while (0)
 #define MOE_PIPE_END()                                                                          \
     do {                                                                                        \
         iss_slot = (iss_slot + 1) & (kStages - 1);                                              \
+        ++iss_g;                                                                                \
         if (++iss_st == nst) {                                                                  \
             iss_st = 0;                                                                         \
             ++iss_j;                                                                            \
@@ -396,7 +413,7 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
         lo.a[0] = lcol * 128 + 16 * ((2 * kq) ^ a_swz(lcol));
         lo.a[1] = lcol * 128 + 16 * ((2 * kq + 1) ^ a_swz(lcol));
         lo.b = col * 32 + 16 * ((kq >> 1) ^ ((lcol >> 3) & 1)) + 8 * (kq & 1);
-        lo.s = col * 4 + kq;
+        lo.s = col * kSRowBytes + kq;
     }
 
     int g = 0;            // (tile, stage) step being computed
@@ -419,14 +436,15 @@ __global__ void __launch_bounds__(kPT, 1) k_gemm_pipe(PipeParams P) {
         for (int st = 0; st < nst; ++st, ++g) {
             {
                 const int after = nsteps - 1 - g;
-                stage_barrier<BM>(dma_wave, after < kAhead - 1 ? after : kAhead - 1);
+                stage_barrier<BM>(dma_wave, after < kAhead - 1 ? after : kAhead - 1, g);
             }
             // a DMA wave spreads stage g + kAhead's loads over this stage's MFMAs
             const bool issuing = dma_wave && g + kAhead < nsteps;
             if (issuing) MOE_PIPE_BEGIN();   /* before the first op: it may set up a new tile */
             const int rs = g & (kStages - 1);
             stage_mfma<GATEUP, MS>(acc, ring + kARing + rs * kABytes, ring + kBRing + rs * kBBytes,
-                               ring + kSRing + rs * kSBytes, lo, [&](int p) {
+                               ring + kSRing + ((g / kSBlk) & 1) * kSBlkBytes + (g % kSBlk) * (kBK / 16), lo,
+                               [&](int p) {
                 if (issuing) {
 #pragma unroll
                     for (int j = 0; j < kOpsPerStage; ++j)
@@ -493,7 +511,7 @@ int cu_count_pipe() {
 
 template <bool GATEUP, int BM>
 moe_status launch_pipe_bm(const PipeParams& P, int64_t slots, hipStream_t s) {
-    const size_t shmem = (size_t)kStages * stage_bytes<BM>();
+    const size_t shmem = (size_t)ring_bytes<BM>();
     if (allow_dynamic_lds(reinterpret_cast<const void*>(&k_gemm_pipe<GATEUP, BM>), shmem) != MOE_OK)
         return MOE_ERR_HIP;
     const int64_t tiles_ub = (slots / BM + std::min<int64_t>(P.E, slots)) * P.ntn;
@@ -519,7 +537,8 @@ moe_status launch_pipe(const PipeParams& P, int64_t slots, hipStream_t s) {
 // Shapes the kernels tile exactly; the activation DMAs address rows by a
 // 32-bit byte offset from the activation base (x for gate/up, h for down).
 bool prefill_pipe_supported(int64_t T, int k, int H, int I) {
-    return H % kBN == 0 && I % (kBN / 2) == 0 && I % kBK == 0 && T * H * 2 < (int64_t)1 << 32 &&
+    return H % kBN == 0 && I % (kBN / 2) == 0 && H % (kBK * kSBlk) == 0 && I % (kBK * kSBlk) == 0 &&
+           T * H * 2 < (int64_t)1 << 32 &&
            T * k * I * 2 < (int64_t)1 << 32;
 }
 
